@@ -1,0 +1,394 @@
+#!/usr/bin/env python3
+"""Benchmark of the layer-boundary path on one MI355X.
+
+A step is one fused boundary at the prefill fused-batch cap: publish P = 8
+bf16 partials [2048, 4096] and fold them into the residual with the RMSNorm
+read (bnd_fold_norm). Inputs and outputs rotate over sets that together exceed
+1 GiB, so the 256 MB Infinity Cache cannot serve a step from a previous one.
+`value` is tokens/s over the K timed steps (wall clock between device
+synchronisations); the roofline block reports the kernel's algorithmic bytes
+over its average duration from HIP events recorded on the launch stream.
+
+Secondary measurements (the quantised read, the MoE finalize over all rows
+and over the reduce-scatter share, the decode chain eager and as a HIP graph)
+and the oracle's CPU baseline go into the same JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused fold+RMSNorm tokens/s and achieved HBM GB/s (% of peak), T=2048 H=4096"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+ROTATE_BYTES = 1 << 30          # >= 4x the 256 MB Infinity Cache
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["kernels.h", "launch.h", "k_partials.hip", "k_moe.hip", "k_read.hip",
+                  "k_complete.hip", "host.cpp"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "reduce_residual_rmsnorm_bnd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches these kernels."""
+    path = os.path.join(PROFILES, "traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel source hash: `([0-9a-f]+)`", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"^\| {re.escape(workload)} \|[^\n]*\| ([0-9.]+) \|$", text, flags=re.M)
+    return float(m.group(1)) if m else None
+
+
+# --------------------------------------------------------------------------
+# timing harness
+# --------------------------------------------------------------------------
+
+class Timed:
+    """Runs step(i) with HIP events around each launch on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, step, n_sets: int, warmup: int, steps: int):
+        torch = self.torch
+        for i in range(warmup):
+            step(i % n_sets, None, None)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step((warmup + i) % n_sets, starts[i], ends[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
+        durs.sort()
+        return {
+            "wall_s": wall,
+            "kernel_mean_s": sum(durs) / len(durs),
+            "kernel_median_s": durs[len(durs) // 2],
+            "kernel_p10_s": durs[len(durs) // 10],
+            "kernel_p90_s": durs[(9 * len(durs)) // 10],
+        }
+
+
+def fold_case(torch, bnd, d, n_sets, fp8=False, row_begin=0, rows=None):
+    """Device sets for a partials fold; returns (step function, algorithmic bytes per launch)."""
+    T, H, P = d["T"], d["H"], d["P"]
+    rows = T - row_begin if rows is None else rows
+    dev = torch.device("cuda:0")
+    L = bnd.lib()
+    base_parts = [c.to(dev) for c in d["partials"]]
+    base_res = d["residual"][row_begin:row_begin + rows].to(dev)
+    w = d["weight"].to(dev)
+    sets = []
+    for s_i in range(n_sets):
+        parts = base_parts if s_i == 0 else [c.clone() for c in base_parts]
+        res = base_res.clone()
+        st = bnd.bnd_stream_create(T, H, res, row_begin, rows)
+        bnd.bnd_written(st, res)
+        if fp8:
+            out = (torch.empty(rows, H, dtype=torch.uint8, device=dev),
+                   torch.empty(rows, dtype=torch.float32, device=dev))
+        else:
+            out = (torch.empty(rows, H, dtype=torch.bfloat16, device=dev),)
+        arr = (ctypes.c_void_p * P)(*[c.data_ptr() for c in parts])
+        sets.append((st, parts, res, out, arr))
+    owed = ctypes.c_uint64()
+    eps = ctypes.c_float(d["eps"])
+    wptr = ctypes.c_void_p(w.data_ptr())
+    hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step(i, ev0, ev1):
+        st, parts, res, out, arr = sets[i]
+        rc = L.bnd_publish_partials(st.handle, arr, P, H, ctypes.byref(owed))
+        if ev0 is not None:
+            ev0.record()
+        if fp8:
+            rc |= L.bnd_fold_norm_quant_fp8(st.handle, owed.value, wptr, eps,
+                                            ctypes.c_void_p(out[0].data_ptr()), H,
+                                            ctypes.c_void_p(out[1].data_ptr()), hs)
+        else:
+            rc |= L.bnd_fold_norm(st.handle, owed.value, wptr, eps,
+                                  ctypes.c_void_p(out[0].data_ptr()), H, hs)
+        if ev1 is not None:
+            ev1.record()
+        if rc:
+            raise RuntimeError(L.bnd_last_error().decode())
+
+    el = rows * H
+    read = (P * el + el) * 2 + H * 4
+    write = el * 2 + (el + rows * 4 if fp8 else el * 2)
+    keep = (sets, base_parts, w)
+    return step, read + write, keep
+
+
+def moe_case(torch, bnd, d, n_sets, row_begin=0, rows=None):
+    T, H, k = d["T"], d["H"], d["k"]
+    rows = T - row_begin if rows is None else rows
+    dev = torch.device("cuda:0")
+    L = bnd.lib()
+    E0 = d["expert_rows"].to(dev)
+    idx0 = d["idx"].to(dev)
+    gate0 = d["gate"].to(dev)
+    res0 = d["residual"][row_begin:row_begin + rows].to(dev)
+    w = d["weight"].to(dev)
+    sets = []
+    for s_i in range(n_sets):
+        E = E0 if s_i == 0 else E0.clone()
+        res = res0.clone()
+        st = bnd.bnd_stream_create(T, H, res, row_begin, rows)
+        bnd.bnd_written(st, res)
+        y = torch.empty(rows, H, dtype=torch.bfloat16, device=dev)
+        sets.append((st, E, res, y))
+    owed = ctypes.c_uint64()
+    eps = ctypes.c_float(d["eps"])
+    wptr = ctypes.c_void_p(w.data_ptr())
+    hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    iptr, gptr = ctypes.c_void_p(idx0.data_ptr()), ctypes.c_void_p(gate0.data_ptr())
+
+    def step(i, ev0, ev1):
+        st, E, res, y = sets[i]
+        rc = L.bnd_publish_moe(st.handle, ctypes.c_void_p(E.data_ptr()), E.shape[0], H, iptr, gptr, k,
+                               ctypes.byref(owed))
+        if ev0 is not None:
+            ev0.record()
+        rc |= L.bnd_moe_finalize_fold_norm(st.handle, owed.value, wptr, eps,
+                                           ctypes.c_void_p(y.data_ptr()), H, hs)
+        if ev1 is not None:
+            ev1.record()
+        if rc:
+            raise RuntimeError(L.bnd_last_error().decode())
+
+    el = rows * H
+    read = rows * k * H * 2 + el * 2 + H * 4 + rows * k * 8
+    write = el * 4
+    return step, read + write, (sets, idx0, gate0, w)
+
+
+def decode_chain(torch, bnd, workloads, T, reps_eager, reps_graph, H=4096, P=4, n_b=96):
+    """1 enter + 96 folds with fresh partials per boundary: eager and HIP-graph us/boundary."""
+    dev = torch.device("cuda:0")
+    start = workloads.decode_start(T, H)
+    x_in = start["x_in"].to(dev)
+    w0 = start["weight"].to(dev)
+    bounds = []
+    for b in range(n_b):
+        d = workloads.decode_boundary(T, b, P, H)
+        bounds.append(([c.to(dev) for c in d["partials"]], d["weight"].to(dev)))
+    res = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    L = bnd.lib()
+    arrs = [(ctypes.c_void_p * P)(*[c.data_ptr() for c in parts]) for parts, _ in bounds]
+    wptrs = [ctypes.c_void_p(w.data_ptr()) for _, w in bounds]
+    eps = ctypes.c_float(1e-6)
+    owed = ctypes.c_uint64()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def chain(st):
+        hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rc = L.bnd_take_output(st.handle)
+        rc |= L.bnd_enter_norm(st.handle, ptr(x_in), H, ptr(w0), eps, ptr(y), H, hs)
+        for b in range(n_b):
+            rc |= L.bnd_publish_partials(st.handle, arrs[b], P, H, ctypes.byref(owed))
+            rc |= L.bnd_fold_norm(st.handle, owed.value, wptrs[b], eps, ptr(y), H, hs)
+        if rc:
+            raise RuntimeError(L.bnd_last_error().decode())
+
+    st = bnd.bnd_stream_create(T, H, res)
+    for _ in range(3):
+        chain(st)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps_eager):
+        chain(st)
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / (reps_eager * (n_b + 1))
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain(st)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        chain(st)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps_graph):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = (time.perf_counter() - t0) / (reps_graph * (n_b + 1))
+    bytes_b = T * (P + 3) * H * 2 + H * 4
+    return {"T": T, "us_per_boundary_eager": eager * 1e6, "us_per_boundary_graph": graph * 1e6,
+            "tokens_per_s_graph": T / graph, "algorithmic_bytes_per_boundary": bytes_b,
+            "GBps_graph": bytes_b / graph / 1e9}
+
+
+def copy_ceiling(torch, n_bytes=1 << 30, reps=20):
+    """A plain device copy of a 1 GiB buffer (torch's copy kernel), for context."""
+    a = torch.empty(n_bytes // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    return {"bytes": 2 * n_bytes, "GBps": 2 * n_bytes / t / 1e9}
+
+
+def cpu_baseline(workloads, d, budget_s: float):
+    """The fp64 oracle (single-threaded) over the whole prefill workload, repeated."""
+    import oracle
+
+    o = oracle.Oracle()
+    parts = [workloads.bf16_bits(c) for c in d["partials"]]
+    res = workloads.bf16_bits(d["residual"])
+    w = d["weight"].numpy()
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        o.fold_norm(parts, res, w, d["eps"])
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": passes * d["T"] / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes of the full prefill boundary (2048 rows x 4096, P=8) "
+                      f"in {el:.1f} s, one thread, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true", help="only the prefill step")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
+              "multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    import reduce_residual_rmsnorm_bnd_amd as bnd
+    from reduce_residual_rmsnorm_bnd_amd import _build
+
+    if not os.path.exists(_build.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    timer = Timed(torch)
+    props = torch.cuda.get_device_properties(0)
+
+    log("generating the prefill workload (T=2048 H=4096 P=8)")
+    d = workloads.prefill()
+    per_set = (d["P"] + 3) * d["T"] * d["H"] * 2
+    n_sets = max(2, -(-ROTATE_BYTES // per_set))
+    step, nbytes, keep = fold_case(torch, bnd, d, n_sets)
+    log(f"timing {args.steps} steps over {n_sets} rotating sets")
+    t = timer.run(step, n_sets, args.warmup, args.steps)
+    achieved = nbytes / t["kernel_mean_s"] / 1e9
+    traffic = traffic_from_profiles("prefill T=2048 H=4096 P=8")
+    result = {
+        "metric": METRIC,
+        "value": args.steps * d["T"] / t["wall_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t["wall_s"] / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill boundary fold+RMSNorm, T=2048 H=4096 P=8, bf16 in/out",
+                   "T": 2048, "H": 4096, "P": 8, "rotation_sets": n_sets,
+                   "device": props.name, "storage": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "kernel": "read_kernel<Partials, 8, 1, bf16>",
+                     "algorithmic_bytes": nbytes,
+                     "kernel_mean_us": t["kernel_mean_s"] * 1e6,
+                     "kernel_median_us": t["kernel_median_s"] * 1e6,
+                     "kernel_p10_us": t["kernel_p10_s"] * 1e6,
+                     "kernel_p90_us": t["kernel_p90_s"] * 1e6},
+    }
+    del keep, step
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = {}
+        log("quantised read (T=2048 H=7168 P=8, fp8 out)")
+        dq = workloads.quantised()
+        n_q = max(2, -(-ROTATE_BYTES // ((dq["P"] + 2) * dq["T"] * dq["H"] * 2 + dq["T"] * dq["H"])))
+        step, nb, keep = fold_case(torch, bnd, dq, n_q, fp8=True)
+        tq = timer.run(step, n_q, 20, 100)
+        sec["fp8_T2048_H7168_P8"] = {"tokens_per_s_kernel": 2048 / tq["kernel_mean_s"],
+                                     "kernel_mean_us": tq["kernel_mean_s"] * 1e6,
+                                     "GBps": nb / tq["kernel_mean_s"] / 1e9,
+                                     "frac": nb / tq["kernel_mean_s"] / 1e9 / PEAK_HBM_GBPS,
+                                     "algorithmic_bytes": nb}
+        del keep, step, dq
+        torch.cuda.empty_cache()
+        log("MoE finalize (T=2048 H=4096 k=8), full rows and rows 768..1023")
+        dm = workloads.moe()
+        n_m = max(2, -(-ROTATE_BYTES // (dm["T"] * (dm["k"] + 3) * dm["H"] * 2)))
+        for name, rb, rows in (("moe_full_T2048_H4096_k8", 0, 2048),
+                               ("moe_slice_rows768_1023", *workloads.MOE_SLICE)):
+            step, nb, keep = moe_case(torch, bnd, dm, n_m, rb, rows)
+            tm = timer.run(step, n_m, 20, 100)
+            sec[name] = {"tokens_per_s_kernel": rows / tm["kernel_mean_s"],
+                         "kernel_mean_us": tm["kernel_mean_s"] * 1e6,
+                         "GBps": nb / tm["kernel_mean_s"] / 1e9,
+                         "frac": nb / tm["kernel_mean_s"] / 1e9 / PEAK_HBM_GBPS,
+                         "algorithmic_bytes": nb}
+            del keep, step
+        del dm
+        torch.cuda.empty_cache()
+        log("decode chain (1 enter + 96 folds), eager and graph")
+        sec["decode"] = [decode_chain(torch, bnd, workloads, T, 20, 50) for T in (1, 8, 32, 128)]
+        torch.cuda.empty_cache()
+        sec["copy_ceiling_1GiB"] = copy_ceiling(torch)
+        result["secondary"] = sec
+
+    log(f"CPU baseline: the oracle for ~{args.cpu_seconds:.0f} s")
+    result["cpu_baseline"] = cpu_baseline(workloads, d, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,564 @@
+// host.cpp -- the C ABI of libboundary: stream state machine, validation,
+// launch-shape choice and dispatch (declared in include/boundary.h).
+//
+// The stream follows the state table of the SGLang guide "Layer boundaries"
+// (section "Residual stream"): Initial -> the read enters; Written -> the
+// read applies no update; Pending -> complete the owed work, fold it into the
+// residual, read. Owed tokens play the part of the guide's OwedOutput
+// handles: a read must present the token of the stream's current
+// publication, so a stale or foreign handle is refused instead of applying
+// the wrong pending work. Every check runs before any launch, so a refused
+// call leaves outputs and state untouched (section "Fusion providers and
+// output decisions": a candidate refuses before modifying its inputs).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "../../include/boundary.h"
+#include "launch.h"
+
+using bnd::Launch;
+using bnd::RowArgs;
+using bnd::Source;
+
+struct bnd_stream {
+  uint64_t serial;
+  uint32_t epoch;
+  int64_t T, H, row_begin, rows;
+  uint16_t* residual;
+  int64_t ld_res;
+  bnd_state state;
+  bool has_residual;
+  bnd_kind kind;
+  bnd_owed owed;
+  // partials (global rows): element (t, h) at src[p] + (t - src_origin) * ld_src + h
+  const uint16_t* src[BND_MAX_SOURCES];
+  int nsrc;
+  int64_t ld_src;
+  int64_t src_origin;
+  // deferred MoE finalize
+  const uint16_t* experts;
+  int64_t n_expert_rows;
+  int64_t ld_e;
+  const int32_t* idx;
+  const float* gate;
+  int k;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<uint64_t> g_serial{1};
+std::atomic<int> g_fused_unavailable{-1};  // -1: read BND_DISABLE_FUSED on first use
+std::atomic<int> g_threads_override{0};
+std::atomic<int> g_vpt_override{0};
+
+bnd_status fail(bnd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(bnd_status_str(st)) + ": " + buf;
+  return st;
+}
+
+bnd_status ok() {
+  g_last_error.clear();
+  return BND_OK;
+}
+
+bool fused_unavailable() {
+  int v = g_fused_unavailable.load();
+  if (v < 0) {
+    const char* e = getenv("BND_DISABLE_FUSED");
+    v = (e && e[0] == '1') ? 1 : 0;
+    int expected = -1;
+    g_fused_unavailable.compare_exchange_strong(expected, v);
+    v = g_fused_unavailable.load();
+  }
+  return v == 1;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bnd_owed make_owed(const bnd_stream* s) { return (s->serial << 24) | (s->epoch & 0xFFFFFFu); }
+
+// Byte range [lo, hi) touched by rows [0, rows) of a row tensor.
+struct Range {
+  uintptr_t lo = 0, hi = 0;
+};
+
+Range rows_range(const void* base, int64_t rows, int64_t ld, int64_t width, int64_t elem) {
+  Range r;
+  if (!base || rows <= 0 || width <= 0) return r;
+  r.lo = reinterpret_cast<uintptr_t>(base);
+  r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + width) * elem);
+  return r;
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bnd_status check_hidden(int64_t H) {
+  if (H < 8 || H > BND_MAX_HIDDEN || H % 8 != 0)
+    return fail(BND_ERR_NO_PATH, "hidden size %lld: need a multiple of 8 in [8, %d]", (long long)H,
+                BND_MAX_HIDDEN);
+  return BND_OK;
+}
+
+bnd_status check_rows_tensor(const char* what, const void* p, int64_t ld, int64_t H, bool needed) {
+  if (!needed) return BND_OK;
+  if (!p) return fail(BND_ERR_INVALID_ARG, "%s is NULL", what);
+  if (!aligned(p, 16)) return fail(BND_ERR_INVALID_ARG, "%s is not 16-byte aligned", what);
+  if (ld < H || ld % 8 != 0)
+    return fail(BND_ERR_INVALID_ARG, "%s leading dimension %lld: need a multiple of 8, >= H = %lld",
+                what, (long long)ld, (long long)H);
+  return BND_OK;
+}
+
+bnd_status check_weight(const float* w, float eps, bool needed) {
+  if (!(eps >= 0.0f) || eps != eps || eps > 3.4e38f)
+    return fail(BND_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!needed) return BND_OK;
+  if (!w) return fail(BND_ERR_INVALID_ARG, "weight is NULL");
+  if (!aligned(w, 16)) return fail(BND_ERR_INVALID_ARG, "weight is not 16-byte aligned");
+  return BND_OK;
+}
+
+// Launch shape: one workgroup per row; threads * vpt vectors of 8 elements
+// must cover the row. Default: the fewest vectors per thread that keep the
+// workgroup within 1024 threads.
+bnd_status choose_launch(int64_t H, int64_t rows, Launch* l) {
+  const int nvec = (int)(H / 8);
+  int vpt = g_vpt_override.load();
+  int threads = g_threads_override.load();
+  if (vpt == 0) vpt = nvec <= 1024 ? 1 : nvec <= 2048 ? 2 : 4;
+  if (threads == 0) {
+    int need = (nvec + vpt - 1) / vpt;
+    threads = ((need + bnd::kWave - 1) / bnd::kWave) * bnd::kWave;
+  }
+  if (vpt != 1 && vpt != 2 && vpt != 4)
+    return fail(BND_ERR_NO_PATH, "vectors per thread %d: need 1, 2 or 4", vpt);
+  if (threads < bnd::kWave || threads > bnd::kMaxThreads || threads % bnd::kWave != 0)
+    return fail(BND_ERR_NO_PATH, "threads per row %d: need a multiple of 64 in [64, 1024]", threads);
+  if ((int64_t)threads * vpt < nvec)
+    return fail(BND_ERR_NO_PATH, "launch shape %d threads x %d vectors cannot cover H = %lld", threads,
+                vpt, (long long)H);
+  if (rows > 0x7fffffff) return fail(BND_ERR_NO_PATH, "too many rows for one grid");
+  l->rows = (int)rows;
+  l->threads = threads;
+  l->vpt = vpt;
+  return BND_OK;
+}
+
+RowArgs base_args(const bnd_stream* s) {
+  RowArgs a;
+  memset(&a, 0, sizeof a);
+  a.H = (int)s->H;
+  a.nvec = (int)(s->H / 8);
+  a.res = s->residual;
+  a.ld_res = s->ld_res;
+  a.has_residual = s->has_residual ? 1 : 0;
+  return a;
+}
+
+// Fill the owed-work part of the arguments for the stream's slice.
+void pending_args(const bnd_stream* s, RowArgs* a) {
+  if (s->kind == BND_KIND_PARTIALS) {
+    for (int p = 0; p < s->nsrc; ++p) a->src[p] = s->src[p] + (s->row_begin - s->src_origin) * s->ld_src;
+    a->ld_src = s->ld_src;
+  } else if (s->kind == BND_KIND_MOE) {
+    a->experts = s->experts;
+    a->ld_e = s->ld_e;
+    a->n_expert_rows = s->n_expert_rows;
+    a->idx = s->idx + s->row_begin * s->k;
+    a->gate = s->gate + s->row_begin * s->k;
+  }
+}
+
+// Input byte ranges of the pending work restricted to the slice.
+int pending_ranges(const bnd_stream* s, Range* out) {
+  int n = 0;
+  if (s->rows <= 0) return 0;
+  if (s->kind == BND_KIND_PARTIALS) {
+    for (int p = 0; p < s->nsrc; ++p)
+      out[n++] = rows_range(s->src[p] + (s->row_begin - s->src_origin) * s->ld_src, s->rows, s->ld_src,
+                            s->H, 2);
+  } else if (s->kind == BND_KIND_MOE) {
+    out[n++] = rows_range(s->experts, s->n_expert_rows, s->ld_e, s->H, 2);
+    out[n++] = rows_range(s->idx + s->row_begin * s->k, s->rows, s->k, s->k, 4);
+    out[n++] = rows_range(s->gate + s->row_begin * s->k, s->rows, s->k, s->k, 4);
+  }
+  return n;
+}
+
+bnd_status check_output_disjoint(const bnd_stream* s, const char* what, const Range& out, bool with_residual,
+                                 const Range* extra = nullptr, int n_extra = 0) {
+  Range in[BND_MAX_SOURCES + 4];
+  int n = pending_ranges(s, in);
+  if (with_residual) in[n++] = rows_range(s->residual, s->rows, s->ld_res, s->H, 2);
+  for (int i = 0; i < n; ++i)
+    if (overlap(out, in[i])) return fail(BND_ERR_INVALID_ARG, "%s overlaps the residual or an input", what);
+  for (int i = 0; i < n_extra; ++i)
+    if (overlap(out, extra[i])) return fail(BND_ERR_INVALID_ARG, "%s overlaps another output", what);
+  return BND_OK;
+}
+
+bnd_status launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BND_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return BND_OK;
+}
+
+// The shared state checks of a read that folds owed work (fold_norm,
+// fold_norm_quant_fp8, moe_finalize_fold_norm). `kind` is the owed-work kind
+// the call completes. On BND_OK, *fold tells whether there is work to fold.
+bnd_status check_fold_state(const bnd_stream* s, bnd_owed owed, bnd_kind kind, bool* fold) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  if (s->state == BND_INITIAL)
+    return fail(BND_ERR_NOT_STARTED, "the stream has neither a residual nor a contribution; enter first");
+  if (s->state == BND_WRITTEN) {
+    if (owed != BND_OWED_NONE) return fail(BND_ERR_FOREIGN_OUTPUT, "the stream owes nothing; the handle is foreign");
+    *fold = false;
+    return BND_OK;
+  }
+  if (s->kind != kind)
+    return fail(BND_ERR_WRONG_KIND, "the pending contribution is a %s, this call completes a %s",
+                s->kind == BND_KIND_MOE ? "MoE finalize handoff" : "set of partials",
+                kind == BND_KIND_MOE ? "MoE finalize handoff" : "set of partials");
+  if (owed != s->owed) return fail(BND_ERR_FOREIGN_OUTPUT, "the handle does not belong to this stream's pending output");
+  if (fused_unavailable() && (kind == BND_KIND_MOE || s->nsrc > 1))
+    return fail(BND_ERR_UNAVAILABLE, "fused completion is switched off; complete_only then a one-source fold");
+  *fold = true;
+  return BND_OK;
+}
+
+void become_written(bnd_stream* s) {
+  s->state = BND_WRITTEN;
+  s->has_residual = true;
+  s->kind = BND_KIND_NONE;
+  s->owed = BND_OWED_NONE;
+  s->nsrc = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bnd_status_str(bnd_status st) {
+  switch (st) {
+    case BND_OK: return "BND_OK";
+    case BND_ERR_INVALID_ARG: return "BND_ERR_INVALID_ARG";
+    case BND_ERR_NOT_STARTED: return "BND_ERR_NOT_STARTED";
+    case BND_ERR_FOREIGN_OUTPUT: return "BND_ERR_FOREIGN_OUTPUT";
+    case BND_ERR_PENDING: return "BND_ERR_PENDING";
+    case BND_ERR_WRONG_KIND: return "BND_ERR_WRONG_KIND";
+    case BND_ERR_NO_PATH: return "BND_ERR_NO_PATH";
+    case BND_ERR_UNAVAILABLE: return "BND_ERR_UNAVAILABLE";
+    case BND_ERR_HIP: return "BND_ERR_HIP";
+  }
+  return "BND_ERR_UNKNOWN";
+}
+
+const char* bnd_last_error(void) { return g_last_error.c_str(); }
+
+const char* bnd_version(void) { return "libboundary 0.1 (gfx950)"; }
+
+bnd_status bnd_set_option(bnd_option opt, int64_t value) {
+  switch (opt) {
+    case BND_OPT_FUSED_UNAVAILABLE:
+      if (value != 0 && value != 1) return fail(BND_ERR_INVALID_ARG, "fused-unavailable takes 0 or 1");
+      g_fused_unavailable.store((int)value);
+      return ok();
+    case BND_OPT_THREADS_PER_ROW:
+      if (value != 0 && (value < 64 || value > 1024 || value % 64 != 0))
+        return fail(BND_ERR_INVALID_ARG, "threads per row: 0 or a multiple of 64 in [64, 1024]");
+      g_threads_override.store((int)value);
+      return ok();
+    case BND_OPT_VECTORS_PER_THREAD:
+      if (value != 0 && value != 1 && value != 2 && value != 4)
+        return fail(BND_ERR_INVALID_ARG, "vectors per thread: 0, 1, 2 or 4");
+      g_vpt_override.store((int)value);
+      return ok();
+  }
+  return fail(BND_ERR_INVALID_ARG, "unknown option %d", (int)opt);
+}
+
+int64_t bnd_get_option(bnd_option opt) {
+  switch (opt) {
+    case BND_OPT_FUSED_UNAVAILABLE: return fused_unavailable() ? 1 : 0;
+    case BND_OPT_THREADS_PER_ROW: return g_threads_override.load();
+    case BND_OPT_VECTORS_PER_THREAD: return g_vpt_override.load();
+  }
+  return -1;
+}
+
+bnd_status bnd_stream_create(bnd_stream** out, int64_t T, int64_t H, int64_t row_begin, int64_t rows,
+                             void* residual, int64_t ld_res) {
+  if (!out) return fail(BND_ERR_INVALID_ARG, "out is NULL");
+  if (T < 0) return fail(BND_ERR_INVALID_ARG, "T = %lld < 0", (long long)T);
+  if (row_begin < 0 || rows < 0 || row_begin + rows > T)
+    return fail(BND_ERR_INVALID_ARG, "slice [%lld, %lld) is not inside [0, %lld)", (long long)row_begin,
+                (long long)(row_begin + rows), (long long)T);
+  bnd_status st = check_hidden(H);
+  if (st) return st;
+  if ((st = check_rows_tensor("residual", residual, ld_res, H, rows > 0))) return st;
+  bnd_stream* s = new (std::nothrow) bnd_stream;
+  if (!s) return fail(BND_ERR_INVALID_ARG, "out of host memory");
+  memset(s, 0, sizeof *s);
+  s->serial = g_serial.fetch_add(1);
+  s->epoch = 0;
+  s->T = T;
+  s->H = H;
+  s->row_begin = row_begin;
+  s->rows = rows;
+  s->residual = static_cast<uint16_t*>(residual);
+  s->ld_res = ld_res;
+  s->state = BND_INITIAL;
+  s->has_residual = false;
+  s->kind = BND_KIND_NONE;
+  s->owed = BND_OWED_NONE;
+  *out = s;
+  return ok();
+}
+
+bnd_status bnd_stream_destroy(bnd_stream* s) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  delete s;
+  return ok();
+}
+
+bnd_state bnd_stream_state(const bnd_stream* s) { return s ? s->state : BND_INITIAL; }
+
+bnd_kind bnd_stream_pending_kind(const bnd_stream* s) { return s ? s->kind : BND_KIND_NONE; }
+
+int bnd_stream_has_residual(const bnd_stream* s) { return (s && s->has_residual) ? 1 : 0; }
+
+bnd_status bnd_publish_partials(bnd_stream* s, const void* const* partials, int P, int64_t ld, bnd_owed* owed) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  if (!owed) return fail(BND_ERR_INVALID_ARG, "owed is NULL");
+  if (s->state == BND_PENDING) return fail(BND_ERR_PENDING, "a contribution is already pending; fold it first");
+  if (P < 1 || P > BND_MAX_SOURCES) return fail(BND_ERR_NO_PATH, "P = %d: need 1..%d partials", P, BND_MAX_SOURCES);
+  if (s->rows > 0 && !partials) return fail(BND_ERR_INVALID_ARG, "partials is NULL");
+  for (int p = 0; p < P && s->rows > 0; ++p) {
+    char what[32];
+    snprintf(what, sizeof what, "partial %d", p);
+    bnd_status st = check_rows_tensor(what, partials[p], ld, s->H, true);
+    if (st) return st;
+  }
+  for (int p = 0; p < P; ++p) s->src[p] = s->rows > 0 ? static_cast<const uint16_t*>(partials[p]) : nullptr;
+  s->nsrc = P;
+  s->ld_src = ld;
+  s->src_origin = 0;
+  s->kind = BND_KIND_PARTIALS;
+  s->state = BND_PENDING;
+  s->epoch++;
+  s->owed = make_owed(s);
+  *owed = s->owed;
+  return ok();
+}
+
+bnd_status bnd_publish_moe(bnd_stream* s, const void* expert_rows, int64_t n_rows, int64_t ld, const int32_t* idx,
+                           const float* gate, int k, bnd_owed* owed) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  if (!owed) return fail(BND_ERR_INVALID_ARG, "owed is NULL");
+  if (s->state == BND_PENDING) return fail(BND_ERR_PENDING, "a contribution is already pending; fold it first");
+  if (k < 1 || k > BND_MAX_SOURCES) return fail(BND_ERR_NO_PATH, "k = %d: need 1..%d picks", k, BND_MAX_SOURCES);
+  if (n_rows < 0) return fail(BND_ERR_INVALID_ARG, "n_rows < 0");
+  if (s->rows > 0) {
+    bnd_status st = check_rows_tensor("expert rows", expert_rows, ld, s->H, n_rows > 0);
+    if (st) return st;
+    if (!idx || !aligned(idx, 4)) return fail(BND_ERR_INVALID_ARG, "idx is NULL or misaligned");
+    if (!gate || !aligned(gate, 4)) return fail(BND_ERR_INVALID_ARG, "gate is NULL or misaligned");
+  }
+  s->experts = static_cast<const uint16_t*>(expert_rows);
+  s->n_expert_rows = n_rows;
+  s->ld_e = ld;
+  s->idx = idx;
+  s->gate = gate;
+  s->k = k;
+  s->nsrc = 0;
+  s->kind = BND_KIND_MOE;
+  s->state = BND_PENDING;
+  s->epoch++;
+  s->owed = make_owed(s);
+  *owed = s->owed;
+  return ok();
+}
+
+bnd_status bnd_enter_norm(bnd_stream* s, const void* x, int64_t ld_x, const float* w, float eps, void* y,
+                          int64_t ld_y, void* hip_stream) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  if (s->state == BND_PENDING) return fail(BND_ERR_PENDING, "a contribution is pending; fold it instead of entering");
+  const bool entering = s->state == BND_INITIAL;
+  const bool any = s->rows > 0;
+  bnd_status st;
+  if ((st = check_weight(w, eps, any))) return st;
+  if ((st = check_rows_tensor("y", y, ld_y, s->H, any))) return st;
+  if (entering && (st = check_rows_tensor("x", x, ld_x, s->H, any))) return st;
+  const bool alias = entering && x == s->residual && ld_x == s->ld_res;
+  Range yr = rows_range(y, s->rows, ld_y, s->H, 2);
+  Range in[2] = {rows_range(s->residual, s->rows, s->ld_res, s->H, 2),
+                 entering ? rows_range(x, s->rows, ld_x, s->H, 2) : Range{}};
+  if (overlap(yr, in[0]) || overlap(yr, in[1])) return fail(BND_ERR_INVALID_ARG, "y overlaps the residual or x");
+  if (entering && !alias && overlap(in[0], in[1]))
+    return fail(BND_ERR_INVALID_ARG, "x partly overlaps the residual storage");
+  if (any) {
+    Launch l;
+    if ((st = choose_launch(s->H, s->rows, &l))) return st;
+    RowArgs a = base_args(s);
+    a.w = w;
+    a.eps = eps;
+    a.y = static_cast<uint16_t*>(y);
+    a.ld_y = ld_y;
+    Source src = Source::Residual;
+    if (entering) {
+      src = Source::Input;
+      a.x_in = static_cast<const uint16_t*>(x);
+      a.ld_x = ld_x;
+      a.copy_input = alias ? 0 : 1;
+    }
+    if ((st = launch_status(bnd::launch_read(src, 0, false, a, l, (hipStream_t)hip_stream), "enter_norm")))
+      return st;
+  }
+  become_written(s);
+  return ok();
+}
+
+static bnd_status fold_read(bnd_stream* s, bnd_owed owed, bnd_kind kind, bool fp8, const float* w, float eps,
+                            void* y, int64_t ld_y, uint8_t* q, int64_t ld_q, float* scale, void* hip_stream,
+                            const char* name) {
+  bool fold = false;
+  bnd_status st = check_fold_state(s, owed, kind, &fold);
+  if (st) return st;
+  const bool any = s->rows > 0;
+  if ((st = check_weight(w, eps, any))) return st;
+  Range outs[2];
+  int n_out = 0;
+  if (fp8) {
+    if (any) {
+      if (!q || !aligned(q, 8)) return fail(BND_ERR_INVALID_ARG, "q is NULL or not 8-byte aligned");
+      if (ld_q < s->H || ld_q % 8 != 0) return fail(BND_ERR_INVALID_ARG, "ld_q: need a multiple of 8, >= H");
+      if (!scale || !aligned(scale, 4)) return fail(BND_ERR_INVALID_ARG, "scale is NULL or misaligned");
+    }
+    outs[n_out++] = rows_range(q, s->rows, ld_q, s->H, 1);
+    outs[n_out++] = rows_range(scale, s->rows, 1, 1, 4);
+    if (overlap(outs[0], outs[1])) return fail(BND_ERR_INVALID_ARG, "q overlaps scale");
+  } else {
+    if ((st = check_rows_tensor("y", y, ld_y, s->H, any))) return st;
+    outs[n_out++] = rows_range(y, s->rows, ld_y, s->H, 2);
+  }
+  for (int i = 0; i < n_out; ++i)
+    if ((st = check_output_disjoint(s, fp8 ? (i ? "scale" : "q") : "y", outs[i], true))) return st;
+  if (any) {
+    Launch l;
+    if ((st = choose_launch(s->H, s->rows, &l))) return st;
+    RowArgs a = base_args(s);
+    a.w = w;
+    a.eps = eps;
+    a.y = static_cast<uint16_t*>(y);
+    a.ld_y = ld_y;
+    a.q = q;
+    a.ld_q = ld_q;
+    a.scale = scale;
+    Source src = Source::Residual;
+    int n = 0;
+    if (fold) {
+      pending_args(s, &a);
+      src = kind == BND_KIND_MOE ? Source::Moe : Source::Partials;
+      n = kind == BND_KIND_MOE ? s->k : s->nsrc;
+    }
+    if ((st = launch_status(bnd::launch_read(src, n, fp8, a, l, (hipStream_t)hip_stream), name))) return st;
+  }
+  become_written(s);
+  return ok();
+}
+
+bnd_status bnd_fold_norm(bnd_stream* s, bnd_owed owed, const float* w, float eps, void* y, int64_t ld_y,
+                         void* hip_stream) {
+  return fold_read(s, owed, BND_KIND_PARTIALS, false, w, eps, y, ld_y, nullptr, 0, nullptr, hip_stream,
+                   "fold_norm");
+}
+
+bnd_status bnd_fold_norm_quant_fp8(bnd_stream* s, bnd_owed owed, const float* w, float eps, uint8_t* q,
+                                   int64_t ld_q, float* scale, void* hip_stream) {
+  return fold_read(s, owed, BND_KIND_PARTIALS, true, w, eps, nullptr, 0, q, ld_q, scale, hip_stream,
+                   "fold_norm_quant_fp8");
+}
+
+bnd_status bnd_moe_finalize_fold_norm(bnd_stream* s, bnd_owed owed, const float* w, float eps, void* y,
+                                      int64_t ld_y, void* hip_stream) {
+  return fold_read(s, owed, BND_KIND_MOE, false, w, eps, y, ld_y, nullptr, 0, nullptr, hip_stream,
+                   "moe_finalize_fold_norm");
+}
+
+bnd_status bnd_complete_only(bnd_stream* s, bnd_owed owed, void* out, int64_t ld_out, bnd_owed* new_owed,
+                             void* hip_stream) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  if (!new_owed) return fail(BND_ERR_INVALID_ARG, "new_owed is NULL");
+  if (s->state == BND_INITIAL) return fail(BND_ERR_NOT_STARTED, "nothing has been published on this stream");
+  if (s->state == BND_WRITTEN) return fail(BND_ERR_WRONG_KIND, "the stream owes nothing to complete");
+  if (owed != s->owed) return fail(BND_ERR_FOREIGN_OUTPUT, "the handle does not belong to this stream's pending output");
+  const bool any = s->rows > 0;
+  bnd_status st;
+  if ((st = check_rows_tensor("out", out, ld_out, s->H, any))) return st;
+  if ((st = check_output_disjoint(s, "out", rows_range(out, s->rows, ld_out, s->H, 2), true))) return st;
+  if (any) {
+    Launch l;
+    if ((st = choose_launch(s->H, s->rows, &l))) return st;
+    RowArgs a = base_args(s);
+    pending_args(s, &a);
+    a.y = static_cast<uint16_t*>(out);
+    a.ld_y = ld_out;
+    const Source src = s->kind == BND_KIND_MOE ? Source::Moe : Source::Partials;
+    const int n = s->kind == BND_KIND_MOE ? s->k : s->nsrc;
+    if ((st = launch_status(bnd::launch_complete(src, n, a, l, (hipStream_t)hip_stream), "complete_only")))
+      return st;
+  }
+  // the stream now owes one plain partial: `out`, addressed by slice row
+  s->kind = BND_KIND_PARTIALS;
+  s->src[0] = any ? static_cast<const uint16_t*>(out) : nullptr;
+  s->nsrc = 1;
+  s->ld_src = ld_out;
+  s->src_origin = s->row_begin;
+  s->experts = nullptr;
+  s->idx = nullptr;
+  s->gate = nullptr;
+  s->epoch++;
+  s->owed = make_owed(s);
+  *new_owed = s->owed;
+  return ok();
+}
+
+bnd_status bnd_written(bnd_stream* s, void* residual, int64_t ld_res) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  bnd_status st = check_rows_tensor("residual", residual, ld_res, s->H, s->rows > 0);
+  if (st) return st;
+  s->residual = static_cast<uint16_t*>(residual);
+  s->ld_res = ld_res;
+  become_written(s);
+  return ok();
+}
+
+bnd_status bnd_take_output(bnd_stream* s) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  if (s->state == BND_PENDING)
+    return fail(BND_ERR_PENDING, "a contribution is pending; fold or norm it before taking the output");
+  s->state = BND_INITIAL;
+  s->has_residual = false;
+  s->kind = BND_KIND_NONE;
+  s->owed = BND_OWED_NONE;
+  s->nsrc = 0;
+  return ok();
+}
+
+}  // extern "C"

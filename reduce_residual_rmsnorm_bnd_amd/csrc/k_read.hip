@@ -1,0 +1,38 @@
+// Reads without owed work (enter from Initial, read of a Written stream) and
+// the dispatcher of every boundary read.
+#include "kernels.h"
+
+namespace bnd {
+
+hipError_t launch_read_partials(int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream);
+hipError_t launch_read_moe(int n, const RowArgs& a, const Launch& l, hipStream_t stream);
+
+namespace {
+// [source: input, residual][vpt slot][bf16, fp8]
+constexpr KernelFn kPlain[2][3][2] = {
+    {{&read_kernel<Source::Input, 0, 1, false>, &read_kernel<Source::Input, 0, 1, true>},
+     {&read_kernel<Source::Input, 0, 2, false>, &read_kernel<Source::Input, 0, 2, true>},
+     {&read_kernel<Source::Input, 0, 4, false>, &read_kernel<Source::Input, 0, 4, true>}},
+    {{&read_kernel<Source::Residual, 0, 1, false>, &read_kernel<Source::Residual, 0, 1, true>},
+     {&read_kernel<Source::Residual, 0, 2, false>, &read_kernel<Source::Residual, 0, 2, true>},
+     {&read_kernel<Source::Residual, 0, 4, false>, &read_kernel<Source::Residual, 0, 4, true>}}};
+}  // namespace
+
+hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
+  switch (src) {
+    case Source::Partials:
+      return launch_read_partials(n, fp8, a, l, stream);
+    case Source::Moe:
+      if (fp8) return hipErrorInvalidValue;
+      return launch_read_moe(n, a, l, stream);
+    case Source::Input:
+    case Source::Residual: {
+      const int slot = vpt_slot(l.vpt);
+      if (slot < 0) return hipErrorInvalidValue;
+      return launch_kernel(kPlain[src == Source::Input ? 0 : 1][slot][fp8 ? 1 : 0], a, l, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bnd

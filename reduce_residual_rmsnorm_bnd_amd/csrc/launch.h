@@ -1,0 +1,59 @@
+// launch.h -- internal interface between the host state machine (host.cpp)
+// and the gfx950 kernels (k_*.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bnd {
+
+constexpr int kMaxSources = 16;
+constexpr int kMaxThreads = 1024;
+constexpr int kWave = 64;
+
+// Arguments of one boundary launch. Every row pointer is already offset to
+// the first row the launch processes, so a kernel addresses row i of each
+// operand at base + i * ld. The grid has one workgroup per row.
+struct RowArgs {
+  const uint16_t* src[kMaxSources];  // partial rows (bf16), one pointer per source
+  int64_t ld_src;                    // elements
+  const uint16_t* experts;           // MoE expert-output rows, indexed by idx (absolute)
+  int64_t ld_e;
+  int64_t n_expert_rows;
+  const int32_t* idx;                // MoE [rows, k], offset to the first row
+  const float* gate;                 // MoE [rows, k]
+  const uint16_t* x_in;              // stack input (enter)
+  int64_t ld_x;
+  uint16_t* res;                     // residual storage
+  int64_t ld_res;
+  const float* w;                    // norm weight [H]
+  uint16_t* y;                       // bf16 read output, or complete_only output
+  int64_t ld_y;
+  uint8_t* q;                        // fp8 read output
+  int64_t ld_q;
+  float* scale;                      // fp8 per-row scale
+  float eps;
+  int H;                             // elements per row
+  int nvec;                          // H / 8
+  int has_residual;                  // 0: fold with r = 0 (Pending without a residual)
+  int copy_input;                    // enter: store x_in into the residual storage
+};
+
+struct Launch {
+  int rows;     // grid size
+  int threads;  // workgroup size, multiple of 64
+  int vpt;      // 16-byte vectors per thread: 1, 2 or 4
+};
+
+enum class Source { Partials, Moe, Input, Residual };
+
+// fold_norm / fold_norm_quant_fp8 / moe_finalize_fold_norm / enter / written read.
+// n = number of sources (partials P or MoE picks k), ignored for Input/Residual.
+hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Launch& l,
+                       hipStream_t stream);
+
+// complete_only: y <- bf16(sum) for partials or MoE picks.
+hipError_t launch_complete(Source src, int n, const RowArgs& a, const Launch& l,
+                           hipStream_t stream);
+
+}  // namespace bnd

@@ -1,0 +1,487 @@
+"""The HIP path against the fp64 oracle, through the C ABI (gfx950 device).
+
+Inputs come from the seeded generator; expected values come only from the
+oracle run on those same inputs (chains of calls are replayed by the oracle on
+its own outputs). bf16 outputs must lie within 2 bf16 ulp (plus the fp32
+accumulation term under cancellation) of the exact value; fp8 codes must match
+except <= 0.1% off by one step. Every output buffer is surrounded by guard rows
+and padding columns filled with a canary pattern that must survive each call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tolerance
+import workloads
+import reduce_residual_rmsnorm_bnd_amd as bnd
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+CANARY16 = -23131  # 0xA5A5 as int16
+CANARY8 = 0xA5
+GUARD = 3
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    yield
+    for opt in (bnd.BND_OPT_FUSED_UNAVAILABLE, bnd.BND_OPT_THREADS_PER_ROW,
+                bnd.BND_OPT_VECTORS_PER_THREAD):
+        bnd.set_option(opt, 0)
+
+
+def bits(t):
+    return workloads.bf16_bits(t.detach().cpu().contiguous())
+
+
+class Guarded:
+    """A [rows, H] view inside a canary-filled buffer with guard rows and padded columns."""
+
+    def __init__(self, rows, H, dtype=torch.bfloat16, pad=0):
+        self.rows, self.H, self.pad = rows, H, pad
+        self.buf = torch.empty(rows + 2 * GUARD, H + pad, dtype=dtype, device=DEV)
+        if dtype == torch.bfloat16:
+            self.buf.view(torch.int16).fill_(CANARY16)
+        elif dtype == torch.uint8:
+            self.buf.fill_(CANARY8)
+        else:
+            self.buf.view(torch.int32).fill_(-1515870811)
+        self.view = self.buf[GUARD:GUARD + rows, :H]
+
+    def from_host(self, t):
+        self.view.copy_(t.to(DEV))
+        return self
+
+    def check_guards(self, what):
+        b = self.buf.cpu()
+        if b.dtype == torch.bfloat16:
+            b, c = b.view(torch.int16), CANARY16
+        elif b.dtype == torch.uint8:
+            c = CANARY8
+        else:
+            b, c = b.view(torch.int32), -1515870811
+        outside = torch.ones_like(b, dtype=torch.bool)
+        outside[GUARD:GUARD + self.rows, :self.H] = False
+        assert torch.all(b[outside] == c), f"{what}: a write landed outside the output"
+
+
+def check_fold(ref, res_bits, y_bits, w, eps, what):
+    a = tolerance.check_bf16(res_bits, ref["x_exact"], ref["mag"], f"{what} residual")
+    b = tolerance.check_bf16(y_bits, ref["y_exact"],
+                             tolerance.read_s_term(ref["x_exact"], ref["mag"], w, eps), f"{what} y")
+    print(f"\n  {what}: residual max {a['max_err_ulp']:.3f} ulp ({a['over_half_ulp']} > 0.5 ulp), "
+          f"y max {b['max_err_ulp']:.3f} ulp ({b['over_half_ulp']} > 0.5 ulp) over {a['n']} elements",
+          flush=True)
+
+
+def run_fold(d, *, row_begin=0, rows=None, fp8=False, pad=0, with_residual=True, partials=None):
+    """One fold through the library; returns host results and the guarded buffers."""
+    T, H = d["T"], d["H"]
+    rows = T - row_begin if rows is None else rows
+    parts = partials if partials is not None else [c.to(DEV) for c in d["partials"]]
+    res = Guarded(rows, H, pad=pad)
+    if with_residual:
+        res.from_host(d["residual"][row_begin:row_begin + rows])
+    w = d["weight"].to(DEV)
+    s = bnd.bnd_stream_create(T, H, res.view, row_begin, rows)
+    if with_residual:
+        bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_partials(s, parts)
+    out = {"res": res}
+    if fp8:
+        q = Guarded(rows, H, torch.uint8, pad=pad)
+        sc = torch.full((rows + 2,), -1.0, dtype=torch.float32, device=DEV)
+        bnd.bnd_fold_norm_quant_fp8(s, owed, w, d["eps"], q.view, sc[1:rows + 1])
+        out.update(q=q, scale_buf=sc)
+    else:
+        y = Guarded(rows, H, pad=pad)
+        bnd.bnd_fold_norm(s, owed, w, d["eps"], y.view)
+        out["y"] = y
+    torch.cuda.synchronize()
+    assert s.state == bnd.BND_WRITTEN and s.has_residual
+    out["stream"] = s
+    return out
+
+
+def oracle_fold(orc, d, *, row_begin=0, rows=None, fp8=False, with_residual=True):
+    T = d["T"]
+    rows = T - row_begin if rows is None else rows
+    res = bits(d["residual"][row_begin:row_begin + rows]) if with_residual else None
+    return orc.fold_norm([bits(c) for c in d["partials"]], res, d["weight"].numpy(), d["eps"],
+                         row_begin=row_begin, rows=rows, fp8=fp8)
+
+
+def assert_fold_matches(orc, d, what, **kw):
+    fp8 = kw.get("fp8", False)
+    got = run_fold(d, **kw)
+    okw = {k: v for k, v in kw.items() if k in ("row_begin", "rows", "fp8", "with_residual")}
+    ref = oracle_fold(orc, d, **okw)
+    w = d["weight"].numpy()
+    got["res"].check_guards(f"{what} residual")
+    res_bits = bits(got["res"].view)
+    if fp8:
+        got["q"].check_guards(f"{what} q")
+        sc = got["scale_buf"].cpu().numpy()
+        assert sc[0] == -1.0 and sc[-1] == -1.0, "scale written outside its rows"
+        tolerance.check_bf16(res_bits, ref["x_exact"], ref["mag"], f"{what} residual")
+        f = tolerance.check_fp8(got["q"].view.cpu().numpy(), ref["q"], f"{what} q")
+        s = tolerance.check_scale(sc[1:-1], ref["scale"], f"{what} scale")
+        print(f"\n  {what}: fp8 off-by-one {f['off_by_one']}/{f['n']}, scale max rel "
+              f"{s['max_rel']:.3g}", flush=True)
+    else:
+        got["y"].check_guards(f"{what} y")
+        check_fold(ref, res_bits, bits(got["y"].view), w, d["eps"], what)
+    return got, ref
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_tiny_fold(orc):
+    assert_fold_matches(orc, workloads.tiny(), "tiny T=16 H=256 P=2")
+
+
+def test_tiny_enter_and_written_read(orc):
+    d = workloads.tiny()
+    T, H = d["T"], d["H"]
+    res = Guarded(T, H)
+    y = Guarded(T, H)
+    w = d["weight"].to(DEV)
+    s = bnd.bnd_stream_create(T, H, res.view)
+    bnd.bnd_enter_norm(s, d["x_in"].to(DEV), w, d["eps"], y.view)
+    torch.cuda.synchronize()
+    assert s.state == bnd.BND_WRITTEN
+    ref = orc.enter_norm(bits(d["x_in"]), w.cpu().numpy(), d["eps"])
+    res.check_guards("enter residual")
+    y.check_guards("enter y")
+    assert np.array_equal(bits(res.view), ref["residual"]), "enter must copy x into the residual"
+    zero = np.zeros((T, H))
+    tolerance.check_bf16(bits(y.view), ref["y_exact"], zero, "enter y")
+    # a stack-entry read of a Written stream skips the enter: y = norm(residual)
+    y2 = Guarded(T, H)
+    bnd.bnd_enter_norm(s, None, w, d["eps"], y2.view)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y2.view), bits(y.view))
+    # the same read through fold_norm with nothing owed, and its fp8 form
+    y3 = Guarded(T, H)
+    bnd.bnd_fold_norm(s, bnd.BND_OWED_NONE, w, d["eps"], y3.view)
+    q = Guarded(T, H, torch.uint8)
+    sc = torch.empty(T, dtype=torch.float32, device=DEV)
+    bnd.bnd_fold_norm_quant_fp8(s, bnd.BND_OWED_NONE, w, d["eps"], q.view, sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y3.view), bits(y.view))
+    assert np.array_equal(bits(res.view), ref["residual"]), "a Written read must not update"
+    rq = orc.fold_norm([np.zeros((T, H), np.uint16)], ref["residual"], w.cpu().numpy(), d["eps"],
+                       fp8=True)
+    tolerance.check_fp8(q.view.cpu().numpy(), rq["q"], "written fp8 q")
+    tolerance.check_scale(sc.cpu().numpy(), rq["scale"], "written fp8 scale")
+
+
+def test_prefill_full(orc):
+    d = workloads.prefill()
+    got, _ = assert_fold_matches(orc, d, "prefill T=2048 H=4096 P=8")
+    again = run_fold(d)
+    assert torch.equal(again["y"].buf, got["y"].buf), "run-to-run results must be bitwise equal"
+    assert torch.equal(again["res"].buf, got["res"].buf)
+
+
+def test_quantised_full(orc):
+    assert_fold_matches(orc, workloads.quantised(), "fp8 T=2048 H=7168 P=8 outliers", fp8=True)
+
+
+def _moe_device(d):
+    return (d["expert_rows"].to(DEV), d["idx"].to(DEV), d["gate"].to(DEV))
+
+
+def run_moe(orc, d, row_begin, rows, what):
+    T, H, k = d["T"], d["H"], d["k"]
+    E, idx, gate = _moe_device(d)
+    res = Guarded(rows, H).from_host(d["residual"][row_begin:row_begin + rows])
+    y = Guarded(rows, H)
+    w = d["weight"].to(DEV)
+    s = bnd.bnd_stream_create(T, H, res.view, row_begin, rows)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_moe(s, E, idx, gate, k)
+    bnd.bnd_moe_finalize_fold_norm(s, owed, w, d["eps"], y.view)
+    torch.cuda.synchronize()
+    assert s.state == bnd.BND_WRITTEN
+    ref = orc.moe_fold_norm(bits(d["expert_rows"]), d["idx"].numpy(), d["gate"].numpy(), k,
+                            bits(d["residual"][row_begin:row_begin + rows]), d["weight"].numpy(),
+                            d["eps"], row_begin=row_begin, rows=rows)
+    res.check_guards(f"{what} residual")
+    y.check_guards(f"{what} y")
+    check_fold(ref, bits(res.view), bits(y.view), d["weight"].numpy(), d["eps"], what)
+    return res, y
+
+
+def test_moe_full_and_slice(orc):
+    d = workloads.moe()
+    full_res, full_y = run_moe(orc, d, 0, d["T"], "MoE T=2048 H=4096 k=8")
+    rb, rows = workloads.MOE_SLICE
+    sl_res, sl_y = run_moe(orc, d, rb, rows, "MoE slice rows 768..1023")
+    # the slice computes exactly the same rows as the full call
+    assert torch.equal(sl_y.view, full_y.view[rb:rb + rows])
+    assert torch.equal(sl_res.view, full_res.view[rb:rb + rows])
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 128])
+def test_decode_chain(orc, T):
+    """1 enter + 96 folds (2 boundaries x 48 layers), each boundary with fresh partials."""
+    H, P, n_b = 4096, 4, 96
+    start = workloads.decode_start(T, H)
+    res = Guarded(T, H)
+    y = Guarded(T, H)
+    s = bnd.bnd_stream_create(T, H, res.view)
+    w0 = start["weight"].to(DEV)
+    bnd.bnd_enter_norm(s, start["x_in"].to(DEV), w0, 1e-6, y.view)
+    ref = orc.enter_norm(bits(start["x_in"]), start["weight"].numpy(), 1e-6)
+    o_res = ref["residual"]
+    torch.cuda.synchronize()
+    tolerance.check_bf16(bits(y.view), ref["y_exact"], np.zeros((T, H)), f"decode T={T} enter")
+    worst_res = worst_y = 0.0
+    for b in range(n_b):
+        d = workloads.decode_boundary(T, b, P, H)
+        parts = [c.to(DEV) for c in d["partials"]]
+        owed = bnd.bnd_publish_partials(s, parts)
+        bnd.bnd_fold_norm(s, owed, d["weight"].to(DEV), d["eps"], y.view)
+        torch.cuda.synchronize()
+        r = orc.fold_norm([bits(c) for c in d["partials"]], o_res, d["weight"].numpy(), d["eps"])
+        a = tolerance.check_bf16(bits(res.view), r["x_exact"], r["mag"], f"decode T={T} b={b} residual")
+        c = tolerance.check_bf16(bits(y.view), r["y_exact"],
+                                 tolerance.read_s_term(r["x_exact"], r["mag"], d["weight"].numpy(),
+                                                       d["eps"]), f"decode T={T} b={b} y")
+        worst_res = max(worst_res, a["max_err_ulp"])
+        worst_y = max(worst_y, c["max_err_ulp"])
+        o_res = r["residual"]
+    res.check_guards("decode residual")
+    y.check_guards("decode y")
+    print(f"\n  decode T={T}: 96 folds, worst residual {worst_res:.3f} ulp, worst y {worst_y:.3f} ulp",
+          flush=True)
+
+
+# ------------------------------------------------------------------ shapes and edge cases
+
+SHAPES = [  # T, H, P, pad, row_begin, rows
+    (1, 8, 1, 0, 0, None),
+    (3, 264, 3, 8, 0, None),
+    (37, 4104, 8, 0, 0, None),
+    (6, 7168, 16, 16, 1, 4),
+    (2, 32768, 2, 0, 0, None),
+    (64, 512, 5, 0, 0, None),
+    (5, 16384, 9, 0, 0, None),
+    (9, 1016, 13, 0, 0, None),
+]
+
+
+@pytest.mark.parametrize("T,H,P,pad,rb,rows", SHAPES)
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_shapes(orc, T, H, P, pad, rb, rows, fp8):
+    d = workloads.fold_inputs(100 + T + H + P, T, H, P)
+    assert_fold_matches(orc, d, f"T={T} H={H} P={P} pad={pad} slice={rb}+{rows}", fp8=fp8, pad=pad,
+                        row_begin=rb, rows=rows)
+
+
+@pytest.mark.parametrize("threads,vpt", [(128, 4), (256, 2), (256, 4), (512, 1), (1024, 1),
+                                         (320, 2), (192, 4)])
+def test_launch_shapes(orc, threads, vpt):
+    bnd.set_option(bnd.BND_OPT_THREADS_PER_ROW, threads)
+    bnd.set_option(bnd.BND_OPT_VECTORS_PER_THREAD, vpt)
+    d = workloads.fold_inputs(7, 33, 4096, 8)
+    assert_fold_matches(orc, d, f"launch {threads}x{vpt}")
+    assert_fold_matches(orc, d, f"launch {threads}x{vpt} fp8", fp8=True)
+
+
+def test_pending_without_residual(orc):
+    d = workloads.fold_inputs(8, 12, 1024, 3)
+    assert_fold_matches(orc, d, "no residual", with_residual=False)
+
+
+def test_outlier_and_zero_rows(orc):
+    d = workloads.fold_inputs(9, 6, 2048, 2)
+    z = torch.zeros(6, 2048, dtype=torch.bfloat16)
+    d["residual"] = d["residual"].clone()
+    d["residual"][2] = 0
+    d["partials"] = [c.clone() for c in d["partials"]]
+    for c in d["partials"]:
+        c[2] = 0
+        c[4, 100] = 3.0e4
+    d["residual"][4, 101] = -2.5e-6
+    assert_fold_matches(orc, d, "zero and outlier rows", fp8=True)
+    assert_fold_matches(orc, d, "zero and outlier rows bf16")
+    del z
+
+
+def test_moe_edge_cases(orc):
+    d = workloads.moe_inputs(11, 40, 1024, 16, 16)  # k = 16 of 16 experts
+    idx = d["idx"].clone()
+    idx[5] = -1                         # a corrupt index contributes nothing
+    idx[17] = d["expert_rows"].shape[0]
+    d["idx"] = idx
+    run_moe(orc, d, 0, 40, "MoE k=16 with out-of-range indices")
+    d1 = workloads.moe_inputs(12, 9, 264, 4, 1)  # k = 1, ragged H
+    run_moe(orc, d1, 3, 5, "MoE k=1 slice")
+
+
+# ------------------------------------------------------------------ invariants on device
+
+def test_invariant_zero_contribution_is_enter(orc):
+    d = workloads.fold_inputs(21, 10, 4096, 1)
+    T, H = 10, 4096
+    zero = [torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)]
+    a = run_fold(d, partials=zero)
+    res = Guarded(T, H)
+    y = Guarded(T, H)
+    s = bnd.bnd_stream_create(T, H, res.view)
+    bnd.bnd_enter_norm(s, d["residual"].to(DEV), d["weight"].to(DEV), d["eps"], y.view)
+    torch.cuda.synchronize()
+    assert torch.equal(a["y"].view, y.view) and torch.equal(a["res"].view, res.view)
+
+
+def test_invariant_written_fold_applies_no_second_update(orc):
+    d = workloads.fold_inputs(22, 16, 4096, 4)
+    got = run_fold(d)
+    s = got["stream"]
+    before = got["res"].view.clone()
+    y2 = Guarded(16, 4096)
+    bnd.bnd_fold_norm(s, bnd.BND_OWED_NONE, d["weight"].to(DEV), d["eps"], y2.view)
+    torch.cuda.synchronize()
+    assert torch.equal(got["res"].view, before), "a second read must not fold again"
+    ref = oracle_fold(orc, d)
+    again = orc.written_norm(ref["residual"], d["weight"].numpy(), d["eps"])
+    tolerance.check_bf16(bits(y2.view), again["y_exact"], np.zeros((16, 4096)), "written read y")
+
+
+def test_invariant_moe_over_stacked_partials_is_fold(orc):
+    d = workloads.fold_inputs(23, 24, 2048, 4)
+    T, H, P = 24, 2048, 4
+    a = run_fold(d)
+    E = torch.cat([c for c in d["partials"]], 0).to(DEV)
+    idx = torch.tensor([[p * T + t for p in range(P)] for t in range(T)], dtype=torch.int32,
+                       device=DEV).reshape(-1)
+    gate = torch.ones(T * P, dtype=torch.float32, device=DEV)
+    res = Guarded(T, H).from_host(d["residual"])
+    y = Guarded(T, H)
+    s = bnd.bnd_stream_create(T, H, res.view)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_moe(s, E, idx, gate, P)
+    bnd.bnd_moe_finalize_fold_norm(s, owed, d["weight"].to(DEV), d["eps"], y.view)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view, a["y"].view) and torch.equal(res.view, a["res"].view)
+
+
+def test_invariant_slice_equals_full_rows(orc):
+    d = workloads.fold_inputs(24, 64, 4096, 8)
+    full = run_fold(d)
+    for rb, rows in ((0, 8), (24, 16), (56, 8), (63, 1)):
+        part = run_fold(d, row_begin=rb, rows=rows)
+        assert torch.equal(part["y"].view, full["y"].view[rb:rb + rows])
+        assert torch.equal(part["res"].view, full["res"].view[rb:rb + rows])
+
+
+# ------------------------------------------------------------------ unfused fallback
+
+def test_complete_only_then_one_source_fold(orc):
+    d = workloads.fold_inputs(31, 20, 4096, 8)
+    T, H = 20, 4096
+    bnd.set_option(bnd.BND_OPT_FUSED_UNAVAILABLE, 1)
+    res = Guarded(T, H).from_host(d["residual"])
+    y = Guarded(T, H)
+    out = Guarded(T, H)
+    w = d["weight"].to(DEV)
+    s = bnd.bnd_stream_create(T, H, res.view)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_partials(s, [c.to(DEV) for c in d["partials"]])
+    with pytest.raises(bnd.BoundaryError) as e:
+        bnd.bnd_fold_norm(s, owed, w, d["eps"], y.view)
+    assert e.value.status == bnd.BND_ERR_UNAVAILABLE
+    owed2 = bnd.bnd_complete_only(s, owed, out.view)
+    assert s.state == bnd.BND_PENDING
+    bnd.bnd_fold_norm(s, owed2, w, d["eps"], y.view)
+    torch.cuda.synchronize()
+    for g in (res, y, out):
+        g.check_guards("fallback")
+    c = orc.complete_partials([bits(p) for p in d["partials"]])
+    tolerance.check_bf16(bits(out.view), c["s_exact"], c["mag"], "complete_only out")
+    ref = orc.fold_norm([c["out"]], bits(d["residual"]), d["weight"].numpy(), d["eps"])
+    check_fold(ref, bits(res.view), bits(y.view), d["weight"].numpy(), d["eps"], "unfused fallback")
+
+
+def test_moe_complete_only(orc):
+    d = workloads.moe_inputs(32, 48, 2048, 32, 8)
+    T, H, k = 48, 2048, 8
+    E, idx, gate = _moe_device(d)
+    rb, rows = 16, 24
+    res = Guarded(rows, H).from_host(d["residual"][rb:rb + rows])
+    out = Guarded(rows, H)
+    y = Guarded(rows, H)
+    s = bnd.bnd_stream_create(T, H, res.view, rb, rows)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_moe(s, E, idx, gate, k)
+    owed2 = bnd.bnd_complete_only(s, owed, out.view)
+    assert s.pending_kind == bnd.BND_KIND_PARTIALS
+    bnd.bnd_fold_norm(s, owed2, d["weight"].to(DEV), d["eps"], y.view)
+    torch.cuda.synchronize()
+    c = orc.complete_moe(bits(d["expert_rows"]), d["idx"].numpy(), d["gate"].numpy(), k,
+                         row_begin=rb, rows=rows)
+    tolerance.check_bf16(bits(out.view), c["s_exact"], c["mag"], "MoE complete_only out")
+    ref = orc.fold_norm([c["out"]], bits(d["residual"][rb:rb + rows]), d["weight"].numpy(),
+                        d["eps"])
+    check_fold(ref, bits(res.view), bits(y.view), d["weight"].numpy(), d["eps"], "MoE unfused")
+
+
+# ------------------------------------------------------------------ errors and empty batches
+
+def test_refused_call_writes_nothing(orc):
+    d = workloads.fold_inputs(41, 8, 1024, 2)
+    res = Guarded(8, 1024).from_host(d["residual"])
+    y = Guarded(8, 1024)
+    s = bnd.bnd_stream_create(8, 1024, res.view)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_partials(s, [c.to(DEV) for c in d["partials"]])
+    res_before = res.buf.clone()
+    y_before = y.buf.clone()
+    w = d["weight"].to(DEV)
+    bad_y = y.buf.view(-1)[1:1 + 8 * 1024].view(8, 1024)  # misaligned by one element
+    for call in (lambda: bnd.bnd_fold_norm(s, owed + 1, w, d["eps"], y.view),
+                 lambda: bnd.bnd_fold_norm(s, owed, w, -1.0, y.view),
+                 lambda: bnd.bnd_fold_norm(s, owed, w, d["eps"], bad_y),
+                 lambda: bnd.bnd_fold_norm(s, owed, w, d["eps"], res.view),
+                 lambda: bnd.bnd_moe_finalize_fold_norm(s, owed, w, d["eps"], y.view)):
+        with pytest.raises(bnd.BoundaryError):
+            call()
+    torch.cuda.synchronize()
+    assert torch.equal(res.buf, res_before) and torch.equal(y.buf, y_before)
+    assert s.state == bnd.BND_PENDING
+    bnd.bnd_fold_norm(s, owed, w, d["eps"], y.view)
+    torch.cuda.synchronize()
+    assert not torch.equal(y.buf, y_before)
+
+
+def test_empty_batch_applies_transitions(orc):
+    H = 4096
+    s = bnd.bnd_stream_create(0, H, None)
+    owed = bnd.bnd_publish_partials(s, [torch.empty(0, H, dtype=torch.bfloat16, device=DEV)] * 2)
+    bnd.bnd_fold_norm(s, owed, torch.empty(H, device=DEV), 1e-6,
+                      torch.empty(0, H, dtype=torch.bfloat16, device=DEV))
+    assert s.state == bnd.BND_WRITTEN
+    bnd.bnd_take_output(s)
+    assert s.state == bnd.BND_INITIAL
+
+
+def test_enter_aliasing_input_and_residual(orc):
+    d = workloads.tiny()
+    T, H = d["T"], d["H"]
+    x = Guarded(T, H).from_host(d["x_in"])
+    y = Guarded(T, H)
+    s = bnd.bnd_stream_create(T, H, x.view)
+    bnd.bnd_enter_norm(s, x.view, d["weight"].to(DEV), d["eps"], y.view)
+    torch.cuda.synchronize()
+    ref = orc.enter_norm(bits(d["x_in"]), d["weight"].numpy(), d["eps"])
+    assert np.array_equal(bits(x.view), bits(d["x_in"]))
+    tolerance.check_bf16(bits(y.view), ref["y_exact"], np.zeros((T, H)), "aliased enter y")
