@@ -64,28 +64,68 @@ def traffic_from_profiles(workload: str):
 # timing harness
 # --------------------------------------------------------------------------
 
-class Timed:
-    """Runs step(i) with HIP events around each launch on the current stream."""
+class HipEvents:
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
 
-    def __init__(self, torch):
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+
+    def elapsed_s(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e-3
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+class Timed:
+    """Runs step(i, start, stop) K times. Every `sample_every`-th launch of the
+    timed region records start/stop events from its own dispatch
+    (bnd_time_next_launch -> hipExtLaunchKernel) on the stream it runs on; the
+    event packets add a few microseconds of queue gap, so sampling keeps the
+    wall-clock rate of the timed region close to an unobserved run."""
+
+    def __init__(self, torch, bnd, sample_every: int = 8):
         self.torch = torch
+        self.L = bnd.lib()
+        self.sample_every = sample_every
 
     def run(self, step, n_sets: int, warmup: int, steps: int):
         torch = self.torch
         for i in range(warmup):
             step(i % n_sets, None, None)
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        sampled = list(range(0, steps, self.sample_every))
+        ev = HipEvents(2 * len(sampled))
+        slot = {i: n for n, i in enumerate(sampled)}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            step((warmup + i) % n_sets, starts[i], ends[i])
+            n = slot.get(i)
+            if n is None:
+                step((warmup + i) % n_sets, None, None)
+            else:
+                step((warmup + i) % n_sets, ev.ev[2 * n], ev.ev[2 * n + 1])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
-        durs.sort()
+        durs = sorted(ev.elapsed_s(2 * n, 2 * n + 1) for n in range(len(sampled)))
+        ev.close()
         return {
             "wall_s": wall,
+            "samples": len(durs),
             "kernel_mean_s": sum(durs) / len(durs),
             "kernel_median_s": durs[len(durs) // 2],
             "kernel_p10_s": durs[len(durs) // 10],
@@ -124,7 +164,7 @@ def fold_case(torch, bnd, d, n_sets, fp8=False, row_begin=0, rows=None):
         st, parts, res, out, arr = sets[i]
         rc = L.bnd_publish_partials(st.handle, arr, P, H, ctypes.byref(owed))
         if ev0 is not None:
-            ev0.record()
+            rc |= L.bnd_time_next_launch(ev0, ev1)
         if fp8:
             rc |= L.bnd_fold_norm_quant_fp8(st.handle, owed.value, wptr, eps,
                                             ctypes.c_void_p(out[0].data_ptr()), H,
@@ -132,8 +172,6 @@ def fold_case(torch, bnd, d, n_sets, fp8=False, row_begin=0, rows=None):
         else:
             rc |= L.bnd_fold_norm(st.handle, owed.value, wptr, eps,
                                   ctypes.c_void_p(out[0].data_ptr()), H, hs)
-        if ev1 is not None:
-            ev1.record()
         if rc:
             raise RuntimeError(L.bnd_last_error().decode())
 
@@ -173,11 +211,9 @@ def moe_case(torch, bnd, d, n_sets, row_begin=0, rows=None):
         rc = L.bnd_publish_moe(st.handle, ctypes.c_void_p(E.data_ptr()), E.shape[0], H, iptr, gptr, k,
                                ctypes.byref(owed))
         if ev0 is not None:
-            ev0.record()
+            rc |= L.bnd_time_next_launch(ev0, ev1)
         rc |= L.bnd_moe_finalize_fold_norm(st.handle, owed.value, wptr, eps,
                                            ctypes.c_void_p(y.data_ptr()), H, hs)
-        if ev1 is not None:
-            ev1.record()
         if rc:
             raise RuntimeError(L.bnd_last_error().decode())
 
@@ -288,10 +324,12 @@ def cpu_baseline(workloads, d, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true", help="only the prefill step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--with-copy", action="store_true",
+                    help="also run the 1 GiB reference copy (a known byte count for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
@@ -310,7 +348,7 @@ def main():
         __graft_entry__.build()
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
-    timer = Timed(torch)
+    timer = Timed(torch, bnd)
     props = torch.cuda.get_device_properties(0)
 
     log("generating the prefill workload (T=2048 H=4096 P=8)")
@@ -337,12 +375,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill boundary fold+RMSNorm, T=2048 H=4096 P=8, bf16 in/out",
                    "T": 2048, "H": 4096, "P": 8, "rotation_sets": n_sets,
-                   "device": props.name, "storage": "bf16"},
+                   "device": getattr(props, "gcnArchName", props.name), "storage": "bf16"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "kernel": "read_kernel<Partials, 8, 1, bf16>",
                      "algorithmic_bytes": nbytes,
                      "kernel_mean_us": t["kernel_mean_s"] * 1e6,
+                     "timed_launches": t["samples"],
                      "kernel_median_us": t["kernel_median_s"] * 1e6,
                      "kernel_p10_us": t["kernel_p10_s"] * 1e6,
                      "kernel_p90_us": t["kernel_p90_s"] * 1e6},
@@ -385,6 +424,8 @@ def main():
         sec["copy_ceiling_1GiB"] = copy_ceiling(torch)
         result["secondary"] = sec
 
+    if args.no_secondary and args.with_copy:
+        result["copy_reference_1GiB"] = copy_ceiling(torch)
     log(f"CPU baseline: the oracle for ~{args.cpu_seconds:.0f} s")
     result["cpu_baseline"] = cpu_baseline(workloads, d, args.cpu_seconds)
     print(json.dumps(result), flush=True)

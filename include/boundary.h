@@ -235,6 +235,14 @@ typedef enum bnd_option {
 BND_API bnd_status bnd_set_option(bnd_option opt, int64_t value);
 BND_API int64_t bnd_get_option(bnd_option opt);
 
+/* Timing: the calling thread's next kernel launch records `start_event` and
+ * `stop_event` (hipEvent_t, created by the caller) from its own dispatch
+ * (hipExtLaunchKernel), so hipEventElapsedTime between them is that
+ * kernel's execution time without queue gaps. The events are used by exactly
+ * one launch (a call that launches nothing leaves them armed); NULL, NULL
+ * disarms. Not for use while a HIP graph is being captured. */
+BND_API bnd_status bnd_time_next_launch(void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

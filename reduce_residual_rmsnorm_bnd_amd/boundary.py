@@ -46,7 +46,7 @@ SYMBOLS = [
     "bnd_stream_has_residual", "bnd_publish_partials", "bnd_publish_moe", "bnd_enter_norm",
     "bnd_fold_norm", "bnd_fold_norm_quant_fp8", "bnd_moe_finalize_fold_norm", "bnd_complete_only",
     "bnd_written", "bnd_take_output", "bnd_status_str", "bnd_last_error", "bnd_version",
-    "bnd_set_option", "bnd_get_option",
+    "bnd_set_option", "bnd_get_option", "bnd_time_next_launch",
 ]
 
 _lib = None
@@ -84,6 +84,7 @@ def _declare(lib):
         "bnd_version": (c.c_char_p, []),
         "bnd_set_option": (st, [c.c_int, i64]),
         "bnd_get_option": (i64, [c.c_int]),
+        "bnd_time_next_launch": (st, [vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -20,6 +20,7 @@
 // No atomics: the result is bitwise reproducible run to run.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,9 +34,41 @@ namespace bnd {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// ---------------------------------------------------------------------------
+// Row access through buffer resources. Every row operand gets a resource whose
+// base is the row and whose size is the row's bytes, so each access is
+// bounds-checked by the hardware (an out-of-range load returns 0 and an
+// out-of-range store is dropped) on top of the explicit lane guards.
+// Cache policy: rows are read exactly once, so loads are non-temporal (nt);
+// stores carry sc1 (write-through past the XCD's L2). Both measured faster on
+// MI355X than the default policy for this 9:2 read:write stream.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void store16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor: 32-bit data format, raw addressing
+constexpr int kLoadOnce = 2;            // cache policy bits: nt
+constexpr int kStoreStream = 16;        // cache policy bits: sc1
+
+__device__ __forceinline__ Rsrc row_rsrc(const void* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 load16(Rsrc r, int byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kLoadOnce);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store16(Rsrc r, int byte_off, uint4 v) {
+  const u32x4 u = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, byte_off, 0, kStoreStream);
+}
+
+__device__ __forceinline__ void store8(Rsrc r, int byte_off, uint2 v) {
+  const u32x2 u = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, byte_off, 0, kStoreStream);
+}
 
 __device__ __forceinline__ void bf16x8_to_f32(uint4 v, float f[8]) {
   f[0] = __uint_as_float(v.x << 16);
@@ -136,37 +169,63 @@ __device__ __forceinline__ void block_reduce(float& ss, float& mx, float* lds_su
 // Loading and completing the contribution of one row: x[v][e] for the
 // thread's VPT vectors. Lanes past the end of the row hold zeros.
 // ---------------------------------------------------------------------------
+
+// Loads are issued by every lane without a guard: a lane past the end of the
+// row addresses beyond its row resource and reads 0, which keeps the loads
+// branch-free so they can all be in flight together.
+//
+// Vectors whose source loads are in flight together. A batch of kb vectors
+// holds 4*(N+1)*kb VGPRs of raw loads next to the row's fp32 values and
+// weights (16*VPT); the largest kb <= VPT that keeps the estimate within the
+// 128 VGPRs of a 1024-thread workgroup avoids scratch spills.
+constexpr int load_batch(int n, int vpt) {
+  for (int kb = vpt; kb > 1; kb /= 2)
+    if (4 * (n + 1) * kb + 16 * vpt + 12 <= 128) return kb;
+  return 1;
+}
 // kFold = false computes the contribution s alone (complete_only).
 template <Source S, int N, int VPT, bool kFold = true>
 __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int tid, int nthr,
                                               const bool (&ok)[VPT], float (&x)[VPT][8]) {
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  const int row_bytes = a.H * 2;
+  int off[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) off[v] = (tid + v * nthr) * 16;
+  const Rsrc res = row_rsrc(a.res + row * a.ld_res, row_bytes);
+  // the residual as a fold input: an empty resource (loads read 0) when the
+  // stream is Pending without a residual
+  const Rsrc res_in = row_rsrc(a.res + row * a.ld_res, a.has_residual ? row_bytes : 0);
   if constexpr (S == Source::Partials) {
-    uint4 c[N][VPT];
-    uint4 r[VPT];
+    constexpr int kB = load_batch(N, VPT);
 #pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const uint16_t* base = a.src[p] + row * a.ld_src;
+    for (int v0 = 0; v0 < VPT; v0 += kB) {
+      uint4 c[N][kB];
+      uint4 r[kB];
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) c[p][v] = ok[v] ? load16(base + (int64_t)(tid + v * nthr) * 8) : zero;
-    }
+      for (int p = 0; p < N; ++p) {
+        const Rsrc src = row_rsrc(a.src[p] + row * a.ld_src, row_bytes);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v)
-      r[v] = (kFold && ok[v] && a.has_residual) ? load16(a.res + row * a.ld_res + (int64_t)(tid + v * nthr) * 8)
-                                       : zero;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      float s[8], t[8], rv[8];
-      bf16x8_to_f32(c[0][v], s);
-#pragma unroll
-      for (int p = 1; p < N; ++p) {
-        bf16x8_to_f32(c[p][v], t);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] += t[e];
+        for (int b = 0; b < kB; ++b) c[p][b] = load16(src, off[v0 + b]);
       }
-      bf16x8_to_f32(r[v], rv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[v][e] = rv[e] + s[e];
+      for (int b = 0; b < kB; ++b) r[b] = kFold ? load16(res_in, off[v0 + b]) : zero;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        float s[8], t[8], rv[8];
+        bf16x8_to_f32(c[0][b], s);
+#pragma unroll
+        for (int p = 1; p < N; ++p) {
+          bf16x8_to_f32(c[p][b], t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[e] += t[e];
+        }
+        bf16x8_to_f32(r[b], rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[v0 + b][e] = rv[e] + s[e];
+      }
+      // keep the next batch's loads behind this batch's sums (register budget)
+      if constexpr (kB < VPT) __builtin_amdgcn_sched_barrier(0);
     }
   } else if constexpr (S == Source::Moe) {
     int64_t er[N];
@@ -178,42 +237,46 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
       er[j] = valid ? e : -1;
       g[j] = a.gate[row * N + j];
     }
-    uint4 c[N][VPT];
-    uint4 r[VPT];
+    constexpr int kB = load_batch(N, VPT);
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const uint16_t* base = a.experts + (er[j] < 0 ? 0 : er[j]) * a.ld_e;
-#pragma unroll
-      for (int v = 0; v < VPT; ++v)
-        c[j][v] = (ok[v] && er[j] >= 0) ? load16(base + (int64_t)(tid + v * nthr) * 8) : zero;
-    }
-#pragma unroll
-    for (int v = 0; v < VPT; ++v)
-      r[v] = (kFold && ok[v] && a.has_residual) ? load16(a.res + row * a.ld_res + (int64_t)(tid + v * nthr) * 8)
-                                       : zero;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      float s[8], t[8], rv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+    for (int v0 = 0; v0 < VPT; v0 += kB) {
+      uint4 c[N][kB];
+      uint4 r[kB];
 #pragma unroll
       for (int j = 0; j < N; ++j) {
-        bf16x8_to_f32(c[j][v], t);
+        // an invalid pick gets an empty resource: its loads return 0 and it is skipped anyway
+        const Rsrc src = row_rsrc(a.experts + (er[j] < 0 ? 0 : er[j]) * a.ld_e, er[j] < 0 ? 0 : row_bytes);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] = fmaf(g[j], t[e], s[e]);
+        for (int b = 0; b < kB; ++b) c[j][b] = load16(src, off[v0 + b]);
       }
-      bf16x8_to_f32(r[v], rv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[v][e] = rv[e] + s[e];
+      for (int b = 0; b < kB; ++b) r[b] = kFold ? load16(res_in, off[v0 + b]) : zero;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        float s[8], t[8], rv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          bf16x8_to_f32(c[j][b], t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[e] = fmaf(g[j], t[e], s[e]);
+        }
+        bf16x8_to_f32(r[b], rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[v0 + b][e] = rv[e] + s[e];
+      }
+      // keep the next batch's loads behind this batch's sums (register budget)
+      if constexpr (kB < VPT) __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     // Input: the stack input x_in (enter); Residual: the stored residual (written read)
-    const uint16_t* base = (S == Source::Input) ? a.x_in + row * a.ld_x : a.res + row * a.ld_res;
+    const Rsrc src = (S == Source::Input) ? row_rsrc(a.x_in + row * a.ld_x, row_bytes) : res;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-      const uint4 raw = ok[v] ? load16(base + (int64_t)(tid + v * nthr) * 8) : zero;
+      const uint4 raw = load16(src, off[v]);
       if constexpr (S == Source::Input) {
-        if (ok[v] && a.copy_input) store16(a.res + row * a.ld_res + (int64_t)(tid + v * nthr) * 8, raw);
+        if (ok[v] && a.copy_input) store16(res, off[v], raw);
       }
       bf16x8_to_f32(raw, x[v]);
     }
@@ -221,18 +284,18 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
 }
 
 template <int VPT>
-__device__ __forceinline__ void load_weight(const RowArgs& a, int tid, int nthr, const bool (&ok)[VPT],
-                                            float (&w)[VPT][8]) {
+__device__ __forceinline__ void load_weight(const RowArgs& a, int tid, int nthr, float (&w)[VPT][8]) {
+  // the weight is shared by all rows: default cache policy, it stays in L2
+  const Rsrc wr = row_rsrc(a.w, a.H * 4);
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
-    if (ok[v]) {
-      const float4* p = reinterpret_cast<const float4*>(a.w + (int64_t)(tid + v * nthr) * 8);
-      lo = p[0];
-      hi = p[1];
-    }
-    w[v][0] = lo.x; w[v][1] = lo.y; w[v][2] = lo.z; w[v][3] = lo.w;
-    w[v][4] = hi.x; w[v][5] = hi.y; w[v][6] = hi.z; w[v][7] = hi.w;
+    const int off = (tid + v * nthr) * 32;
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16, 0, 0);
+    w[v][0] = __uint_as_float(lo.x); w[v][1] = __uint_as_float(lo.y);
+    w[v][2] = __uint_as_float(lo.z); w[v][3] = __uint_as_float(lo.w);
+    w[v][4] = __uint_as_float(hi.x); w[v][5] = __uint_as_float(hi.y);
+    w[v][6] = __uint_as_float(hi.z); w[v][7] = __uint_as_float(hi.w);
   }
 }
 
@@ -252,8 +315,10 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
 
   float x[VPT][8];
   load_and_fold<S, N, VPT>(a, row, tid, nthr, ok, x);
+  // with four vectors per thread the weights wait until the loads are summed
+  if constexpr (VPT >= 4) __builtin_amdgcn_sched_barrier(0);
   float w[VPT][8];
-  load_weight<VPT>(a, tid, nthr, ok, w);
+  load_weight<VPT>(a, tid, nthr, w);
 
   float ss = 0.0f, mx = 0.0f;
 #pragma unroll
@@ -269,25 +334,29 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
   block_reduce<FP8>(ss, mx, lds_sum, lds_max);
   const float inv = 1.0f / sqrtf(ss / (float)a.H + a.eps);
 
+  const int row_bytes = a.H * 2;
   if constexpr (S == Source::Partials || S == Source::Moe) {
+    const Rsrc res = row_rsrc(a.res + row * a.ld_res, row_bytes);
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
-      if (ok[v]) store16(a.res + row * a.ld_res + (int64_t)(tid + v * nthr) * 8, f32_to_bf16x8(x[v]));
+      if (ok[v]) store16(res, (tid + v * nthr) * 16, f32_to_bf16x8(x[v]));
   }
 
   if constexpr (!FP8) {
+    const Rsrc yr = row_rsrc(a.y + row * a.ld_y, row_bytes);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = (x[v][e] * inv) * w[v][e];
-      if (ok[v]) store16(a.y + row * a.ld_y + (int64_t)(tid + v * nthr) * 8, f32_to_bf16x8(y));
+      if (ok[v]) store16(yr, (tid + v * nthr) * 16, f32_to_bf16x8(y));
     }
   } else {
     // y_h = (x_h w_h) inv. Rounding is monotone, so max_h |y_h| is exactly
     // (max_h |x_h w_h|) inv: the scale is fp32(max|y| / 448) of these y.
     const float amax = mx * inv;
     const float scale = amax / 448.0f;
+    const Rsrc qr = row_rsrc(a.q + row * a.ld_q, a.H);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       float t[8];
@@ -297,7 +366,7 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
         const float u = scale > 0.0f ? y / scale : 0.0f;
         t[e] = fminf(fmaxf(u, -448.0f), 448.0f);
       }
-      if (ok[v]) *reinterpret_cast<uint2*>(a.q + row * a.ld_q + (int64_t)(tid + v * nthr) * 8) = f32_to_e4m3x8(t);
+      if (ok[v]) store8(qr, (tid + v * nthr) * 8, f32_to_e4m3x8(t));
     }
     if (tid == 0) a.scale[row] = scale;
   }
@@ -314,9 +383,10 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
   for (int v = 0; v < VPT; ++v) ok[v] = (tid + v * nthr) < a.nvec;
   float s[VPT][8];
   load_and_fold<S, N, VPT, false>(a, row, tid, nthr, ok, s);
+  const Rsrc out = row_rsrc(a.y + row * a.ld_y, a.H * 2);
 #pragma unroll
   for (int v = 0; v < VPT; ++v)
-    if (ok[v]) store16(a.y + row * a.ld_y + (int64_t)(tid + v * nthr) * 8, f32_to_bf16x8(s[v]));
+    if (ok[v]) store16(out, (tid + v * nthr) * 16, f32_to_bf16x8(s[v]));
 }
 
 // ---------------------------------------------------------------------------
@@ -337,6 +407,9 @@ constexpr std::array<KernelFn, sizeof...(I)> complete_table(std::integer_sequenc
 inline hipError_t launch_kernel(KernelFn fn, const RowArgs& a, const Launch& l, hipStream_t stream) {
   RowArgs copy = a;
   void* args[] = {&copy};
+  if (l.start || l.stop)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)l.rows), dim3((unsigned)l.threads),
+                              args, 0, stream, l.start, l.stop, 0);
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)l.rows), dim3((unsigned)l.threads),
                          args, 0, stream);
 }

@@ -43,6 +43,8 @@ struct Launch {
   int rows;     // grid size
   int threads;  // workgroup size, multiple of 64
   int vpt;      // 16-byte vectors per thread: 1, 2 or 4
+  hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
+  hipEvent_t stop = nullptr;
 };
 
 enum class Source { Partials, Moe, Input, Residual };
