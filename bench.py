@@ -378,10 +378,11 @@ def main():
                    "device": getattr(props, "gcnArchName", props.name), "storage": "bf16"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "read_kernel<Partials, 8, 1, bf16>",
+                     "kernel": "read_kernel<Partials, P=8, bf16 out> (bnd_fold_norm)",
                      "algorithmic_bytes": nbytes,
                      "kernel_mean_us": t["kernel_mean_s"] * 1e6,
                      "timed_launches": t["samples"],
+                     "steady_state_us_per_launch": t["wall_s"] / args.steps * 1e6,
                      "kernel_median_us": t["kernel_median_s"] * 1e6,
                      "kernel_p10_us": t["kernel_p10_s"] * 1e6,
                      "kernel_p90_us": t["kernel_p90_s"] * 1e6},
