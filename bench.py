@@ -182,7 +182,10 @@ def fold_case(torch, bnd, d, n_sets, fp8=False, row_begin=0, rows=None):
     return step, read + write, keep
 
 
-def moe_case(torch, bnd, d, n_sets, row_begin=0, rows=None):
+def moe_case(torch, bnd, d, n_sets, row_begin=0, rows=None, terminal_gemma=False):
+    """MoE finalize sets; with terminal_gemma the streams use the Gemma weight form and each
+    step releases the stream after the finalize (the final norm of a stack), then marks the
+    residual written again for the next step (host-only calls)."""
     T, H, k = d["T"], d["H"], d["k"]
     rows = T - row_begin if rows is None else rows
     dev = torch.device("cuda:0")
@@ -197,6 +200,8 @@ def moe_case(torch, bnd, d, n_sets, row_begin=0, rows=None):
         E = E0 if s_i == 0 else E0.clone()
         res = res0.clone()
         st = bnd.bnd_stream_create(T, H, res, row_begin, rows)
+        if terminal_gemma:
+            bnd.bnd_stream_set_norm_form(st, bnd.BND_NORM_GEMMA)
         bnd.bnd_written(st, res)
         y = torch.empty(rows, H, dtype=torch.bfloat16, device=dev)
         sets.append((st, E, res, y))
@@ -214,6 +219,9 @@ def moe_case(torch, bnd, d, n_sets, row_begin=0, rows=None):
             rc |= L.bnd_time_next_launch(ev0, ev1)
         rc |= L.bnd_moe_finalize_fold_norm(st.handle, owed.value, wptr, eps,
                                            ctypes.c_void_p(y.data_ptr()), H, hs)
+        if terminal_gemma:
+            rc |= L.bnd_take_output(st.handle)
+            rc |= L.bnd_written(st.handle, ctypes.c_void_p(res.data_ptr()), H)
         if rc:
             raise RuntimeError(L.bnd_last_error().decode())
 
@@ -407,9 +415,10 @@ def main():
         log("MoE finalize (T=2048 H=4096 k=8), full rows and rows 768..1023")
         dm = workloads.moe()
         n_m = max(2, -(-ROTATE_BYTES // (dm["T"] * (dm["k"] + 3) * dm["H"] * 2)))
-        for name, rb, rows in (("moe_full_T2048_H4096_k8", 0, 2048),
-                               ("moe_slice_rows768_1023", *workloads.MOE_SLICE)):
-            step, nb, keep = moe_case(torch, bnd, dm, n_m, rb, rows)
+        for name, rb, rows, tg in (("moe_full_T2048_H4096_k8", 0, 2048, False),
+                                   ("moe_slice_rows768_1023", *workloads.MOE_SLICE, False),
+                                   ("moe_terminal_gemma_T2048_H4096_k8", 0, 2048, True)):
+            step, nb, keep = moe_case(torch, bnd, dm, n_m, rb, rows, terminal_gemma=tg)
             tm = timer.run(step, n_m, 20, 100)
             sec[name] = {"tokens_per_s_kernel": rows / tm["kernel_mean_s"],
                          "kernel_mean_us": tm["kernel_mean_s"] * 1e6,

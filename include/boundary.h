@@ -81,6 +81,13 @@ typedef enum bnd_kind {
   BND_KIND_MOE = 2       /* deferred MoE finalize handoff */
 } bnd_kind;
 
+/* Weight form of the consumer's RMSNorm. PLAIN: y = x * inv * w. GEMMA:
+ * y = x * inv * (1 + w), the GemmaRMSNorm weight that the guide's fused
+ * terminal finalize reads (section "Enter and leave the layer stack"); the
+ * page does not spell the form out, this is the Gemma convention of a weight
+ * stored as an offset from one. */
+typedef enum bnd_norm_form { BND_NORM_PLAIN = 0, BND_NORM_GEMMA = 1 } bnd_norm_form;
+
 typedef enum bnd_status {
   BND_OK = 0,
   BND_ERR_INVALID_ARG = -1,    /* null / misaligned pointer, bad ld, eps < 0, bad rows, overlap */
@@ -121,6 +128,12 @@ BND_API bnd_state bnd_stream_state(const bnd_stream* s);
 BND_API bnd_kind bnd_stream_pending_kind(const bnd_stream* s);
 /* 1 when the residual storage holds the stream's residual value. */
 BND_API int bnd_stream_has_residual(const bnd_stream* s);
+
+/* Weight form used by every later read on this stream (host only; the
+ * default is BND_NORM_PLAIN). A model stack uses one norm class throughout,
+ * so the form belongs to the stream rather than to each call.
+ * Errors: INVALID_ARG (NULL stream, unknown form). */
+BND_API bnd_status bnd_stream_set_norm_form(bnd_stream* s, bnd_norm_form form);
 
 /* ------------------------------------------------------------------------ */
 /* Publishing owed work (host only, nothing is launched)                    */

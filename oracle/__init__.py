@@ -42,12 +42,12 @@ def _bind(lib):
     lib.orc_e4m3_value.restype = ctypes.c_double
     lib.orc_e4m3_round.argtypes = [ctypes.c_double]
     lib.orc_e4m3_round.restype = ctypes.c_uint8
-    lib.orc_enter_norm.argtypes = [i64, i64, p, i64, p, f32, p, i64, p, i64, p]
-    lib.orc_written_norm.argtypes = [i64, i64, p, i64, p, f32, p, i64, p]
-    lib.orc_fold_norm.argtypes = [i64, i64, i64, i32, p, i64, p, i64, p, f32, p, i64, p, i64,
-                                  p, i64, p, p, p, p]
+    lib.orc_enter_norm.argtypes = [i64, i64, p, i64, p, f32, i32, p, i64, p, i64, p]
+    lib.orc_written_norm.argtypes = [i64, i64, p, i64, p, f32, i32, p, i64, p]
+    lib.orc_fold_norm.argtypes = [i64, i64, i64, i32, p, i64, p, i64, p, f32, i32, p, i64, p,
+                                  i64, p, i64, p, p, p, p]
     lib.orc_moe_fold_norm.argtypes = [i64, i64, i64, i32, p, i64, i64, p, p, p, i64, p, f32,
-                                      p, i64, p, i64, p, i64, p, p, p, p]
+                                      i32, p, i64, p, i64, p, i64, p, p, p, p]
     lib.orc_complete_partials.argtypes = [i64, i64, i64, i32, p, i64, p, i64, p, p]
     lib.orc_complete_moe.argtypes = [i64, i64, i64, i32, p, i64, i64, p, p, p, i64, p, p]
     for f in ("orc_enter_norm", "orc_written_norm", "orc_fold_norm", "orc_moe_fold_norm",
@@ -107,29 +107,31 @@ class Oracle:
         return self.lib.orc_e4m3_round(v)
 
     # boundary reads ----------------------------------------------------
-    def enter_norm(self, x_in, w, eps):
+    def enter_norm(self, x_in, w, eps, gemma=False):
         x_in = _u16(x_in)
         rows, H = x_in.shape
         w = np.ascontiguousarray(w, dtype=np.float32)
         res = np.empty((rows, H), np.uint16)
         y = np.empty((rows, H), np.uint16)
         y_ex = np.empty((rows, H), np.float64)
-        rc = self.lib.orc_enter_norm(rows, H, _p(x_in), H, _p(w), eps, _p(res), H, _p(y), H,
-                                     _p(y_ex))
+        rc = self.lib.orc_enter_norm(rows, H, _p(x_in), H, _p(w), eps, int(gemma), _p(res), H,
+                                     _p(y), H, _p(y_ex))
         assert rc == 0
         return {"residual": res, "y": y, "y_exact": y_ex}
 
-    def written_norm(self, residual, w, eps):
+    def written_norm(self, residual, w, eps, gemma=False):
         residual = _u16(residual)
         rows, H = residual.shape
         w = np.ascontiguousarray(w, dtype=np.float32)
         y = np.empty((rows, H), np.uint16)
         y_ex = np.empty((rows, H), np.float64)
-        rc = self.lib.orc_written_norm(rows, H, _p(residual), H, _p(w), eps, _p(y), H, _p(y_ex))
+        rc = self.lib.orc_written_norm(rows, H, _p(residual), H, _p(w), eps, int(gemma), _p(y), H,
+                                       _p(y_ex))
         assert rc == 0
         return {"y": y, "y_exact": y_ex}
 
-    def fold_norm(self, partials, residual, w, eps, *, row_begin=0, rows=None, fp8=False):
+    def fold_norm(self, partials, residual, w, eps, *, row_begin=0, rows=None, fp8=False,
+                  gemma=False):
         """partials: list of [T,H] uint16 (global rows); residual: [rows,H] uint16 slice or None."""
         partials = [_u16(c) for c in partials]
         T, H = partials[0].shape
@@ -149,8 +151,8 @@ class Oracle:
         else:
             y = np.empty((rows, H), np.uint16)
         rc = self.lib.orc_fold_norm(rows, H, row_begin, len(partials), _ptr_array(partials), H,
-                                    _p(residual), H, _p(w), eps, _p(res), H, _p(y), H, _p(q), H,
-                                    _p(scale), _p(x_ex), _p(y_ex), _p(mag))
+                                    _p(residual), H, _p(w), eps, int(gemma), _p(res), H, _p(y), H,
+                                    _p(q), H, _p(scale), _p(x_ex), _p(y_ex), _p(mag))
         assert rc == 0
         out = {"residual": res, "x_exact": x_ex, "y_exact": y_ex, "mag": mag}
         if fp8:
@@ -160,7 +162,7 @@ class Oracle:
         return out
 
     def moe_fold_norm(self, E, idx, gate, k, residual, w, eps, *, row_begin=0, rows=None,
-                      fp8=False):
+                      fp8=False, gemma=False):
         E = _u16(E)
         n_rows, H = E.shape
         idx = np.ascontiguousarray(idx, dtype=np.int32)
@@ -182,8 +184,8 @@ class Oracle:
         else:
             y = np.empty((rows, H), np.uint16)
         rc = self.lib.orc_moe_fold_norm(rows, H, row_begin, k, _p(E), H, n_rows, _p(idx),
-                                        _p(gate), _p(residual), H, _p(w), eps, _p(res), H, _p(y),
-                                        H, _p(q), H, _p(scale), _p(x_ex), _p(y_ex), _p(mag))
+                                        _p(gate), _p(residual), H, _p(w), eps, int(gemma), _p(res), H,
+                                        _p(y), H, _p(q), H, _p(scale), _p(x_ex), _p(y_ex), _p(mag))
         assert rc == 0
         out = {"residual": res, "x_exact": x_ex, "y_exact": y_ex, "mag": mag}
         if fp8:

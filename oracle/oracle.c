@@ -36,7 +36,11 @@
  *
  * The RMSNorm read: y_h = x_h * w_h / sqrt(mean_h(x_h^2) + eps), with eps
  * (an fp32 value) inside the square root. The pages name RMSNorm without
- * printing its formula; this is the standard definition.
+ * printing its formula; this is the standard definition. The guide's
+ * terminal finalize (section "Enter and leave the layer stack") reads a
+ * GemmaRMSNorm weight instead; the page does not define it, and the reading
+ * taken here is the Gemma convention of a weight stored as an offset from
+ * one: y_h = x_h * (1 + w_h) / sqrt(mean_h(x_h^2) + eps). `gemma` selects it.
  *
  * Quantised read (fp8): per row, scale = fp32(max_h |y_h| / 448) and
  * q_h = e4m3(y_h / scale), OCP E4M3FN ("OFP8 Formats for Deep Learning",
@@ -197,9 +201,13 @@ static double rms_inverse(int64_t H, const double* x, float eps) {
   return 1.0 / sqrt(sum_sq / (double)H + (double)eps);
 }
 
-/* The read: y_h = x_h * inv * w_h. */
-static void normalise_row(int64_t H, const double* x, double inv, const float* w, double* y) {
-  for (int64_t h = 0; h < H; ++h) y[h] = x[h] * inv * (double)w[h];
+/* The read: y_h = x_h * inv * w_h, or x_h * inv * (1 + w_h) for a Gemma weight. */
+static void normalise_row(int64_t H, const double* x, double inv, const float* w, int gemma,
+                          double* y) {
+  for (int64_t h = 0; h < H; ++h) {
+    double scale = gemma ? 1.0 + (double)w[h] : (double)w[h];
+    y[h] = x[h] * inv * scale;
+  }
 }
 
 static void store_bf16_row(int64_t H, const double* v, uint16_t* out) {
@@ -259,14 +267,14 @@ static void scratch_free(scratch_t* w) {
 /* Read from the Initial state: the residual is initialised from the stack
  * input x_in, and y = norm(x_in). */
 int orc_enter_norm(int64_t rows, int64_t H, const uint16_t* x_in, int64_t ld_x, const float* w,
-                   float eps, uint16_t* res_out, int64_t ld_ro, uint16_t* y_out, int64_t ld_y,
-                   double* y_exact) {
+                   float eps, int gemma, uint16_t* res_out, int64_t ld_ro, uint16_t* y_out,
+                   int64_t ld_y, double* y_exact) {
   scratch_t b;
   if (scratch_alloc(&b, H)) return -1;
   for (int64_t i = 0; i < rows; ++i) {
     for (int64_t h = 0; h < H; ++h) b.x[h] = orc_bf16_value(x_in[i * ld_x + h]);
     double inv = rms_inverse(H, b.x, eps);
-    normalise_row(H, b.x, inv, w, b.y);
+    normalise_row(H, b.x, inv, w, gemma, b.y);
     if (res_out) memcpy(res_out + i * ld_ro, x_in + i * ld_x, sizeof(uint16_t) * (size_t)H);
     store_bf16_row(H, b.y, y_out + i * ld_y);
     copy_out(H, b.y, y_exact ? y_exact + i * H : NULL);
@@ -277,8 +285,8 @@ int orc_enter_norm(int64_t rows, int64_t H, const uint16_t* x_in, int64_t ld_x, 
 
 /* Read from the Written state: y = norm(residual), no update. */
 int orc_written_norm(int64_t rows, int64_t H, const uint16_t* res, int64_t ld_r, const float* w,
-                     float eps, uint16_t* y_out, int64_t ld_y, double* y_exact) {
-  return orc_enter_norm(rows, H, res, ld_r, w, eps, NULL, 0, y_out, ld_y, y_exact);
+                     float eps, int gemma, uint16_t* y_out, int64_t ld_y, double* y_exact) {
+  return orc_enter_norm(rows, H, res, ld_r, w, eps, gemma, NULL, 0, y_out, ld_y, y_exact);
 }
 
 /* Read from the Pending state with P plain partials: complete, fold, norm.
@@ -286,16 +294,16 @@ int orc_written_norm(int64_t rows, int64_t H, const uint16_t* res, int64_t ld_r,
  * Exactly one of y_out (bf16 read) or q_out/scale_out (fp8 read) is used. */
 int orc_fold_norm(int64_t rows, int64_t H, int64_t row_begin, int P,
                   const uint16_t* const* partials, int64_t ld_p, const uint16_t* residual,
-                  int64_t ld_r, const float* w, float eps, uint16_t* res_out, int64_t ld_ro,
-                  uint16_t* y_out, int64_t ld_y, uint8_t* q_out, int64_t ld_q, float* scale_out,
-                  double* x_exact, double* y_exact, double* mag) {
+                  int64_t ld_r, const float* w, float eps, int gemma, uint16_t* res_out,
+                  int64_t ld_ro, uint16_t* y_out, int64_t ld_y, uint8_t* q_out, int64_t ld_q,
+                  float* scale_out, double* x_exact, double* y_exact, double* mag) {
   scratch_t b;
   if (scratch_alloc(&b, H)) return -1;
   for (int64_t i = 0; i < rows; ++i) {
     complete_partials_row(H, P, partials, ld_p, row_begin + i, b.s, b.mag);
     apply_update_row(H, residual ? residual + i * ld_r : NULL, b.s, b.x, b.mag);
     double inv = rms_inverse(H, b.x, eps);
-    normalise_row(H, b.x, inv, w, b.y);
+    normalise_row(H, b.x, inv, w, gemma, b.y);
     store_bf16_row(H, b.x, res_out + i * ld_ro);
     if (y_out) store_bf16_row(H, b.y, y_out + i * ld_y);
     if (q_out) scale_out[i] = store_fp8_row(H, b.y, q_out + i * ld_q);
@@ -312,7 +320,7 @@ int orc_fold_norm(int64_t rows, int64_t H, int64_t row_begin, int P,
 int orc_moe_fold_norm(int64_t rows, int64_t H, int64_t row_begin, int k, const uint16_t* E,
                       int64_t ld_e, int64_t n_rows_e, const int32_t* idx, const float* gate,
                       const uint16_t* residual, int64_t ld_r, const float* w, float eps,
-                      uint16_t* res_out, int64_t ld_ro, uint16_t* y_out, int64_t ld_y,
+                      int gemma, uint16_t* res_out, int64_t ld_ro, uint16_t* y_out, int64_t ld_y,
                       uint8_t* q_out, int64_t ld_q, float* scale_out, double* x_exact,
                       double* y_exact, double* mag) {
   scratch_t b;
@@ -321,7 +329,7 @@ int orc_moe_fold_norm(int64_t rows, int64_t H, int64_t row_begin, int k, const u
     complete_moe_row(H, k, E, ld_e, n_rows_e, idx, gate, row_begin + i, b.s, b.mag);
     apply_update_row(H, residual ? residual + i * ld_r : NULL, b.s, b.x, b.mag);
     double inv = rms_inverse(H, b.x, eps);
-    normalise_row(H, b.x, inv, w, b.y);
+    normalise_row(H, b.x, inv, w, gemma, b.y);
     store_bf16_row(H, b.x, res_out + i * ld_ro);
     if (y_out) store_bf16_row(H, b.y, y_out + i * ld_y);
     if (q_out) scale_out[i] = store_fp8_row(H, b.y, q_out + i * ld_q);

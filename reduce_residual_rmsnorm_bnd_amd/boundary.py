@@ -35,6 +35,8 @@ BND_ERR_HIP = -8
 BND_OWED_NONE = 0
 BND_MAX_SOURCES = 16
 BND_MAX_HIDDEN = 32768
+# bnd_norm_form
+BND_NORM_PLAIN, BND_NORM_GEMMA = 0, 1
 # bnd_option
 BND_OPT_FUSED_UNAVAILABLE = 1
 BND_OPT_THREADS_PER_ROW = 2
@@ -43,7 +45,7 @@ BND_OPT_VECTORS_PER_THREAD = 3
 # exported symbols, in header order
 SYMBOLS = [
     "bnd_stream_create", "bnd_stream_destroy", "bnd_stream_state", "bnd_stream_pending_kind",
-    "bnd_stream_has_residual", "bnd_publish_partials", "bnd_publish_moe", "bnd_enter_norm",
+    "bnd_stream_has_residual", "bnd_stream_set_norm_form", "bnd_publish_partials", "bnd_publish_moe", "bnd_enter_norm",
     "bnd_fold_norm", "bnd_fold_norm_quant_fp8", "bnd_moe_finalize_fold_norm", "bnd_complete_only",
     "bnd_written", "bnd_take_output", "bnd_status_str", "bnd_last_error", "bnd_version",
     "bnd_set_option", "bnd_get_option", "bnd_time_next_launch",
@@ -70,6 +72,7 @@ def _declare(lib):
         "bnd_stream_state": (c.c_int, [vp]),
         "bnd_stream_pending_kind": (c.c_int, [vp]),
         "bnd_stream_has_residual": (c.c_int, [vp]),
+        "bnd_stream_set_norm_form": (st, [vp, c.c_int]),
         "bnd_publish_partials": (st, [vp, c.POINTER(vp), i32, i64, c.POINTER(u64)]),
         "bnd_publish_moe": (st, [vp, vp, i64, i64, vp, vp, i32, c.POINTER(u64)]),
         "bnd_enter_norm": (st, [vp, vp, i64, vp, f32, vp, i64, vp]),
@@ -208,6 +211,10 @@ def bnd_stream_create(T: int, H: int, residual: torch.Tensor | None, row_begin: 
 
 def bnd_stream_destroy(s: Stream) -> None:
     s.destroy()
+
+
+def bnd_stream_set_norm_form(s: Stream, form: int) -> None:
+    _check(lib().bnd_stream_set_norm_form(s.handle, form))
 
 
 def bnd_publish_partials(s: Stream, partials: Sequence[torch.Tensor]) -> int:

@@ -35,6 +35,7 @@ struct bnd_stream {
   uint16_t* residual;
   int64_t ld_res;
   bnd_state state;
+  bnd_norm_form norm_form;
   bool has_residual;
   bnd_kind kind;
   bnd_owed owed;
@@ -181,6 +182,7 @@ RowArgs base_args(const bnd_stream* s) {
   a.res = s->residual;
   a.ld_res = s->ld_res;
   a.has_residual = s->has_residual ? 1 : 0;
+  a.gemma = s->norm_form == BND_NORM_GEMMA ? 1 : 0;
   return a;
 }
 
@@ -344,6 +346,7 @@ bnd_status bnd_stream_create(bnd_stream** out, int64_t T, int64_t H, int64_t row
   s->residual = static_cast<uint16_t*>(residual);
   s->ld_res = ld_res;
   s->state = BND_INITIAL;
+  s->norm_form = BND_NORM_PLAIN;
   s->has_residual = false;
   s->kind = BND_KIND_NONE;
   s->owed = BND_OWED_NONE;
@@ -362,6 +365,14 @@ bnd_state bnd_stream_state(const bnd_stream* s) { return s ? s->state : BND_INIT
 bnd_kind bnd_stream_pending_kind(const bnd_stream* s) { return s ? s->kind : BND_KIND_NONE; }
 
 int bnd_stream_has_residual(const bnd_stream* s) { return (s && s->has_residual) ? 1 : 0; }
+
+bnd_status bnd_stream_set_norm_form(bnd_stream* s, bnd_norm_form form) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  if (form != BND_NORM_PLAIN && form != BND_NORM_GEMMA)
+    return fail(BND_ERR_INVALID_ARG, "unknown norm form %d", (int)form);
+  s->norm_form = form;
+  return ok();
+}
 
 bnd_status bnd_publish_partials(bnd_stream* s, const void* const* partials, int P, int64_t ld, bnd_owed* owed) {
   if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");

@@ -287,6 +287,7 @@ template <int VPT>
 __device__ __forceinline__ void load_weight(const RowArgs& a, int tid, int nthr, float (&w)[VPT][8]) {
   // the weight is shared by all rows: default cache policy, it stays in L2
   const Rsrc wr = row_rsrc(a.w, a.H * 4);
+  const bool gemma = a.gemma != 0;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int off = (tid + v * nthr) * 32;
@@ -296,6 +297,10 @@ __device__ __forceinline__ void load_weight(const RowArgs& a, int tid, int nthr,
     w[v][2] = __uint_as_float(lo.z); w[v][3] = __uint_as_float(lo.w);
     w[v][4] = __uint_as_float(hi.x); w[v][5] = __uint_as_float(hi.y);
     w[v][6] = __uint_as_float(hi.z); w[v][7] = __uint_as_float(hi.w);
+    if (gemma) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[v][e] = 1.0f + w[v][e];
+    }
   }
 }
 

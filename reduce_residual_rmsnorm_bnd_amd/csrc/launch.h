@@ -36,6 +36,7 @@ struct RowArgs {
   int H;                             // elements per row
   int nvec;                          // H / 8
   int has_residual;                  // 0: fold with r = 0 (Pending without a residual)
+  int gemma;                         // 1: the norm weight is an offset from one, y = x inv (1 + w)
   int copy_input;                    // enter: store x_in into the residual storage
 };
 

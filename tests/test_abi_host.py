@@ -63,7 +63,7 @@ def owed_out():
 
 def test_library_exports_every_declared_symbol():
     decl = re.findall(r"^BND_API\s+[\w\s\*]+?\b(bnd_\w+)\s*\(", open(HEADER).read(), flags=re.M)
-    assert len(decl) == len(set(decl)) == 20
+    assert len(decl) == len(set(decl)) == 21
     assert sorted(decl) == sorted(B.SYMBOLS)
     for name in decl:
         assert hasattr(L, name), name
@@ -274,6 +274,15 @@ def test_fused_unavailable_refuses_multi_source_only():
     assert L.bnd_moe_finalize_fold_norm(m, om, None, 1e-6, None, H, None) == B.BND_ERR_UNAVAILABLE
     assert L.bnd_set_option(B.BND_OPT_FUSED_UNAVAILABLE, 0) == 0
     assert L.bnd_moe_finalize_fold_norm(m, om, None, 1e-6, None, H, None) == 0
+
+
+def test_norm_form_validation():
+    h = create()
+    assert L.bnd_stream_set_norm_form(h, B.BND_NORM_GEMMA) == 0
+    assert L.bnd_stream_set_norm_form(h, B.BND_NORM_PLAIN) == 0
+    assert L.bnd_stream_set_norm_form(h, 2) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_stream_set_norm_form(None, 0) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_stream_state(h) == B.BND_INITIAL
 
 
 def test_options_validation():

@@ -81,7 +81,8 @@ def check_fold(ref, res_bits, y_bits, w, eps, what):
           flush=True)
 
 
-def run_fold(d, *, row_begin=0, rows=None, fp8=False, pad=0, with_residual=True, partials=None):
+def run_fold(d, *, row_begin=0, rows=None, fp8=False, pad=0, with_residual=True, partials=None,
+             gemma=False):
     """One fold through the library; returns host results and the guarded buffers."""
     T, H = d["T"], d["H"]
     rows = T - row_begin if rows is None else rows
@@ -91,6 +92,8 @@ def run_fold(d, *, row_begin=0, rows=None, fp8=False, pad=0, with_residual=True,
         res.from_host(d["residual"][row_begin:row_begin + rows])
     w = d["weight"].to(DEV)
     s = bnd.bnd_stream_create(T, H, res.view, row_begin, rows)
+    if gemma:
+        bnd.bnd_stream_set_norm_form(s, bnd.BND_NORM_GEMMA)
     if with_residual:
         bnd.bnd_written(s, res.view)
     owed = bnd.bnd_publish_partials(s, parts)
@@ -110,20 +113,22 @@ def run_fold(d, *, row_begin=0, rows=None, fp8=False, pad=0, with_residual=True,
     return out
 
 
-def oracle_fold(orc, d, *, row_begin=0, rows=None, fp8=False, with_residual=True):
+def oracle_fold(orc, d, *, row_begin=0, rows=None, fp8=False, with_residual=True, gemma=False):
     T = d["T"]
     rows = T - row_begin if rows is None else rows
     res = bits(d["residual"][row_begin:row_begin + rows]) if with_residual else None
     return orc.fold_norm([bits(c) for c in d["partials"]], res, d["weight"].numpy(), d["eps"],
-                         row_begin=row_begin, rows=rows, fp8=fp8)
+                         row_begin=row_begin, rows=rows, fp8=fp8, gemma=gemma)
 
 
 def assert_fold_matches(orc, d, what, **kw):
     fp8 = kw.get("fp8", False)
     got = run_fold(d, **kw)
-    okw = {k: v for k, v in kw.items() if k in ("row_begin", "rows", "fp8", "with_residual")}
+    okw = {k: v for k, v in kw.items() if k in ("row_begin", "rows", "fp8", "with_residual", "gemma")}
     ref = oracle_fold(orc, d, **okw)
     w = d["weight"].numpy()
+    if kw.get("gemma"):
+        w = 1.0 + w.astype(np.float64)  # the read's effective weight, for the tolerance
     got["res"].check_guards(f"{what} residual")
     res_bits = bits(got["res"].view)
     if fp8:
@@ -199,24 +204,29 @@ def _moe_device(d):
     return (d["expert_rows"].to(DEV), d["idx"].to(DEV), d["gate"].to(DEV))
 
 
-def run_moe(orc, d, row_begin, rows, what):
+def run_moe(orc, d, row_begin, rows, what, gemma=False, terminal=False):
     T, H, k = d["T"], d["H"], d["k"]
     E, idx, gate = _moe_device(d)
     res = Guarded(rows, H).from_host(d["residual"][row_begin:row_begin + rows])
     y = Guarded(rows, H)
     w = d["weight"].to(DEV)
     s = bnd.bnd_stream_create(T, H, res.view, row_begin, rows)
+    if gemma:
+        bnd.bnd_stream_set_norm_form(s, bnd.BND_NORM_GEMMA)
     bnd.bnd_written(s, res.view)
     owed = bnd.bnd_publish_moe(s, E, idx, gate, k)
     bnd.bnd_moe_finalize_fold_norm(s, owed, w, d["eps"], y.view)
+    if terminal:  # the final norm releases the stream after handing on its output
+        bnd.bnd_take_output(s)
     torch.cuda.synchronize()
-    assert s.state == bnd.BND_WRITTEN
+    assert s.state == (bnd.BND_INITIAL if terminal else bnd.BND_WRITTEN)
     ref = orc.moe_fold_norm(bits(d["expert_rows"]), d["idx"].numpy(), d["gate"].numpy(), k,
                             bits(d["residual"][row_begin:row_begin + rows]), d["weight"].numpy(),
-                            d["eps"], row_begin=row_begin, rows=rows)
+                            d["eps"], row_begin=row_begin, rows=rows, gemma=gemma)
     res.check_guards(f"{what} residual")
     y.check_guards(f"{what} y")
-    check_fold(ref, bits(res.view), bits(y.view), d["weight"].numpy(), d["eps"], what)
+    w_eff = d["weight"].numpy().astype(np.float64) + (1.0 if gemma else 0.0)
+    check_fold(ref, bits(res.view), bits(y.view), w_eff, d["eps"], what)
     return res, y
 
 
@@ -485,3 +495,92 @@ def test_enter_aliasing_input_and_residual(orc):
     ref = orc.enter_norm(bits(d["x_in"]), d["weight"].numpy(), d["eps"])
     assert np.array_equal(bits(x.view), bits(d["x_in"]))
     tolerance.check_bf16(bits(y.view), ref["y_exact"], np.zeros((T, H)), "aliased enter y")
+
+
+# ------------------------------------------------------------------ HIP graph replay
+
+def test_graph_replay_matches_eager(orc):
+    """A decode-style chain (enter + 4 folds) captured once and replayed several times, with
+    eager library work and synchronisations in between; every replay must equal the eager run."""
+    T, H, P, n_b = 8, 4096, 4, 4
+    start = workloads.decode_start(T, H)
+    bounds = [workloads.decode_boundary(T, b, P, H) for b in range(n_b)]
+    x_in = start["x_in"].to(DEV)
+    w0 = start["weight"].to(DEV)
+    parts = [[c.to(DEV) for c in d["partials"]] for d in bounds]
+    ws = [d["weight"].to(DEV) for d in bounds]
+
+    def chain(res, y):
+        s = bnd.bnd_stream_create(T, H, res)
+        bnd.bnd_enter_norm(s, x_in, w0, 1e-6, y)
+        for b in range(n_b):
+            owed = bnd.bnd_publish_partials(s, parts[b])
+            bnd.bnd_fold_norm(s, owed, ws[b], 1e-6, y)
+        return s
+
+    res_e = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    y_e = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    chain(res_e, y_e)
+    torch.cuda.synchronize()
+
+    res_g = torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
+    y_g = torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain(res_g, y_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        keep = chain(res_g, y_g)
+    other_res = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    other_y = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    for rep in range(4):
+        res_g.zero_()
+        y_g.zero_()
+        g.replay()
+        chain(other_res, other_y)  # eager library work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(res_g, res_e), f"replay {rep}: residual differs from the eager run"
+        assert torch.equal(y_g, y_e), f"replay {rep}: y differs from the eager run"
+    del keep
+
+
+# ------------------------------------------------------------------ Gemma-form weight
+
+def _gemma_inputs(seed, T, H, P):
+    d = workloads.fold_inputs(seed, T, H, P, w_mean=0.0, w_std=0.1)  # offsets from one
+    return d
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_gemma_fold(orc, fp8):
+    d = _gemma_inputs(71, 96, 4096, 8)
+    assert_fold_matches(orc, d, f"Gemma weight fold {'fp8' if fp8 else 'bf16'}", fp8=fp8, gemma=True)
+    d2 = _gemma_inputs(72, 7, 7168, 3)
+    assert_fold_matches(orc, d2, "Gemma weight H=7168 slice", fp8=fp8, gemma=True, row_begin=2,
+                        rows=4)
+
+
+def test_gemma_enter(orc):
+    d = _gemma_inputs(73, 12, 2048, 1)
+    T, H = 12, 2048
+    res = Guarded(T, H)
+    y = Guarded(T, H)
+    s = bnd.bnd_stream_create(T, H, res.view)
+    bnd.bnd_stream_set_norm_form(s, bnd.BND_NORM_GEMMA)
+    x = workloads.stack_input(73, T, H)
+    bnd.bnd_enter_norm(s, x.to(DEV), d["weight"].to(DEV), d["eps"], y.view)
+    torch.cuda.synchronize()
+    ref = orc.enter_norm(bits(x), d["weight"].numpy(), d["eps"], gemma=True)
+    assert np.array_equal(bits(res.view), ref["residual"])
+    tolerance.check_bf16(bits(y.view), ref["y_exact"], np.zeros((T, H)), "Gemma enter y")
+
+
+def test_gemma_terminal_moe_finalize(orc):
+    """The terminal finalize of the guide: a deferred MoE handoff finalized, folded and
+    normalised with a GemmaRMSNorm weight in one pass, then the stream is released."""
+    d = workloads.moe_inputs(74, 512, 4096, 128, 8, w_mean=0.0, w_std=0.1)
+    run_moe(orc, d, 0, 512, "terminal MoE finalize, Gemma weight", gemma=True, terminal=True)
+    run_moe(orc, d, 192, 64, "terminal MoE finalize share, Gemma weight", gemma=True, terminal=True)

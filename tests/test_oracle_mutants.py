@@ -33,9 +33,13 @@ MUTANTS = {
                     "return 1.0 / sqrt(sum_sq / (double)H);"),
     "sum_not_mean": ("return 1.0 / sqrt(sum_sq / (double)H + (double)eps);",
                      "return 1.0 / sqrt(sum_sq + (double)eps);"),
-    "weight_dropped": ("y[h] = x[h] * inv * (double)w[h];", "y[h] = x[h] * inv;"),
-    "norm_of_rounded_snapshot": ("y[h] = x[h] * inv * (double)w[h];",
-                                 "y[h] = orc_bf16_value(orc_bf16_round(x[h])) * inv * (double)w[h];"),
+    "weight_dropped": ("y[h] = x[h] * inv * scale;", "y[h] = x[h] * inv;"),
+    "norm_of_rounded_snapshot": ("y[h] = x[h] * inv * scale;",
+                                 "y[h] = orc_bf16_value(orc_bf16_round(x[h])) * inv * scale;"),
+    "gemma_offset_ignored": ("double scale = gemma ? 1.0 + (double)w[h] : (double)w[h];",
+                             "double scale = (double)w[h];"),
+    "gemma_everywhere": ("double scale = gemma ? 1.0 + (double)w[h] : (double)w[h];",
+                         "double scale = 1.0 + (double)w[h];"),
     "bf16_ties_away": ("if (frac > 0.5 || (frac == 0.5 && fmod(n_r, 2.0) != 0.0)) n_r += 1.0;\n    r = n_r * step;\n  }\n  float f",
                        "if (frac >= 0.5) n_r += 1.0;\n    r = n_r * step;\n  }\n  float f"),
     "bf16_truncate": ("if (frac > 0.5 || (frac == 0.5 && fmod(n_r, 2.0) != 0.0)) n_r += 1.0;\n    r = n_r * step;\n  }\n  float f",
