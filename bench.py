@@ -231,6 +231,49 @@ def moe_case(torch, bnd, d, n_sets, row_begin=0, rows=None, terminal_gemma=False
     return step, read + write, (sets, idx0, gate0, w)
 
 
+def aux_case(torch, bnd, d, n_sets, kind):
+    """snapshot or add_to_output over the prefill workload: each step publishes the partials,
+    runs the call into a separate output, then marks the residual written again (host-only)
+    so the next step can publish."""
+    T, H, P = d["T"], d["H"], d["P"]
+    dev = torch.device("cuda:0")
+    L = bnd.lib()
+    base_parts = [c.to(dev) for c in d["partials"]]
+    base_res = d["residual"].to(dev)
+    extra0 = d["residual"].to(dev)  # any [T, H] bf16 tensor serves as the extra contribution
+    sets = []
+    for s_i in range(n_sets):
+        parts = base_parts if s_i == 0 else [c.clone() for c in base_parts]
+        res = base_res.clone()
+        extra = extra0.clone()
+        st = bnd.bnd_stream_create(T, H, res)
+        bnd.bnd_written(st, res)
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        arr = (ctypes.c_void_p * P)(*[c.data_ptr() for c in parts])
+        sets.append((st, parts, res, extra, out, arr))
+    owed = ctypes.c_uint64()
+    new = ctypes.c_uint64()
+    hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step(i, ev0, ev1):
+        st, parts, res, extra, out, arr = sets[i]
+        rc = L.bnd_publish_partials(st.handle, arr, P, H, ctypes.byref(owed))
+        if ev0 is not None:
+            rc |= L.bnd_time_next_launch(ev0, ev1)
+        if kind == "snapshot":
+            rc |= L.bnd_snapshot(st.handle, owed.value, ctypes.c_void_p(out.data_ptr()), H, hs)
+        else:
+            rc |= L.bnd_add_to_output(st.handle, owed.value, ctypes.c_void_p(extra.data_ptr()), H,
+                                      ctypes.c_void_p(out.data_ptr()), H, ctypes.byref(new), hs)
+        rc |= L.bnd_written(st.handle, ctypes.c_void_p(res.data_ptr()), H)
+        if rc:
+            raise RuntimeError(L.bnd_last_error().decode())
+
+    el = T * H
+    nbytes = (P + 1) * el * 2 + el * 2
+    return step, nbytes, (sets, base_parts)
+
+
 def decode_chain(torch, bnd, workloads, T, reps_eager, reps_graph, H=4096, P=4, n_b=96):
     """1 enter + 96 folds with fresh partials per boundary: eager and HIP-graph us/boundary."""
     dev = torch.device("cuda:0")
@@ -427,6 +470,27 @@ def main():
                          "algorithmic_bytes": nb}
             del keep, step
         del dm
+        torch.cuda.empty_cache()
+        log("snapshot and add_to_output (prefill sizes), the largest RSv share of 2047 rows")
+        for kind in ("snapshot", "add_to_output"):
+            step, nb, keep = aux_case(torch, bnd, d, n_sets, kind)
+            ta = timer.run(step, n_sets, 20, 100)
+            sec[f"{kind}_T2048_H4096_P8"] = {"kernel_mean_us": ta["kernel_mean_s"] * 1e6,
+                                             "GBps": nb / ta["kernel_mean_s"] / 1e9,
+                                             "frac": nb / ta["kernel_mean_s"] / 1e9 / PEAK_HBM_GBPS,
+                                             "algorithmic_bytes": nb}
+            del keep, step
+        counts = [300, 0, 511, 256, 257, 1, 400, 322]
+        rb, rows, Tr = bnd.bnd_rsv_share(counts, 2)
+        dr = workloads.fold_inputs(6, Tr, 4096, 8)
+        step, nb, keep = fold_case(torch, bnd, dr, n_sets, row_begin=rb, rows=rows)
+        tr = timer.run(step, n_sets, 20, 100)
+        sec["rsv_share_511_of_2047_H4096_P8"] = {"row_begin": rb, "rows": rows,
+                                                  "kernel_mean_us": tr["kernel_mean_s"] * 1e6,
+                                                  "GBps": nb / tr["kernel_mean_s"] / 1e9,
+                                                  "frac": nb / tr["kernel_mean_s"] / 1e9 / PEAK_HBM_GBPS,
+                                                  "algorithmic_bytes": nb}
+        del keep, step, dr
         torch.cuda.empty_cache()
         log("decode chain (1 enter + 96 folds), eager and graph")
         sec["decode"] = [decode_chain(torch, bnd, workloads, T, 20, 50) for T in (1, 8, 32, 128)]

@@ -211,6 +211,40 @@ BND_API bnd_status bnd_moe_finalize_fold_norm(bnd_stream* s, bnd_owed owed, cons
 BND_API bnd_status bnd_complete_only(bnd_stream* s, bnd_owed owed, void* out, int64_t ld_out,
                              bnd_owed* new_owed, void* hip_stream);
 
+/* Add an extra contribution exactly once (guide, section "Auxiliary capture
+ * and extra contributions": add_to_output completes the contribution before
+ * adding the extra once and keeps the residual update pending; the
+ * integration checklist routes deepstack embeddings through it).
+ * out[i, :] = bf16(s + extra[row_begin + i, :]) for the slice rows, where s is
+ * the completed owed sum (partials, or the MoE finalize) and extra is
+ * [T, H] bf16 indexed by global row like the partials. The stream stays
+ * Pending, owing one partial that is `out`; *new_owed receives its handle.
+ * Errors: as bnd_complete_only, and INVALID_ARG for a missing or
+ * overlapping extra. */
+BND_API bnd_status bnd_add_to_output(bnd_stream* s, bnd_owed owed, const void* extra, int64_t ld_extra,
+                                     void* out, int64_t ld_out, bnd_owed* new_owed, void* hip_stream);
+
+/* A plain residual snapshot that leaves the owed work in place (guide,
+ * section "Auxiliary capture and extra contributions": snapshot() produces
+ * an owned plain residual snapshot, the sum runs on a copy without consuming
+ * the main contribution, and a producer-specific handoff is refused).
+ * out[i, :] = bf16(r + s) for the slice rows (r = 0 on a Pending stream
+ * without a residual; from Written, owed = BND_OWED_NONE and out is a copy of
+ * the residual). The stream, its residual and its owed handle do not change.
+ * Errors: NOT_STARTED (Initial), FOREIGN_OUTPUT, WRONG_KIND (MoE handoff
+ * pending), INVALID_ARG, NO_PATH, HIP. */
+BND_API bnd_status bnd_snapshot(bnd_stream* s, bnd_owed owed, void* out, int64_t ld_out, void* hip_stream);
+
+/* Row share of rank r under a variable-size reduce-scatter (guide, section
+ * "Choose a reduction policy": rsv, whose per-rank row counts come from the
+ * batch metadata rather than an even split): rows
+ * [sum_{i<r} counts[i], that + counts[r]) of a batch of T = sum(counts) rows,
+ * for bnd_stream_create's row_begin and rows. Host only.
+ * Errors: INVALID_ARG (NULL pointer, r outside [0, R), a negative count,
+ * overflow). */
+BND_API bnd_status bnd_rsv_share(const int64_t* counts, int R, int r, int64_t* row_begin, int64_t* rows,
+                                 int64_t* T);
+
 /* ------------------------------------------------------------------------ */
 /* Host-only transitions (guide: the residual.batch helpers)                */
 /* ------------------------------------------------------------------------ */

@@ -48,10 +48,12 @@ def _bind(lib):
                                   i64, p, i64, p, p, p, p]
     lib.orc_moe_fold_norm.argtypes = [i64, i64, i64, i32, p, i64, i64, p, p, p, i64, p, f32,
                                       i32, p, i64, p, i64, p, i64, p, p, p, p]
-    lib.orc_complete_partials.argtypes = [i64, i64, i64, i32, p, i64, p, i64, p, p]
-    lib.orc_complete_moe.argtypes = [i64, i64, i64, i32, p, i64, i64, p, p, p, i64, p, p]
+    lib.orc_complete_partials.argtypes = [i64, i64, i64, i32, p, i64, p, i64, p, i64, p, p]
+    lib.orc_complete_moe.argtypes = [i64, i64, i64, i32, p, i64, i64, p, p, p, i64, p, i64, p,
+                                     p]
+    lib.orc_snapshot.argtypes = [i64, i64, i64, i32, p, i64, p, i64, p, i64, p, p]
     for f in ("orc_enter_norm", "orc_written_norm", "orc_fold_norm", "orc_moe_fold_norm",
-              "orc_complete_partials", "orc_complete_moe"):
+              "orc_complete_partials", "orc_complete_moe", "orc_snapshot"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -194,30 +196,56 @@ class Oracle:
             out["y"] = y
         return out
 
-    def complete_partials(self, partials, *, row_begin=0, rows=None):
+    def complete_partials(self, partials, *, row_begin=0, rows=None, extra=None):
+        """complete_output (extra None) or add_to_output (extra: [T,H] uint16, global rows)."""
         partials = [_u16(c) for c in partials]
         T, H = partials[0].shape
         rows = T - row_begin if rows is None else rows
+        if extra is not None:
+            extra = _u16(extra)
+            assert extra.shape == (T, H)
         out = np.empty((rows, H), np.uint16)
         s_ex = np.empty((rows, H), np.float64)
         mag = np.empty((rows, H), np.float64)
         rc = self.lib.orc_complete_partials(rows, H, row_begin, len(partials),
-                                            _ptr_array(partials), H, _p(out), H, _p(s_ex),
-                                            _p(mag))
+                                            _ptr_array(partials), H, _p(extra), H, _p(out), H,
+                                            _p(s_ex), _p(mag))
         assert rc == 0
         return {"out": out, "s_exact": s_ex, "mag": mag}
 
-    def complete_moe(self, E, idx, gate, k, *, row_begin=0, rows=None):
+    def complete_moe(self, E, idx, gate, k, *, row_begin=0, rows=None, extra=None):
         E = _u16(E)
         n_rows, H = E.shape
         idx = np.ascontiguousarray(idx, dtype=np.int32)
         gate = np.ascontiguousarray(gate, dtype=np.float32)
         T = idx.size // k
         rows = T - row_begin if rows is None else rows
+        if extra is not None:
+            extra = _u16(extra)
+            assert extra.shape == (T, H)
         out = np.empty((rows, H), np.uint16)
         s_ex = np.empty((rows, H), np.float64)
         mag = np.empty((rows, H), np.float64)
         rc = self.lib.orc_complete_moe(rows, H, row_begin, k, _p(E), H, n_rows, _p(idx),
-                                       _p(gate), _p(out), H, _p(s_ex), _p(mag))
+                                       _p(gate), _p(extra), H, _p(out), H, _p(s_ex), _p(mag))
         assert rc == 0
         return {"out": out, "s_exact": s_ex, "mag": mag}
+
+    def snapshot(self, partials, residual, *, H=None, row_begin=0, rows=None):
+        """bf16(r + sum of partials) for the slice rows; partials may be empty (a copy)."""
+        partials = [_u16(c) for c in partials]
+        if residual is not None:
+            residual = _u16(residual)
+        if partials:
+            T, H = partials[0].shape
+            rows = T - row_begin if rows is None else rows
+        else:
+            rows, H = residual.shape
+        out = np.empty((rows, H), np.uint16)
+        x_ex = np.empty((rows, H), np.float64)
+        mag = np.empty((rows, H), np.float64)
+        arr = _ptr_array(partials) if partials else None
+        rc = self.lib.orc_snapshot(rows, H, row_begin, len(partials), arr, H, _p(residual), H,
+                                   _p(out), H, _p(x_ex), _p(mag))
+        assert rc == 0
+        return {"out": out, "x_exact": x_ex, "mag": mag}

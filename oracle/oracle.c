@@ -343,14 +343,28 @@ int orc_moe_fold_norm(int64_t rows, int64_t H, int64_t row_begin, int k, const u
 
 /* complete_output: finish the owed sum only, leaving the update pending.
  * The completed contribution is stored as bf16 (the only rounded
- * intermediate of the path, by the definition of this call). */
+ * intermediate of the path, by the definition of this call).
+ * add_to_output (guide, section "Auxiliary capture and extra
+ * contributions"): the contribution is completed first and then the extra
+ * tensor is added exactly once; `extra` (nullable, [T, H] bf16, global rows)
+ * selects it. */
+static void add_extra_row(int64_t H, const uint16_t* extra, double* s, double* mag) {
+  for (int64_t h = 0; h < H; ++h) {
+    double e = orc_bf16_value(extra[h]);
+    s[h] += e;
+    mag[h] += fabs(e);
+  }
+}
+
 int orc_complete_partials(int64_t rows, int64_t H, int64_t row_begin, int P,
-                          const uint16_t* const* partials, int64_t ld_p, uint16_t* out,
-                          int64_t ld_o, double* s_exact, double* mag) {
+                          const uint16_t* const* partials, int64_t ld_p, const uint16_t* extra,
+                          int64_t ld_x, uint16_t* out, int64_t ld_o, double* s_exact,
+                          double* mag) {
   scratch_t b;
   if (scratch_alloc(&b, H)) return -1;
   for (int64_t i = 0; i < rows; ++i) {
     complete_partials_row(H, P, partials, ld_p, row_begin + i, b.s, b.mag);
+    if (extra) add_extra_row(H, extra + (row_begin + i) * ld_x, b.s, b.mag);
     store_bf16_row(H, b.s, out + i * ld_o);
     copy_out(H, b.s, s_exact ? s_exact + i * H : NULL);
     copy_out(H, b.mag, mag ? mag + i * H : NULL);
@@ -361,13 +375,35 @@ int orc_complete_partials(int64_t rows, int64_t H, int64_t row_begin, int P,
 
 int orc_complete_moe(int64_t rows, int64_t H, int64_t row_begin, int k, const uint16_t* E,
                      int64_t ld_e, int64_t n_rows_e, const int32_t* idx, const float* gate,
-                     uint16_t* out, int64_t ld_o, double* s_exact, double* mag) {
+                     const uint16_t* extra, int64_t ld_x, uint16_t* out, int64_t ld_o,
+                     double* s_exact, double* mag) {
   scratch_t b;
   if (scratch_alloc(&b, H)) return -1;
   for (int64_t i = 0; i < rows; ++i) {
     complete_moe_row(H, k, E, ld_e, n_rows_e, idx, gate, row_begin + i, b.s, b.mag);
+    if (extra) add_extra_row(H, extra + (row_begin + i) * ld_x, b.s, b.mag);
     store_bf16_row(H, b.s, out + i * ld_o);
     copy_out(H, b.s, s_exact ? s_exact + i * H : NULL);
+    copy_out(H, b.mag, mag ? mag + i * H : NULL);
+  }
+  scratch_free(&b);
+  return 0;
+}
+
+/* snapshot (guide, section "Auxiliary capture and extra contributions"): a
+ * plain bf16 copy of the residual the pending update would produce,
+ * bf16(r + s), computed on the side; the residual and the owed work are left
+ * as they are. P = 0 (nothing owed) copies the residual. */
+int orc_snapshot(int64_t rows, int64_t H, int64_t row_begin, int P,
+                 const uint16_t* const* partials, int64_t ld_p, const uint16_t* residual,
+                 int64_t ld_r, uint16_t* out, int64_t ld_o, double* x_exact, double* mag) {
+  scratch_t b;
+  if (scratch_alloc(&b, H)) return -1;
+  for (int64_t i = 0; i < rows; ++i) {
+    complete_partials_row(H, P, partials, ld_p, row_begin + i, b.s, b.mag);
+    apply_update_row(H, residual ? residual + i * ld_r : NULL, b.s, b.x, b.mag);
+    store_bf16_row(H, b.x, out + i * ld_o);
+    copy_out(H, b.x, x_exact ? x_exact + i * H : NULL);
     copy_out(H, b.mag, mag ? mag + i * H : NULL);
   }
   scratch_free(&b);

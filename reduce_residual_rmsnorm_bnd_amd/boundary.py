@@ -47,7 +47,7 @@ SYMBOLS = [
     "bnd_stream_create", "bnd_stream_destroy", "bnd_stream_state", "bnd_stream_pending_kind",
     "bnd_stream_has_residual", "bnd_stream_set_norm_form", "bnd_publish_partials", "bnd_publish_moe", "bnd_enter_norm",
     "bnd_fold_norm", "bnd_fold_norm_quant_fp8", "bnd_moe_finalize_fold_norm", "bnd_complete_only",
-    "bnd_written", "bnd_take_output", "bnd_status_str", "bnd_last_error", "bnd_version",
+    "bnd_add_to_output", "bnd_snapshot", "bnd_rsv_share", "bnd_written", "bnd_take_output", "bnd_status_str", "bnd_last_error", "bnd_version",
     "bnd_set_option", "bnd_get_option", "bnd_time_next_launch",
 ]
 
@@ -80,6 +80,10 @@ def _declare(lib):
         "bnd_fold_norm_quant_fp8": (st, [vp, u64, vp, f32, vp, i64, vp, vp]),
         "bnd_moe_finalize_fold_norm": (st, [vp, u64, vp, f32, vp, i64, vp]),
         "bnd_complete_only": (st, [vp, u64, vp, i64, c.POINTER(u64), vp]),
+        "bnd_add_to_output": (st, [vp, u64, vp, i64, vp, i64, c.POINTER(u64), vp]),
+        "bnd_snapshot": (st, [vp, u64, vp, i64, vp]),
+        "bnd_rsv_share": (st, [c.POINTER(i64), i32, i32, c.POINTER(i64), c.POINTER(i64),
+                               c.POINTER(i64)]),
         "bnd_written": (st, [vp, vp, i64]),
         "bnd_take_output": (st, [vp]),
         "bnd_status_str": (c.c_char_p, [st]),
@@ -287,6 +291,31 @@ def bnd_complete_only(s: Stream, owed: int, out: torch.Tensor, hip_stream=None) 
                                    _hip_stream(hip_stream)))
     s._pending = s._pending + [out]
     return new.value
+
+
+def bnd_add_to_output(s: Stream, owed: int, extra: torch.Tensor, out: torch.Tensor,
+                      hip_stream=None) -> int:
+    eptr, ld_e = _rows(extra, "extra", s.T if s.rows else 0, s.H, torch.bfloat16)
+    optr, ld_o = _rows(out, "out", s.rows, s.H, torch.bfloat16)
+    new = ctypes.c_uint64()
+    _check(lib().bnd_add_to_output(s.handle, owed, eptr, ld_e, optr, ld_o, ctypes.byref(new),
+                                   _hip_stream(hip_stream)))
+    s._pending = s._pending + [extra, out]
+    return new.value
+
+
+def bnd_snapshot(s: Stream, owed: int, out: torch.Tensor, hip_stream=None) -> None:
+    optr, ld_o = _rows(out, "out", s.rows, s.H, torch.bfloat16)
+    _check(lib().bnd_snapshot(s.handle, owed, optr, ld_o, _hip_stream(hip_stream)))
+
+
+def bnd_rsv_share(counts: Sequence[int], r: int):
+    """(row_begin, rows, T) of rank r for per-rank row counts."""
+    arr = (ctypes.c_int64 * len(counts))(*counts)
+    b, n, t = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().bnd_rsv_share(arr, len(counts), r, ctypes.byref(b), ctypes.byref(n),
+                               ctypes.byref(t)))
+    return b.value, n.value, t.value
 
 
 def bnd_written(s: Stream, residual: torch.Tensor) -> None:

@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <new>
@@ -532,8 +533,11 @@ bnd_status bnd_moe_finalize_fold_norm(bnd_stream* s, bnd_owed owed, const float*
                    "moe_finalize_fold_norm");
 }
 
-bnd_status bnd_complete_only(bnd_stream* s, bnd_owed owed, void* out, int64_t ld_out, bnd_owed* new_owed,
-                             void* hip_stream) {
+// complete_only (extra == NULL) and add_to_output: out = bf16(s [+ extra]) for
+// the slice rows, then the stream owes one plain partial that is `out`.
+static bnd_status complete_into(bnd_stream* s, bnd_owed owed, bool with_extra, const void* extra,
+                                int64_t ld_extra, void* out, int64_t ld_out, bnd_owed* new_owed, void* hip_stream,
+                                const char* name) {
   if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
   if (!new_owed) return fail(BND_ERR_INVALID_ARG, "new_owed is NULL");
   if (s->state == BND_INITIAL) return fail(BND_ERR_NOT_STARTED, "nothing has been published on this stream");
@@ -542,17 +546,29 @@ bnd_status bnd_complete_only(bnd_stream* s, bnd_owed owed, void* out, int64_t ld
   const bool any = s->rows > 0;
   bnd_status st;
   if ((st = check_rows_tensor("out", out, ld_out, s->H, any))) return st;
-  if ((st = check_output_disjoint(s, "out", rows_range(out, s->rows, ld_out, s->H, 2), true))) return st;
+  const Range out_r = rows_range(out, s->rows, ld_out, s->H, 2);
+  if ((st = check_output_disjoint(s, "out", out_r, true))) return st;
+  const uint16_t* extra_rows = nullptr;
+  if (with_extra) {
+    if ((st = check_rows_tensor("extra", extra, ld_extra, s->H, any))) return st;
+    if (any) {
+      extra_rows = static_cast<const uint16_t*>(extra) + s->row_begin * ld_extra;
+      if (overlap(out_r, rows_range(extra_rows, s->rows, ld_extra, s->H, 2)))
+        return fail(BND_ERR_INVALID_ARG, "out overlaps extra");
+    }
+  }
   if (any) {
     Launch l;
     if ((st = choose_launch(s->H, s->rows, &l))) return st;
     RowArgs a = base_args(s);
     pending_args(s, &a);
+    a.extra = extra_rows;
+    a.ld_extra = ld_extra;
     a.y = static_cast<uint16_t*>(out);
     a.ld_y = ld_out;
     const Source src = s->kind == BND_KIND_MOE ? Source::Moe : Source::Partials;
     const int n = s->kind == BND_KIND_MOE ? s->k : s->nsrc;
-    if ((st = launch_status(bnd::launch_complete(src, n, a, l, (hipStream_t)hip_stream), "complete_only")))
+    if ((st = launch_status(bnd::launch_complete(src, n, false, a, l, (hipStream_t)hip_stream), name)))
       return st;
   }
   // the stream now owes one plain partial: `out`, addressed by slice row
@@ -567,6 +583,65 @@ bnd_status bnd_complete_only(bnd_stream* s, bnd_owed owed, void* out, int64_t ld
   s->epoch++;
   s->owed = make_owed(s);
   *new_owed = s->owed;
+  return ok();
+}
+
+bnd_status bnd_complete_only(bnd_stream* s, bnd_owed owed, void* out, int64_t ld_out, bnd_owed* new_owed,
+                             void* hip_stream) {
+  return complete_into(s, owed, false, nullptr, 0, out, ld_out, new_owed, hip_stream, "complete_only");
+}
+
+bnd_status bnd_add_to_output(bnd_stream* s, bnd_owed owed, const void* extra, int64_t ld_extra, void* out,
+                             int64_t ld_out, bnd_owed* new_owed, void* hip_stream) {
+  return complete_into(s, owed, true, extra, ld_extra, out, ld_out, new_owed, hip_stream, "add_to_output");
+}
+
+bnd_status bnd_snapshot(bnd_stream* s, bnd_owed owed, void* out, int64_t ld_out, void* hip_stream) {
+  if (!s) return fail(BND_ERR_INVALID_ARG, "stream is NULL");
+  if (s->state == BND_INITIAL) return fail(BND_ERR_NOT_STARTED, "the stream has no residual and owes nothing");
+  if (s->state == BND_WRITTEN && owed != BND_OWED_NONE)
+    return fail(BND_ERR_FOREIGN_OUTPUT, "the stream owes nothing; the handle is foreign");
+  if (s->state == BND_PENDING) {
+    if (s->kind == BND_KIND_MOE)
+      return fail(BND_ERR_WRONG_KIND, "a snapshot needs a plain contribution; complete the MoE handoff first");
+    if (owed != s->owed) return fail(BND_ERR_FOREIGN_OUTPUT, "the handle does not belong to this stream's pending output");
+  }
+  const bool any = s->rows > 0;
+  bnd_status st;
+  if ((st = check_rows_tensor("out", out, ld_out, s->H, any))) return st;
+  if ((st = check_output_disjoint(s, "out", rows_range(out, s->rows, ld_out, s->H, 2), true))) return st;
+  if (any) {
+    Launch l;
+    if ((st = choose_launch(s->H, s->rows, &l))) return st;
+    RowArgs a = base_args(s);
+    a.y = static_cast<uint16_t*>(out);
+    a.ld_y = ld_out;
+    Source src = Source::Residual;
+    int n = 0;
+    if (s->state == BND_PENDING) {
+      pending_args(s, &a);
+      src = Source::Partials;
+      n = s->nsrc;
+    }
+    if ((st = launch_status(bnd::launch_complete(src, n, true, a, l, (hipStream_t)hip_stream), "snapshot")))
+      return st;
+  }
+  return ok();
+}
+
+bnd_status bnd_rsv_share(const int64_t* counts, int R, int r, int64_t* row_begin, int64_t* rows, int64_t* T) {
+  if (!counts || !row_begin || !rows || !T) return fail(BND_ERR_INVALID_ARG, "NULL argument");
+  if (R < 1 || r < 0 || r >= R) return fail(BND_ERR_INVALID_ARG, "rank %d outside [0, %d)", r, R);
+  int64_t begin = 0, total = 0;
+  for (int i = 0; i < R; ++i) {
+    if (counts[i] < 0) return fail(BND_ERR_INVALID_ARG, "rank %d has a negative row count", i);
+    if (total > INT64_MAX - counts[i]) return fail(BND_ERR_INVALID_ARG, "row counts overflow");
+    if (i == r) begin = total;
+    total += counts[i];
+  }
+  *row_begin = begin;
+  *rows = counts[r];
+  *T = total;
   return ok();
 }
 

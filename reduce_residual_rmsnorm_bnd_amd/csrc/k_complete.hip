@@ -1,4 +1,6 @@
-// complete_only: the owed sum alone (P partials or k MoE picks), stored bf16.
+// complete_only and add_to_output (the owed sum of P partials or k MoE picks,
+// plus an optional extra row, stored bf16) and snapshot (residual plus the sum
+// of P partials, or a copy of the residual, stored bf16 into a separate output).
 #include "kernels.h"
 
 namespace bnd {
@@ -6,18 +8,26 @@ namespace bnd {
 namespace {
 using Seq = std::make_integer_sequence<int, kMaxSources>;
 constexpr std::array<std::array<KernelFn, kMaxSources>, 3> kPartials = {
-    complete_table<Source::Partials, 1>(Seq{}), complete_table<Source::Partials, 2>(Seq{}),
-    complete_table<Source::Partials, 4>(Seq{})};
+    complete_table<Source::Partials, 1, false>(Seq{}), complete_table<Source::Partials, 2, false>(Seq{}),
+    complete_table<Source::Partials, 4, false>(Seq{})};
+constexpr std::array<std::array<KernelFn, kMaxSources>, 3> kPartialsFold = {
+    complete_table<Source::Partials, 1, true>(Seq{}), complete_table<Source::Partials, 2, true>(Seq{}),
+    complete_table<Source::Partials, 4, true>(Seq{})};
 constexpr std::array<std::array<KernelFn, kMaxSources>, 3> kMoe = {
-    complete_table<Source::Moe, 1>(Seq{}), complete_table<Source::Moe, 2>(Seq{}),
-    complete_table<Source::Moe, 4>(Seq{})};
+    complete_table<Source::Moe, 1, false>(Seq{}), complete_table<Source::Moe, 2, false>(Seq{}),
+    complete_table<Source::Moe, 4, false>(Seq{})};
+constexpr KernelFn kCopy[3] = {&complete_kernel<Source::Residual, 0, 1, true>,
+                               &complete_kernel<Source::Residual, 0, 2, true>,
+                               &complete_kernel<Source::Residual, 0, 4, true>};
 }  // namespace
 
-hipError_t launch_complete(Source src, int n, const RowArgs& a, const Launch& l, hipStream_t stream) {
+hipError_t launch_complete(Source src, int n, bool fold, const RowArgs& a, const Launch& l, hipStream_t stream) {
   const int slot = vpt_slot(l.vpt);
-  if (slot < 0 || n < 1 || n > kMaxSources) return hipErrorInvalidValue;
-  if (src == Source::Partials) return launch_kernel(kPartials[slot][n - 1], a, l, stream);
-  if (src == Source::Moe) return launch_kernel(kMoe[slot][n - 1], a, l, stream);
+  if (slot < 0) return hipErrorInvalidValue;
+  if (src == Source::Residual) return fold ? launch_kernel(kCopy[slot], a, l, stream) : hipErrorInvalidValue;
+  if (n < 1 || n > kMaxSources) return hipErrorInvalidValue;
+  if (src == Source::Partials) return launch_kernel((fold ? kPartialsFold : kPartials)[slot][n - 1], a, l, stream);
+  if (src == Source::Moe && !fold) return launch_kernel(kMoe[slot][n - 1], a, l, stream);
   return hipErrorInvalidValue;
 }
 

@@ -377,8 +377,11 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
   }
 }
 
-// complete_only: the contribution alone, stored as bf16.
-template <Source S, int N, int VPT>
+// complete_only / add_to_output (kFold = false): the contribution, plus the
+// extra row when one is given, stored as bf16. snapshot (kFold = true): the
+// folded row r + s stored as bf16 into a separate output; the residual is
+// only read.
+template <Source S, int N, int VPT, bool kFold>
 __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -387,7 +390,19 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
 #pragma unroll
   for (int v = 0; v < VPT; ++v) ok[v] = (tid + v * nthr) < a.nvec;
   float s[VPT][8];
-  load_and_fold<S, N, VPT, false>(a, row, tid, nthr, ok, s);
+  load_and_fold<S, N, VPT, kFold>(a, row, tid, nthr, ok, s);
+  if constexpr (!kFold) {
+    if (a.extra) {
+      const Rsrc ex = row_rsrc(a.extra + row * a.ld_extra, a.H * 2);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        float t[8];
+        bf16x8_to_f32(load16(ex, (tid + v * nthr) * 16), t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[v][e] += t[e];
+      }
+    }
+  }
   const Rsrc out = row_rsrc(a.y + row * a.ld_y, a.H * 2);
 #pragma unroll
   for (int v = 0; v < VPT; ++v)
@@ -404,9 +419,9 @@ constexpr std::array<KernelFn, sizeof...(I)> read_table(std::integer_sequence<in
   return {{&read_kernel<S, I + 1, VPT, FP8>...}};
 }
 
-template <Source S, int VPT, int... I>
+template <Source S, int VPT, bool kFold, int... I>
 constexpr std::array<KernelFn, sizeof...(I)> complete_table(std::integer_sequence<int, I...>) {
-  return {{&complete_kernel<S, I + 1, VPT>...}};
+  return {{&complete_kernel<S, I + 1, VPT, kFold>...}};
 }
 
 inline hipError_t launch_kernel(KernelFn fn, const RowArgs& a, const Launch& l, hipStream_t stream) {

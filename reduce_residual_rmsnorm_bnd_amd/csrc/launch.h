@@ -22,6 +22,8 @@ struct RowArgs {
   int64_t n_expert_rows;
   const int32_t* idx;                // MoE [rows, k], offset to the first row
   const float* gate;                 // MoE [rows, k]
+  const uint16_t* extra;             // add_to_output: a contribution added once after the sum
+  int64_t ld_extra;
   const uint16_t* x_in;              // stack input (enter)
   int64_t ld_x;
   uint16_t* res;                     // residual storage
@@ -55,8 +57,9 @@ enum class Source { Partials, Moe, Input, Residual };
 hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Launch& l,
                        hipStream_t stream);
 
-// complete_only: y <- bf16(sum) for partials or MoE picks.
-hipError_t launch_complete(Source src, int n, const RowArgs& a, const Launch& l,
+// complete_only / add_to_output: y <- bf16(sum [+ extra]) for partials or MoE picks.
+// With fold, y <- bf16(residual + sum) (snapshot); Residual with n = 0 copies the residual.
+hipError_t launch_complete(Source src, int n, bool fold, const RowArgs& a, const Launch& l,
                            hipStream_t stream);
 
 }  // namespace bnd

@@ -251,6 +251,50 @@ def pin_bruteforce_complete(o):
                 assert int(out["out"][t, h]) == b
 
 
+def pin_add_to_output(o):
+    """Complete, then add the extra once: exact brute force, and a zero extra is complete_only."""
+    parts, _, _ = _tiny_fold_case(43, 3, 16, 3, wide=True)
+    extra = bits(bval(_tiny_fold_case(44, 3, 16, 1, wide=True)[0][0]))
+    out = o.complete_partials(parts, extra=extra, row_begin=1, rows=2)
+    for i in range(2):
+        s = _exact_contrib_partials(parts, 1 + i, 16)
+        for h in range(16):
+            v = s[h] + exact.bf16_value(int(extra[1 + i, h]))
+            assert Fraction(out["s_exact"][i, h]) == v
+            assert int(out["out"][i, h]) == exact.bf16_round(v)[0]
+    z = o.complete_partials(parts, extra=np.zeros_like(parts[0]))
+    assert np.array_equal(z["out"], o.complete_partials(parts)["out"])
+    E, idx, gate, _, _ = _tiny_moe_case(45, 3, 8, 5, 2)
+    ex = workloads.bf16_bits(workloads.to_bf16(workloads.normal_f32(45, 9, (3, 8)))).copy()
+    m = o.complete_moe(E, idx, gate, 2, extra=ex)
+    for t in range(3):
+        s = _exact_contrib_moe(E, idx, gate, 2, t, 8)
+        for h in range(8):
+            v = s[h] + exact.bf16_value(int(ex[t, h]))
+            b, tie = exact.bf16_round(v)
+            if tie > abs(v) * Fraction(1, 10**12):
+                assert int(m["out"][t, h]) == b
+
+
+def pin_snapshot(o):
+    """bf16(r + s) on the side: exact brute force, equal to the fold's stored residual, and a
+    plain copy when nothing is owed."""
+    parts, res_full, w = _tiny_fold_case(46, 4, 16, 3, wide=True)
+    snap = o.snapshot(parts, res_full[1:].copy(), row_begin=1, rows=3)
+    for i in range(3):
+        s = _exact_contrib_partials(parts, 1 + i, 16)
+        for h in range(16):
+            x = exact.bf16_value(int(res_full[1 + i, h])) + s[h]
+            assert Fraction(snap["x_exact"][i, h]) == x
+            assert int(snap["out"][i, h]) == exact.bf16_round(x)[0]
+    fold = o.fold_norm(parts, res_full[1:].copy(), w, 1e-6, row_begin=1, rows=3)
+    assert np.array_equal(snap["out"], fold["residual"])
+    nores = o.snapshot(parts, None)
+    assert np.array_equal(nores["out"], o.complete_partials(parts)["out"])
+    copy = o.snapshot([], res_full)
+    assert np.array_equal(copy["out"], res_full)
+
+
 # ---------------------------------------------------------------- number formats
 
 def pin_bf16_codec(o):
@@ -350,4 +394,4 @@ def pin_invariants(o):
 
 PINS = [pin_e1_closed_form, pin_e2_fold, pin_e3_eps_inside_root, pin_e4_one_hot, pin_e5_fp8,
         pin_e6_zero_row, pin_e7_gemma, pin_bruteforce_fold, pin_bruteforce_fp8, pin_bruteforce_moe,
-        pin_bruteforce_complete, pin_bf16_codec, pin_e4m3_codec, pin_invariants]
+        pin_bruteforce_complete, pin_add_to_output, pin_snapshot, pin_bf16_codec, pin_e4m3_codec, pin_invariants]

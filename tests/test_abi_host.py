@@ -63,7 +63,7 @@ def owed_out():
 
 def test_library_exports_every_declared_symbol():
     decl = re.findall(r"^BND_API\s+[\w\s\*]+?\b(bnd_\w+)\s*\(", open(HEADER).read(), flags=re.M)
-    assert len(decl) == len(set(decl)) == 21
+    assert len(decl) == len(set(decl)) == 24
     assert sorted(decl) == sorted(B.SYMBOLS)
     for name in decl:
         assert hasattr(L, name), name
@@ -108,6 +108,10 @@ def _call(h, call, owed):
         return L.bnd_moe_finalize_fold_norm(h, owed or 0, w, 1e-6, None, H, None)
     if call == "complete_only":
         return L.bnd_complete_only(h, owed or 0, None, H, ctypes.byref(o), None)
+    if call == "add_to_output":
+        return L.bnd_add_to_output(h, owed or 0, None, H, None, H, ctypes.byref(o), None)
+    if call == "snapshot":
+        return L.bnd_snapshot(h, owed or 0, None, H, None)
     if call == "publish_partials":
         return L.bnd_publish_partials(h, (VP * 1)(None), 1, H, ctypes.byref(o))
     if call == "publish_moe":
@@ -283,6 +287,48 @@ def test_norm_form_validation():
     assert L.bnd_stream_set_norm_form(h, 2) == B.BND_ERR_INVALID_ARG
     assert L.bnd_stream_set_norm_form(None, 0) == B.BND_ERR_INVALID_ARG
     assert L.bnd_stream_state(h) == B.BND_INITIAL
+
+
+def test_snapshot_keeps_the_owed_work():
+    h = create()
+    o = _to_state(h, "PENDING_PARTIALS")
+    assert L.bnd_snapshot(h, o, None, H, None) == 0
+    assert L.bnd_stream_state(h) == B.BND_PENDING and L.bnd_stream_pending_kind(h) == B.BND_KIND_PARTIALS
+    assert L.bnd_fold_norm(h, o, None, 1e-6, None, H, None) == 0  # the same handle still folds
+    assert L.bnd_snapshot(h, o, None, H, None) == B.BND_ERR_FOREIGN_OUTPUT  # Written: nothing owed
+    assert L.bnd_snapshot(h, 0, None, H, None) == 0
+
+
+def test_add_to_output_validation():
+    h, o = _pending()
+    new = owed_out()
+    # extra required, aligned, and not overlapping the output
+    assert L.bnd_add_to_output(h, o, None, H, fake(1 << 30), H, ctypes.byref(new), None) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_add_to_output(h, o, fake((1 << 29) + 2), H, fake(1 << 30), H, ctypes.byref(new), None) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_add_to_output(h, o, fake(1 << 30), H, fake(1 << 30), H, ctypes.byref(new), None) == B.BND_ERR_INVALID_ARG
+    _unchanged(h)
+
+
+def test_rsv_share():
+    counts = [300, 0, 511, 256, 257, 1, 400, 322]
+    T = sum(counts)
+    begin = 0
+    for r, c in enumerate(counts):
+        b, n, t = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        assert L.bnd_rsv_share((ctypes.c_int64 * 8)(*counts), 8, r, ctypes.byref(b), ctypes.byref(n),
+                               ctypes.byref(t)) == 0
+        assert (b.value, n.value, t.value) == (begin, c, T)
+        begin += c
+    assert bnd.bnd_rsv_share(counts, 2) == (300, 511, T)
+    b, n, t = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    arr = (ctypes.c_int64 * 3)(4, -1, 2)
+    assert L.bnd_rsv_share(arr, 3, 0, ctypes.byref(b), ctypes.byref(n), ctypes.byref(t)) == B.BND_ERR_INVALID_ARG
+    arr = (ctypes.c_int64 * 3)(4, 1, 2)
+    assert L.bnd_rsv_share(arr, 3, 3, ctypes.byref(b), ctypes.byref(n), ctypes.byref(t)) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_rsv_share(arr, 3, -1, ctypes.byref(b), ctypes.byref(n), ctypes.byref(t)) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_rsv_share(None, 3, 0, ctypes.byref(b), ctypes.byref(n), ctypes.byref(t)) == B.BND_ERR_INVALID_ARG
+    big = (ctypes.c_int64 * 2)(2**62, 2**62)
+    assert L.bnd_rsv_share(big, 2, 1, ctypes.byref(b), ctypes.byref(n), ctypes.byref(t)) == B.BND_ERR_INVALID_ARG
 
 
 def test_options_validation():

@@ -584,3 +584,122 @@ def test_gemma_terminal_moe_finalize(orc):
     d = workloads.moe_inputs(74, 512, 4096, 128, 8, w_mean=0.0, w_std=0.1)
     run_moe(orc, d, 0, 512, "terminal MoE finalize, Gemma weight", gemma=True, terminal=True)
     run_moe(orc, d, 192, 64, "terminal MoE finalize share, Gemma weight", gemma=True, terminal=True)
+
+
+# ------------------------------------------------------------------ variable-size shares (RSv)
+
+RSV_COUNTS = [300, 0, 511, 256, 257, 1, 400, 322]  # T = 2047, not a multiple of the rank count
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_rsv_shares_tile_the_batch(orc, fp8):
+    T = sum(RSV_COUNTS)
+    d = workloads.fold_inputs(81, T, 4096, 8)
+    full = run_fold(d, fp8=fp8)
+    key = "q" if fp8 else "y"
+    for r in range(len(RSV_COUNTS)):
+        rb, rows, t = bnd.bnd_rsv_share(RSV_COUNTS, r)
+        assert t == T
+        part = run_fold(d, row_begin=rb, rows=rows, fp8=fp8)
+        assert torch.equal(part[key].view, full[key].view[rb:rb + rows])
+        assert torch.equal(part["res"].view, full["res"].view[rb:rb + rows])
+        if fp8:
+            assert torch.equal(part["scale_buf"][1:rows + 1], full["scale_buf"][1 + rb:1 + rb + rows])
+    for r in (2, 5):
+        rb, rows, _ = bnd.bnd_rsv_share(RSV_COUNTS, r)
+        assert_fold_matches(orc, d, f"RSv share {r} ({rows} rows at {rb})", fp8=fp8, row_begin=rb,
+                            rows=rows)
+
+
+def test_rsv_moe_shares(orc):
+    counts = [5, 17, 0, 42]
+    d = workloads.moe_inputs(82, sum(counts), 2048, 32, 8)
+    full_res, full_y = run_moe(orc, d, 0, sum(counts), "MoE RSv full")
+    for r in range(len(counts)):
+        rb, rows, _ = bnd.bnd_rsv_share(counts, r)
+        res, y = run_moe(orc, d, rb, rows, f"MoE RSv share {r}")
+        assert torch.equal(y.view, full_y.view[rb:rb + rows])
+
+
+# ------------------------------------------------------------------ add_to_output, snapshot
+
+def test_add_to_output_then_fold(orc):
+    T, H, P = 40, 4096, 8
+    d = workloads.fold_inputs(83, T, H, P)
+    extra = workloads.to_bf16(workloads.normal_f32(83, 12345, (T, H), 0.0, 0.25))
+    rb, rows = 8, 24
+    res = Guarded(rows, H).from_host(d["residual"][rb:rb + rows])
+    out = Guarded(rows, H)
+    y = Guarded(rows, H)
+    w = d["weight"].to(DEV)
+    s = bnd.bnd_stream_create(T, H, res.view, rb, rows)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_partials(s, [c.to(DEV) for c in d["partials"]])
+    owed2 = bnd.bnd_add_to_output(s, owed, extra.to(DEV), out.view)
+    assert s.state == bnd.BND_PENDING and s.pending_kind == bnd.BND_KIND_PARTIALS
+    res_before = res.view.clone()
+    bnd.bnd_fold_norm(s, owed2, w, d["eps"], y.view)
+    torch.cuda.synchronize()
+    for g in (res, out, y):
+        g.check_guards("add_to_output")
+    c = orc.complete_partials([bits(p) for p in d["partials"]], extra=bits(extra), row_begin=rb,
+                              rows=rows)
+    tolerance.check_bf16(bits(out.view), c["s_exact"], c["mag"], "add_to_output out")
+    assert not torch.equal(res.view, res_before)
+    ref = orc.fold_norm([c["out"]], bits(d["residual"][rb:rb + rows]), d["weight"].numpy(), d["eps"])
+    check_fold(ref, bits(res.view), bits(y.view), d["weight"].numpy(), d["eps"], "add_to_output fold")
+
+
+def test_add_to_output_on_moe_handoff(orc):
+    d = workloads.moe_inputs(84, 33, 2048, 16, 4)
+    T, H, k = 33, 2048, 4
+    extra = workloads.to_bf16(workloads.normal_f32(84, 12345, (T, H), 0.0, 0.25))
+    E, idx, gate = _moe_device(d)
+    res = Guarded(T, H).from_host(d["residual"])
+    out = Guarded(T, H)
+    s = bnd.bnd_stream_create(T, H, res.view)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_moe(s, E, idx, gate, k)
+    bnd.bnd_add_to_output(s, owed, extra.to(DEV), out.view)
+    torch.cuda.synchronize()
+    c = orc.complete_moe(bits(d["expert_rows"]), d["idx"].numpy(), d["gate"].numpy(), k,
+                         extra=bits(extra))
+    tolerance.check_bf16(bits(out.view), c["s_exact"], c["mag"], "MoE add_to_output out")
+
+
+def test_snapshot_leaves_the_owed_work(orc):
+    T, H, P = 64, 4096, 8
+    d = workloads.fold_inputs(85, T, H, P)
+    res = Guarded(T, H).from_host(d["residual"])
+    snap = Guarded(T, H)
+    y = Guarded(T, H)
+    w = d["weight"].to(DEV)
+    s = bnd.bnd_stream_create(T, H, res.view)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_partials(s, [c.to(DEV) for c in d["partials"]])
+    before = res.view.clone()
+    bnd.bnd_snapshot(s, owed, snap.view)
+    torch.cuda.synchronize()
+    assert torch.equal(res.view, before), "a snapshot must not touch the residual"
+    assert s.state == bnd.BND_PENDING
+    ref = orc.snapshot([bits(c) for c in d["partials"]], bits(d["residual"]))
+    tolerance.check_bf16(bits(snap.view), ref["x_exact"], ref["mag"], "snapshot")
+    bnd.bnd_fold_norm(s, owed, w, d["eps"], y.view)   # the same handle still folds
+    torch.cuda.synchronize()
+    assert torch.equal(snap.view, res.view), "the snapshot is the residual the fold stores"
+    snap2 = Guarded(T, H)
+    bnd.bnd_snapshot(s, bnd.BND_OWED_NONE, snap2.view)  # Written: a copy of the residual
+    torch.cuda.synchronize()
+    assert torch.equal(snap2.view, res.view)
+    for g in (res, snap, snap2, y):
+        g.check_guards("snapshot")
+    # a MoE handoff is refused and left pending
+    dm = workloads.moe_inputs(86, 8, 1024, 8, 2)
+    E, idx, gate = _moe_device(dm)
+    r2 = Guarded(8, 1024).from_host(dm["residual"])
+    s2 = bnd.bnd_stream_create(8, 1024, r2.view)
+    bnd.bnd_written(s2, r2.view)
+    o2 = bnd.bnd_publish_moe(s2, E, idx, gate, 2)
+    with pytest.raises(bnd.BoundaryError) as e:
+        bnd.bnd_snapshot(s2, o2, Guarded(8, 1024).view)
+    assert e.value.status == bnd.BND_ERR_WRONG_KIND and s2.state == bnd.BND_PENDING

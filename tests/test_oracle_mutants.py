@@ -49,6 +49,12 @@ MUTANTS = {
     "fnuz_max": ("float scale = (float)(amax / 448.0);", "float scale = (float)(amax / 240.0);"),
     "scale_inverted": ("double v = y[h] / (double)scale;", "double v = y[h] * (double)scale;"),
     "moe_index_ignored": ("int64_t e = idx[t * k + j];", "int64_t e = t * k + j;"),
+    "extra_dropped": ("if (extra) add_extra_row(H, extra + (row_begin + i) * ld_x, b.s, b.mag);",
+                      "(void)extra;"),
+    "extra_not_global_row": ("if (extra) add_extra_row(H, extra + (row_begin + i) * ld_x, b.s, b.mag);",
+                             "if (extra) add_extra_row(H, extra + i * ld_x, b.s, b.mag);"),
+    "snapshot_drops_residual": ("apply_update_row(H, residual ? residual + i * ld_r : NULL, b.s, b.x, b.mag);\n    store_bf16_row(H, b.x, out + i * ld_o);",
+                                "apply_update_row(H, NULL, b.s, b.x, b.mag);\n    store_bf16_row(H, b.x, out + i * ld_o);"),
 }
 
 
