@@ -139,26 +139,54 @@ bnd_status check_weight(const float* w, float eps, bool needed) {
   return BND_OK;
 }
 
+// Compute units of the current device (256 on MI355X), read once.
+int compute_units() {
+  static std::atomic<int> cus{0};
+  int n = cus.load();
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+    cus.store(n);
+  }
+  return n;
+}
+
 // Launch shape: one workgroup per row; threads * vpt vectors of 8 elements
-// must cover the row. Default, from same-process launch-shape comparisons on
-// MI355X: two vectors per thread once a row has more than 256 vectors
-// (H > 2048), four beyond 2048 vectors (H > 16384). With two vectors and
-// P = 8 a kernel needs about 60 VGPRs, so eight 4-wave workgroups fit on a
-// CU and all 2048 rows of a prefill batch are resident at once (one vector
-// per thread with 8-wave workgroups measured 4% slower). Workgroups of at
-// least 256 threads are rounded up to whole multiples of 256 so every SIMD
-// of the CU gets the same number of waves (7- or 5-wave workgroups measured
-// 3-6% slower than 8- or 4-wave ones).
+// must cover the row. Defaults, from launch-shape sweeps on MI355X:
+//  - one vector per thread while every row of the launch can be resident at
+//    once with that shape (rows * waves per row <= 32 waves per CU): more
+//    waves per row hide more latency, 5-11% faster for 128..1024 rows;
+//  - otherwise two vectors per thread (H <= 16384), four beyond: with two
+//    vectors and P = 8 a kernel needs about 60 VGPRs, eight 4-wave workgroups
+//    fit on a CU and all 2048 rows of a prefill batch are resident together
+//    (8-wave workgroups would need two rounds, 4% slower);
+//  - workgroups of at least 256 threads are rounded up to whole multiples of
+//    256 so every SIMD of the CU gets the same number of waves (7- or 5-wave
+//    workgroups measured 3-6% slower than 8- or 4-wave ones).
+int round_threads(int need) {
+  const int unit = need >= 256 ? 4 * bnd::kWave : bnd::kWave;
+  return ((need + unit - 1) / unit) * unit;
+}
+
 bnd_status choose_launch(int64_t H, int64_t rows, Launch* l) {
   const int nvec = (int)(H / 8);
   int vpt = g_vpt_override.load();
   int threads = g_threads_override.load();
-  if (vpt == 0) vpt = nvec <= 256 ? 1 : nvec <= 2048 ? 2 : 4;
-  if (threads == 0) {
-    const int need = (nvec + vpt - 1) / vpt;
-    const int unit = need >= 256 ? 4 * bnd::kWave : bnd::kWave;
-    threads = ((need + unit - 1) / unit) * unit;
+  if (vpt == 0) {
+    if (nvec <= 256) {
+      vpt = 1;
+    } else if (nvec <= 1024 &&
+               rows * (int64_t)(round_threads(nvec) / bnd::kWave) <= (int64_t)compute_units() * 32) {
+      vpt = 1;
+    } else {
+      vpt = nvec <= 2048 ? 2 : 4;
+    }
   }
+  if (threads == 0) threads = round_threads((nvec + vpt - 1) / vpt);
   if (vpt != 1 && vpt != 2 && vpt != 4)
     return fail(BND_ERR_NO_PATH, "vectors per thread %d: need 1, 2 or 4", vpt);
   if (threads < bnd::kWave || threads > bnd::kMaxThreads || threads % bnd::kWave != 0)

@@ -41,6 +41,25 @@ def bits(t):
     return workloads.bf16_bits(t.detach().cpu().contiguous())
 
 
+class forced_shape:
+    """Pin the launch shape (threads per row, vectors per thread) for a block of calls.
+
+    The residual is elementwise and does not depend on the launch shape; the read's sum of
+    squares is reduced in an order fixed by the shape, so comparisons of y between calls with
+    different row counts are bit-exact only under one shape."""
+
+    def __init__(self, threads, vpt):
+        self.threads, self.vpt = threads, vpt
+
+    def __enter__(self):
+        bnd.set_option(bnd.BND_OPT_THREADS_PER_ROW, self.threads)
+        bnd.set_option(bnd.BND_OPT_VECTORS_PER_THREAD, self.vpt)
+
+    def __exit__(self, *exc):
+        bnd.set_option(bnd.BND_OPT_THREADS_PER_ROW, 0)
+        bnd.set_option(bnd.BND_OPT_VECTORS_PER_THREAD, 0)
+
+
 class Guarded:
     """A [rows, H] view inside a canary-filled buffer with guard rows and padded columns."""
 
@@ -235,9 +254,13 @@ def test_moe_full_and_slice(orc):
     full_res, full_y = run_moe(orc, d, 0, d["T"], "MoE T=2048 H=4096 k=8")
     rb, rows = workloads.MOE_SLICE
     sl_res, sl_y = run_moe(orc, d, rb, rows, "MoE slice rows 768..1023")
-    # the slice computes exactly the same rows as the full call
-    assert torch.equal(sl_y.view, full_y.view[rb:rb + rows])
+    # the slice stores exactly the residual rows of the full call, whatever the launch shapes
     assert torch.equal(sl_res.view, full_res.view[rb:rb + rows])
+    # and under one launch shape exactly the same y
+    with forced_shape(256, 2):
+        _, fy = run_moe(orc, d, 0, d["T"], "MoE full, 256x2")
+        _, sy = run_moe(orc, d, rb, rows, "MoE slice, 256x2")
+    assert torch.equal(sy.view, fy.view[rb:rb + rows])
 
 
 @pytest.mark.parametrize("T", [1, 8, 32, 128])
@@ -387,11 +410,13 @@ def test_invariant_moe_over_stacked_partials_is_fold(orc):
 
 def test_invariant_slice_equals_full_rows(orc):
     d = workloads.fold_inputs(24, 64, 4096, 8)
-    full = run_fold(d)
-    for rb, rows in ((0, 8), (24, 16), (56, 8), (63, 1)):
-        part = run_fold(d, row_begin=rb, rows=rows)
-        assert torch.equal(part["y"].view, full["y"].view[rb:rb + rows])
-        assert torch.equal(part["res"].view, full["res"].view[rb:rb + rows])
+    for shape in ((256, 2), (512, 1)):
+        with forced_shape(*shape):
+            full = run_fold(d)
+            for rb, rows in ((0, 8), (24, 16), (56, 8), (63, 1)):
+                part = run_fold(d, row_begin=rb, rows=rows)
+                assert torch.equal(part["y"].view, full["y"].view[rb:rb + rows])
+                assert torch.equal(part["res"].view, full["res"].view[rb:rb + rows])
 
 
 # ------------------------------------------------------------------ unfused fallback
@@ -595,16 +620,21 @@ RSV_COUNTS = [300, 0, 511, 256, 257, 1, 400, 322]  # T = 2047, not a multiple of
 def test_rsv_shares_tile_the_batch(orc, fp8):
     T = sum(RSV_COUNTS)
     d = workloads.fold_inputs(81, T, 4096, 8)
-    full = run_fold(d, fp8=fp8)
     key = "q" if fp8 else "y"
+    full = run_fold(d, fp8=fp8)
+    with forced_shape(256, 2):
+        full_f = run_fold(d, fp8=fp8)
     for r in range(len(RSV_COUNTS)):
         rb, rows, t = bnd.bnd_rsv_share(RSV_COUNTS, r)
         assert t == T
         part = run_fold(d, row_begin=rb, rows=rows, fp8=fp8)
-        assert torch.equal(part[key].view, full[key].view[rb:rb + rows])
         assert torch.equal(part["res"].view, full["res"].view[rb:rb + rows])
+        with forced_shape(256, 2):
+            part_f = run_fold(d, row_begin=rb, rows=rows, fp8=fp8)
+        assert torch.equal(part_f[key].view, full_f[key].view[rb:rb + rows])
         if fp8:
-            assert torch.equal(part["scale_buf"][1:rows + 1], full["scale_buf"][1 + rb:1 + rb + rows])
+            assert torch.equal(part_f["scale_buf"][1:rows + 1],
+                               full_f["scale_buf"][1 + rb:1 + rb + rows])
     for r in (2, 5):
         rb, rows, _ = bnd.bnd_rsv_share(RSV_COUNTS, r)
         assert_fold_matches(orc, d, f"RSv share {r} ({rows} rows at {rb})", fp8=fp8, row_begin=rb,
@@ -618,7 +648,8 @@ def test_rsv_moe_shares(orc):
     for r in range(len(counts)):
         rb, rows, _ = bnd.bnd_rsv_share(counts, r)
         res, y = run_moe(orc, d, rb, rows, f"MoE RSv share {r}")
-        assert torch.equal(y.view, full_y.view[rb:rb + rows])
+        assert torch.equal(res.view, full_res.view[rb:rb + rows])
+        assert torch.equal(y.view, full_y.view[rb:rb + rows])  # same shape: fewer rows than CUs
 
 
 # ------------------------------------------------------------------ add_to_output, snapshot
