@@ -351,6 +351,64 @@ def copy_ceiling(torch, n_bytes=1 << 30, reps=20):
     return {"bytes": 2 * n_bytes, "GBps": 2 * n_bytes / t / 1e9}
 
 
+def device_memory_info():
+    """Memory clock and bus width as the HIP runtime reports them, and the peak they imply."""
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    dev = ctypes.c_int()
+    if hip.hipGetDevice(ctypes.byref(dev)) != 0:
+        return None
+    vals = {}
+    # hipDeviceAttributeMemoryClockRate = 60, MemoryBusWidth = 59, MultiprocessorCount = 63
+    for name, attr in (("memory_clock_khz", 60), ("memory_bus_width_bits", 59),
+                       ("compute_units", 63)):
+        v = ctypes.c_int()
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) == 0:
+            vals[name] = v.value
+    return vals
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads_baseline(workloads, d, budget_s: float, threads: int):
+    """The same oracle function over row chunks, one chunk per host thread (ctypes releases
+    the GIL); only the harness partitions the rows."""
+    import concurrent.futures as cf
+
+    import oracle
+
+    o = oracle.Oracle()
+    parts = [workloads.bf16_bits(c) for c in d["partials"]]
+    res = workloads.bf16_bits(d["residual"])
+    w = d["weight"].numpy()
+    T = d["T"]
+    bounds = [(T * i // threads, T * (i + 1) // threads) for i in range(threads)]
+
+    def chunk(b):
+        lo, hi = b
+        o.fold_norm(parts, res[lo:hi].copy(), w, d["eps"], row_begin=lo, rows=hi - lo)
+
+    passes = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        while True:
+            list(ex.map(chunk, bounds))
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    return {"value": passes * T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} passes of the full prefill boundary split into {threads} row "
+                      f"chunks in {el:.1f} s, fp64", "cpu": cpu_model()}
+
+
 def cpu_baseline(workloads, d, budget_s: float):
     """The fp64 oracle (single-threaded) over the whole prefill workload, repeated."""
     import oracle
@@ -369,7 +427,7 @@ def cpu_baseline(workloads, d, budget_s: float):
             break
     return {"value": passes * d["T"] / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} passes of the full prefill boundary (2048 rows x 4096, P=8) "
-                      f"in {el:.1f} s, one thread, fp64"}
+                      f"in {el:.1f} s, one thread, fp64", "cpu": cpu_model()}
 
 
 def main():
@@ -426,7 +484,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill boundary fold+RMSNorm, T=2048 H=4096 P=8, bf16 in/out",
                    "T": 2048, "H": 4096, "P": 8, "rotation_sets": n_sets,
-                   "device": getattr(props, "gcnArchName", props.name), "storage": "bf16"},
+                   "device": getattr(props, "gcnArchName", props.name), "storage": "bf16",
+                   "device_memory": device_memory_info()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "kernel": "read_kernel<Partials, P=8, bf16 out> (bnd_fold_norm)",
@@ -502,6 +561,11 @@ def main():
         result["copy_reference_1GiB"] = copy_ceiling(torch)
     log(f"CPU baseline: the oracle for ~{args.cpu_seconds:.0f} s")
     result["cpu_baseline"] = cpu_baseline(workloads, d, args.cpu_seconds)
+    if not args.no_secondary:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        log(f"CPU baseline on {threads} threads for ~{args.cpu_seconds / 2:.0f} s")
+        result["secondary"]["cpu_baseline_threads"] = cpu_threads_baseline(
+            workloads, d, args.cpu_seconds / 2, threads)
     print(json.dumps(result), flush=True)
 
 
