@@ -287,20 +287,18 @@ template <int VPT>
 __device__ __forceinline__ void load_weight(const RowArgs& a, int tid, int nthr, float (&w)[VPT][8]) {
   // the weight is shared by all rows: default cache policy, it stays in L2
   const Rsrc wr = row_rsrc(a.w, a.H * 4);
-  const bool gemma = a.gemma != 0;
+  // Gemma form: the stored weight is an offset from one. Added without a branch (w + 0 for the
+  // plain form) so the weight loads schedule like the rest of the row's loads.
+  const float offset = a.gemma ? 1.0f : 0.0f;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int off = (tid + v * nthr) * 32;
     const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
     const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16, 0, 0);
-    w[v][0] = __uint_as_float(lo.x); w[v][1] = __uint_as_float(lo.y);
-    w[v][2] = __uint_as_float(lo.z); w[v][3] = __uint_as_float(lo.w);
-    w[v][4] = __uint_as_float(hi.x); w[v][5] = __uint_as_float(hi.y);
-    w[v][6] = __uint_as_float(hi.z); w[v][7] = __uint_as_float(hi.w);
-    if (gemma) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w[v][e] = 1.0f + w[v][e];
-    }
+    w[v][0] = __uint_as_float(lo.x) + offset; w[v][1] = __uint_as_float(lo.y) + offset;
+    w[v][2] = __uint_as_float(lo.z) + offset; w[v][3] = __uint_as_float(lo.w) + offset;
+    w[v][4] = __uint_as_float(hi.x) + offset; w[v][5] = __uint_as_float(hi.y) + offset;
+    w[v][6] = __uint_as_float(hi.z) + offset; w[v][7] = __uint_as_float(hi.w) + offset;
   }
 }
 
