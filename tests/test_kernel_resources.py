@@ -1,0 +1,79 @@
+"""Register budgets of the fold kernels, read from the compiler (no GPU needed).
+
+The launch heuristic gives a row one vector per thread when all rows fit on the chip at once,
+counting 32 resident waves per CU, i.e. 8 per SIMD. A wave holds 512 / 8 = 64 VGPRs at that
+occupancy, so the fold and read kernels with one or two vectors per thread and up to eight
+partial sources must stay within 64 VGPRs and never use scratch. A data-dependent branch around
+the Gemma weight offset once pushed the P = 8 fold to 100 VGPRs (half the resident rows, about
+a microsecond on the prefill boundary); this test fails on such a change before it reaches a
+benchmark.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "reduce_residual_rmsnorm_bnd_amd", "csrc")
+HIPCC = "/opt/rocm/bin/hipcc"
+
+# same device flags as the library build
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "--offload-device-only",
+         "-Rpass-analysis=kernel-resource-usage"]
+
+NAME = re.compile(r"Function Name: _ZN3bnd11read_kernelILNS_6SourceE(\d)ELi(\d+)ELi(\d)ELb([01])E")
+FIELD = re.compile(r"remark: +(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)")
+SOURCES = {0: "Partials", 1: "Moe", 2: "Input", 3: "Residual"}
+
+
+def _resources(tmp_path, files):
+    procs = {f: subprocess.Popen([HIPCC, *FLAGS, "-c", os.path.join(CSRC, f), "-o", str(tmp_path / (f + ".o"))],
+                                 cwd=CSRC, stderr=subprocess.PIPE, text=True) for f in files}
+    table = {}
+    for f, p in procs.items():
+        _, err = p.communicate(timeout=600)
+        assert p.returncode == 0, err[-3000:]
+        current = None
+        for line in err.splitlines():
+            m = NAME.search(line)
+            if m:
+                current = (SOURCES[int(m.group(1))], int(m.group(2)), int(m.group(3)), m.group(4) == "1")
+                table[current] = {}
+                continue
+            m = FIELD.search(line)
+            if m and current is not None and m.group(1) not in table[current]:
+                table[current][m.group(1)] = int(m.group(2))
+    return table
+
+
+@pytest.fixture(scope="module")
+def resources(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not installed")
+    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip"])
+
+
+def test_every_instance_reported(resources):
+    # 16 source counts x 3 vector counts x bf16/fp8 for partials; 3 x 2 each for input and residual
+    assert sum(1 for k in resources if k[0] == "Partials") == 96
+    assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
+
+
+def test_fold_kernels_fit_eight_waves_per_simd(resources):
+    over = {k: v["VGPRs"] for k, v in resources.items()
+            if k[2] <= 2 and (k[0] != "Partials" or k[1] <= 8) and v["VGPRs"] > 64}
+    assert not over, f"kernels above 64 VGPRs (fewer than 8 waves per SIMD): {over}"
+
+
+def test_prefill_fold_register_use(resources):
+    # the prefill boundary's kernel (P = 8, two vectors per thread), bf16 and fp8 outputs
+    for fp8 in (False, True):
+        r = resources[("Partials", 8, 2, fp8)]
+        assert r["VGPRs"] <= 64 and r["Occupancy [waves/SIMD]"] == 8, r
+
+
+def test_no_scratch(resources):
+    spilled = {k: v["ScratchSize [bytes/lane]"] for k, v in resources.items() if v["ScratchSize [bytes/lane]"]}
+    assert not spilled, f"kernels using scratch: {spilled}"
