@@ -10,8 +10,10 @@ synchronisations); the roofline block reports the kernel's algorithmic bytes
 over its average duration from HIP events recorded on the launch stream.
 
 Secondary measurements (the quantised read, the MoE finalize over all rows
-and over the reduce-scatter share, the decode chain eager and as a HIP graph)
-and the oracle's CPU baseline go into the same JSON line.
+and over the reduce-scatter share, the decode chain eager and as a HIP graph,
+a streaming kernel with the fold's 9:2 read:write mix and no arithmetic as an
+achievable-bandwidth context figure) and the oracle's CPU baseline go into the
+same JSON line.
 """
 from __future__ import annotations
 
@@ -351,6 +353,55 @@ def copy_ceiling(torch, n_bytes=1 << 30, reps=20):
     return {"bytes": 2 * n_bytes, "GBps": 2 * n_bytes / t / 1e9}
 
 
+def back_to_back_us(torch, launch, n_sets: int, reps: int = 300, warmup: int = 20) -> float:
+    """Mean time per launch of `reps` back-to-back launches, no per-launch events: events on
+    torch's current stream (where the launches go) around the whole run."""
+    for i in range(warmup):
+        launch(i % n_sets)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        launch((warmup + i) % n_sets)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def stream_ceiling(torch, T: int, H: int, fold_us: float):
+    """The 9:2 streaming kernel (libboundary_ceiling.so: the fold's rows, loads and stores, no
+    arithmetic) over rotating sets of the prefill shape, for three launch shapes; compared with
+    the fold timed the same way (back-to-back launches) in the same process."""
+    from reduce_residual_rmsnorm_bnd_amd import _build
+
+    L = ctypes.CDLL(_build.CEILING_LIB_PATH)
+    vp = ctypes.c_void_p
+    L.bnd_ceiling_mix_9r2w.argtypes = [ctypes.POINTER(vp), vp, vp, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp]
+    nbytes = 11 * T * H * 2
+    n_sets = max(2, -(-ROTATE_BYTES // nbytes))
+    sets = []
+    for _ in range(n_sets):
+        bufs = [torch.zeros(T, H, dtype=torch.bfloat16, device="cuda:0") for _ in range(11)]
+        sets.append((bufs, (vp * 9)(*[b.data_ptr() for b in bufs[:9]]), vp(bufs[9].data_ptr()),
+                     vp(bufs[10].data_ptr())))
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    shapes = {}
+    for threads, vpt in ((256, 2), (512, 1), (128, 4)):
+        def launch(i, threads=threads, vpt=vpt):
+            _, src, o0, o1 = sets[i]
+            rc = L.bnd_ceiling_mix_9r2w(src, o0, o1, T, H, H, threads, vpt, stream)
+            if rc:
+                raise RuntimeError(f"ceiling launch failed: {rc}")
+        shapes[f"{threads}x{vpt}"] = back_to_back_us(torch, launch, n_sets)
+    best = min(shapes, key=shapes.get)
+    del sets
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us_per_launch_by_shape": shapes, "best_shape": best,
+            "GBps": nbytes / shapes[best] / 1e3, "frac": nbytes / shapes[best] / 1e3 / PEAK_HBM_GBPS,
+            "fold_back_to_back_us": fold_us, "fold_time_over_ceiling_time": fold_us / shapes[best]}
+
+
 def device_memory_info():
     """Memory clock and bus width as the HIP runtime reports them, and the peak they imply."""
     hip = ctypes.CDLL("libamdhip64.so.7")
@@ -410,24 +461,34 @@ def cpu_threads_baseline(workloads, d, budget_s: float, threads: int):
 
 
 def cpu_baseline(workloads, d, budget_s: float):
-    """The fp64 oracle (single-threaded) over the whole prefill workload, repeated."""
+    """The fp64 oracle, single-threaded and pinned to one host core, over the whole prefill
+    workload, repeated for about `budget_s`; the rate of the median pass."""
     import oracle
 
     o = oracle.Oracle()
     parts = [workloads.bf16_bits(c) for c in d["partials"]]
     res = workloads.bf16_bits(d["residual"])
     w = d["weight"].numpy()
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        o.fold_norm(parts, res, w, d["eps"])
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": passes * d["T"] / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} passes of the full prefill boundary (2048 rows x 4096, P=8) "
-                      f"in {el:.1f} s, one thread, fp64", "cpu": cpu_model()}
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})  # the calling thread, which runs the oracle
+    try:
+        times = []
+        t0 = time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            o.fold_norm(parts, res, w, d["eps"])
+            times.append(time.perf_counter() - t1)
+            el = time.perf_counter() - t0
+            if el >= budget_s and len(times) >= 3:
+                break
+    finally:
+        os.sched_setaffinity(0, allowed)
+    med = sorted(times)[len(times) // 2]
+    return {"value": d["T"] / med, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} passes of the full prefill boundary (2048 rows x 4096, P=8) "
+                      f"in {el:.1f} s, one thread pinned to core {core}, fp64; rate of the "
+                      f"median pass", "cpu": cpu_model()}
 
 
 def main():
@@ -497,11 +558,14 @@ def main():
                      "kernel_p10_us": t["kernel_p10_s"] * 1e6,
                      "kernel_p90_us": t["kernel_p90_s"] * 1e6},
     }
+    fold_us = None if args.no_secondary else back_to_back_us(torch, lambda i: step(i, None, None), n_sets)
     del keep, step
     torch.cuda.empty_cache()
 
     if not args.no_secondary:
         sec = {}
+        log("9:2 streaming ceiling (the fold's loads and stores without arithmetic)")
+        sec["stream_ceiling_9r2w_T2048_H4096"] = stream_ceiling(torch, d["T"], d["H"], fold_us)
         log("quantised read (T=2048 H=7168 P=8, fp8 out)")
         dq = workloads.quantised()
         n_q = max(2, -(-ROTATE_BYTES // ((dq["P"] + 2) * dq["T"] * dq["H"] * 2 + dq["T"] * dq["H"])))

@@ -1,0 +1,93 @@
+// ceiling.hip -- measurement support, not part of the boundary path.
+//
+// A kernel with the prefill fold's memory access mix and none of its arithmetic: for every
+// 16-byte vector of a row it reads nine rows (eight partials and the residual) and writes two
+// (the residual and the normalised output), one row per workgroup, through the same per-row
+// buffer resources and cache policy (non-temporal loads, sc1 stores) as the fold. The loaded
+// vectors are combined with XOR so that every load is consumed and every store depends on all
+// nine. Its rate on a device is what that memory system delivers for this 9:2 read:write stream
+// in this layout; the fold is compared with it as context. Built into its own library
+// (libboundary_ceiling.so); the boundary library does not contain it.
+#include "kernels.h"
+
+namespace {
+
+constexpr int kSources = 9;
+
+struct MixArgs {
+  const uint16_t* src[kSources];
+  uint16_t* out0;
+  uint16_t* out1;
+  int64_t ld;      // elements between rows, same for every operand
+  int row_bytes;   // bytes of a row that are read and written
+};
+
+template <int VPT>
+__global__ __launch_bounds__(bnd::kMaxThreads) void mix_kernel(const MixArgs a) {
+  const int64_t row = blockIdx.x;
+  const int nthr = blockDim.x;
+  int off[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) off[v] = (threadIdx.x + v * nthr) * 16;
+  uint4 acc[VPT];
+  {
+    const bnd::Rsrc r = bnd::row_rsrc(a.src[0] + row * a.ld, a.row_bytes);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) acc[v] = bnd::load16(r, off[v]);
+  }
+#pragma unroll
+  for (int p = 1; p < kSources; ++p) {
+    const bnd::Rsrc r = bnd::row_rsrc(a.src[p] + row * a.ld, a.row_bytes);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const uint4 t = bnd::load16(r, off[v]);
+      acc[v].x ^= t.x; acc[v].y ^= t.y; acc[v].z ^= t.z; acc[v].w ^= t.w;
+    }
+  }
+  const bnd::Rsrc o0 = bnd::row_rsrc(a.out0 + row * a.ld, a.row_bytes);
+  const bnd::Rsrc o1 = bnd::row_rsrc(a.out1 + row * a.ld, a.row_bytes);
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    bnd::store16(o0, off[v], acc[v]);
+    bnd::store16(o1, off[v], acc[v]);
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+// Launches the 9:2 streaming kernel once on `stream`.
+//   src        nine device pointers to [rows, ld] bf16 row-major operands (read)
+//   out0/out1  two device pointers to [rows, ld] bf16 operands (written; may not alias src)
+//   rows       grid size, one workgroup per row, 1 .. 2^31-1
+//   row_elems  bf16 elements per row that are streamed, a multiple of 8, row_elems <= ld
+//   threads    workgroup size, a multiple of 64 in [64, 1024]; vpt in {1, 2, 4};
+//              threads * vpt * 8 must cover row_elems
+// Returns 0 on success, -1 on an invalid argument (nothing launched), or the hipError_t of the
+// launch.
+extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix_9r2w(
+    const void* const* src, void* out0, void* out1, int64_t rows, int64_t ld, int64_t row_elems,
+    int threads, int vpt, hipStream_t stream) {
+  if (!src || !out0 || !out1 || rows < 1 || rows > 0x7fffffff || row_elems < 8 || row_elems % 8 ||
+      ld < row_elems || ld % 8 || row_elems * 2 > 0x7fffffff)
+    return -1;
+  if (threads < 64 || threads > bnd::kMaxThreads || threads % 64 || (vpt != 1 && vpt != 2 && vpt != 4) ||
+      (int64_t)threads * vpt * 8 < row_elems)
+    return -1;
+  MixArgs a;
+  for (int p = 0; p < kSources; ++p) {
+    if (!src[p] || !aligned16(src[p])) return -1;
+    a.src[p] = static_cast<const uint16_t*>(src[p]);
+  }
+  if (!aligned16(out0) || !aligned16(out1)) return -1;
+  a.out0 = static_cast<uint16_t*>(out0);
+  a.out1 = static_cast<uint16_t*>(out1);
+  a.ld = ld;
+  a.row_bytes = (int)(row_elems * 2);
+  void* args[] = {&a};
+  const void* fn = vpt == 1   ? reinterpret_cast<const void*>(&mix_kernel<1>)
+                   : vpt == 2 ? reinterpret_cast<const void*>(&mix_kernel<2>)
+                              : reinterpret_cast<const void*>(&mix_kernel<4>);
+  return (int)hipLaunchKernel(fn, dim3((unsigned)rows), dim3((unsigned)threads), args, 0, stream);
+}

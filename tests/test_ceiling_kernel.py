@@ -1,0 +1,72 @@
+"""The benchmark's streaming-ceiling kernel (libboundary_ceiling.so).
+
+It is a context figure, not part of the boundary path; these tests only make sure it streams
+what it claims (every output element is the XOR of the nine inputs, nothing outside the rows'
+streamed elements is written) and that bad launch shapes are refused before any launch.
+"""
+import ctypes
+
+import pytest
+import torch
+
+from reduce_residual_rmsnorm_bnd_amd import _build
+
+VP = ctypes.c_void_p
+
+
+def _lib():
+    L = ctypes.CDLL(_build.CEILING_LIB_PATH)
+    L.bnd_ceiling_mix_9r2w.argtypes = [ctypes.POINTER(VP), VP, VP, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, VP]
+    L.bnd_ceiling_mix_9r2w.restype = ctypes.c_int
+    return L
+
+
+def test_ceiling_refuses_bad_shapes():
+    # fake, never dereferenced addresses: every call below fails validation before a launch
+    L = _lib()
+    a = 0x7F0000000000
+    src = (VP * 9)(*[a + (i << 24) for i in range(9)])
+    o0, o1 = VP(a + (20 << 24)), VP(a + (21 << 24))
+    bad = [
+        (src, o0, o1, 0, 4096, 4096, 256, 2),        # no rows
+        (src, o0, o1, 4, 4096, 4096, 32, 2),         # threads below a wavefront
+        (src, o0, o1, 4, 4096, 4096, 96 + 1, 2),     # threads not a multiple of 64
+        (src, o0, o1, 4, 4096, 4096, 2048, 1),       # threads above 1024
+        (src, o0, o1, 4, 4096, 4096, 256, 3),        # vectors per thread not 1, 2 or 4
+        (src, o0, o1, 4, 4096, 4096, 128, 2),        # 128 x 2 x 8 < 4096: cannot cover the row
+        (src, o0, o1, 4, 4096, 4100, 512, 1),        # row elements not a multiple of 8
+        (src, o0, o1, 4, 4092, 4096, 512, 1),        # ld shorter than the row
+        (src, o0, o1, 4, 4100, 4096, 512, 1),        # ld not a multiple of 8
+        (src, VP(a + 8), o1, 4, 4096, 4096, 512, 1),  # misaligned output
+        (src, None, o1, 4, 4096, 4096, 512, 1),      # null output
+        (None, o0, o1, 4, 4096, 4096, 512, 1),       # null source table
+    ]
+    for args in bad:
+        assert L.bnd_ceiling_mix_9r2w(*args, None) == -1, args
+    src[4] = a + 2  # a misaligned source
+    assert L.bnd_ceiling_mix_9r2w(src, o0, o1, 4, 4096, 4096, 512, 1, None) == -1
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,H,ld,threads,vpt", [(37, 4096, 4096, 256, 2), (5, 1000, 1016, 64, 2),
+                                                   (3, 8, 8, 64, 1), (9, 4096, 4104, 128, 4)])
+def test_ceiling_streams_the_xor(rows, H, ld, threads, vpt):
+    L = _lib()
+    g = torch.Generator().manual_seed(rows * 7 + vpt)
+    host = [torch.randint(-32768, 32768, (rows, ld), dtype=torch.int16, generator=g) for _ in range(9)]
+    srcs = [h.to("cuda:0") for h in host]
+    out = [torch.full((rows, ld), 7, dtype=torch.int16, device="cuda:0") for _ in range(2)]
+    print(f"\n  ceiling rows={rows} H={H} ld={ld} {threads}x{vpt}", flush=True)
+    rc = L.bnd_ceiling_mix_9r2w((VP * 9)(*[s.data_ptr() for s in srcs]), out[0].data_ptr(),
+                                out[1].data_ptr(), rows, ld, H, threads, vpt,
+                                torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    expect = host[0].clone()
+    for h in host[1:]:
+        expect ^= h
+    for o in out:
+        o = o.cpu()
+        assert torch.equal(o[:, :H], expect[:, :H])
+        assert bool((o[:, H:] == 7).all())
