@@ -34,7 +34,7 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 1 << 30          # >= 4x the 256 MB Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["kernels.h", "launch.h", "k_partials.hip", "k_moe.hip", "k_read.hip",
-                  "k_complete.hip", "host.cpp"]
+                  "k_complete.hip", "k_wave.hip", "k_wave_fp8.hip", "k_wave_moe.hip", "host.cpp"]
 
 
 def log(msg: str) -> None:
@@ -99,9 +99,19 @@ class Timed:
     timed region records start/stop events from its own dispatch
     (bnd_time_next_launch -> hipExtLaunchKernel) on the stream it runs on; the
     event packets add a few microseconds of queue gap, so sampling keeps the
-    wall-clock rate of the timed region close to an unobserved run."""
+    wall-clock rate of the timed region close to an unobserved run.
 
-    def __init__(self, torch, bnd, sample_every: int = 8):
+    Two per-launch figures come from those events, each reading high in one
+    regime. A sampled launch's own start-to-stop time: its start is taken while
+    the previous kernel's last waves still drain, so it reads high when the
+    stream runs back to back. The interval from one sampled launch's start to
+    the next one's spans exactly `sample_every` launches and carries that
+    offset at both ends; divided by `sample_every` it is the time per launch of
+    the running stream, which reads high when the host's issue rate or queue
+    gaps, not the kernel, set the pace (short kernels). The kernel time is the
+    smaller of the two means."""
+
+    def __init__(self, torch, bnd, sample_every: int = 32):
         self.torch = torch
         self.L = bnd.lib()
         self.sample_every = sample_every
@@ -111,6 +121,8 @@ class Timed:
         for i in range(warmup):
             step(i % n_sets, None, None)
         sampled = list(range(0, steps, self.sample_every))
+        if len(sampled) < 2:
+            raise ValueError(f"{steps} steps give fewer than two sampled launches")
         ev = HipEvents(2 * len(sampled))
         slot = {i: n for n, i in enumerate(sampled)}
         torch.cuda.synchronize()
@@ -124,15 +136,26 @@ class Timed:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         durs = sorted(ev.elapsed_s(2 * n, 2 * n + 1) for n in range(len(sampled)))
+        gaps = [ev.elapsed_s(2 * n, 2 * n + 2) / self.sample_every for n in range(len(sampled) - 1)]
         ev.close()
+        dispatch = sum(durs) / len(durs)
+        interval = sum(gaps) / len(gaps)
         return {
             "wall_s": wall,
-            "samples": len(durs),
-            "kernel_mean_s": sum(durs) / len(durs),
-            "kernel_median_s": durs[len(durs) // 2],
-            "kernel_p10_s": durs[len(durs) // 10],
-            "kernel_p90_s": durs[(9 * len(durs)) // 10],
+            "kernel_s": min(dispatch, interval),
+            "dispatch_event_mean_s": dispatch,
+            "dispatch_event_median_s": durs[len(durs) // 2],
+            "dispatch_events": len(durs),
+            "interval_mean_s": interval,
+            "intervals": len(gaps),
+            "launches_per_interval": self.sample_every,
         }
+
+
+def kernel_fields(t) -> dict:
+    return {"kernel_us": t["kernel_s"] * 1e6,
+            "dispatch_event_mean_us": t["dispatch_event_mean_s"] * 1e6,
+            "interval_us_per_launch": t["interval_mean_s"] * 1e6}
 
 
 def fold_case(torch, bnd, d, n_sets, fp8=False, row_begin=0, rows=None):
@@ -370,7 +393,7 @@ def back_to_back_us(torch, launch, n_sets: int, reps: int = 300, warmup: int = 2
 
 def stream_ceiling(torch, T: int, H: int, fold_us: float):
     """The 9:2 streaming kernel (libboundary_ceiling.so: the fold's rows, loads and stores, no
-    arithmetic) over rotating sets of the prefill shape, for three launch shapes; compared with
+    arithmetic) over rotating sets of the prefill shape, for four launch shapes; compared with
     the fold timed the same way (back-to-back launches) in the same process."""
     from reduce_residual_rmsnorm_bnd_amd import _build
 
@@ -387,7 +410,7 @@ def stream_ceiling(torch, T: int, H: int, fold_us: float):
                      vp(bufs[10].data_ptr())))
     stream = vp(torch.cuda.current_stream().cuda_stream)
     shapes = {}
-    for threads, vpt in ((256, 2), (512, 1), (128, 4)):
+    for threads, vpt in ((256, 2), (512, 1), (128, 4), (64, 8)):
         def launch(i, threads=threads, vpt=vpt):
             _, src, o0, o1 = sets[i]
             rc = L.bnd_ceiling_mix_9r2w(src, o0, o1, T, H, H, threads, vpt, stream)
@@ -494,7 +517,7 @@ def cpu_baseline(workloads, d, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true", help="only the prefill step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -528,7 +551,7 @@ def main():
     step, nbytes, keep = fold_case(torch, bnd, d, n_sets)
     log(f"timing {args.steps} steps over {n_sets} rotating sets")
     t = timer.run(step, n_sets, args.warmup, args.steps)
-    achieved = nbytes / t["kernel_mean_s"] / 1e9
+    achieved = nbytes / t["kernel_s"] / 1e9
     traffic = traffic_from_profiles("prefill T=2048 H=4096 P=8")
     result = {
         "metric": METRIC,
@@ -549,14 +572,20 @@ def main():
                    "device_memory": device_memory_info()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "read_kernel<Partials, P=8, bf16 out> (bnd_fold_norm)",
+                     "kernel": "bnd_fold_norm's kernel (one wavefront per row at 2048 rows x 4096 on "
+                               "256 CUs: wave_read_kernel<Partials, P=8, bf16>)",
                      "algorithmic_bytes": nbytes,
-                     "kernel_mean_us": t["kernel_mean_s"] * 1e6,
-                     "timed_launches": t["samples"],
-                     "steady_state_us_per_launch": t["wall_s"] / args.steps * 1e6,
-                     "kernel_median_us": t["kernel_median_s"] * 1e6,
-                     "kernel_p10_us": t["kernel_p10_s"] * 1e6,
-                     "kernel_p90_us": t["kernel_p90_s"] * 1e6},
+                     "kernel_mean_us": t["kernel_s"] * 1e6,
+                     "kernel_timing": "the smaller of two HIP-event means over the timed region: "
+                                      "sampled launches' own start-to-stop, and start-to-start "
+                                      "intervals between sampled launches / launches spanned",
+                     "dispatch_event_mean_us": t["dispatch_event_mean_s"] * 1e6,
+                     "dispatch_event_median_us": t["dispatch_event_median_s"] * 1e6,
+                     "dispatch_events": t["dispatch_events"],
+                     "interval_us_per_launch": t["interval_mean_s"] * 1e6,
+                     "intervals": t["intervals"],
+                     "launches_per_interval": t["launches_per_interval"],
+                     "steady_state_us_per_launch": t["wall_s"] / args.steps * 1e6},
     }
     fold_us = None if args.no_secondary else back_to_back_us(torch, lambda i: step(i, None, None), n_sets)
     del keep, step
@@ -570,11 +599,10 @@ def main():
         dq = workloads.quantised()
         n_q = max(2, -(-ROTATE_BYTES // ((dq["P"] + 2) * dq["T"] * dq["H"] * 2 + dq["T"] * dq["H"])))
         step, nb, keep = fold_case(torch, bnd, dq, n_q, fp8=True)
-        tq = timer.run(step, n_q, 20, 100)
-        sec["fp8_T2048_H7168_P8"] = {"tokens_per_s_kernel": 2048 / tq["kernel_mean_s"],
-                                     "kernel_mean_us": tq["kernel_mean_s"] * 1e6,
-                                     "GBps": nb / tq["kernel_mean_s"] / 1e9,
-                                     "frac": nb / tq["kernel_mean_s"] / 1e9 / PEAK_HBM_GBPS,
+        tq = timer.run(step, n_q, 20, 256)
+        sec["fp8_T2048_H7168_P8"] = {"tokens_per_s_kernel": 2048 / tq["kernel_s"], **kernel_fields(tq),
+                                     "GBps": nb / tq["kernel_s"] / 1e9,
+                                     "frac": nb / tq["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                                      "algorithmic_bytes": nb}
         del keep, step, dq
         torch.cuda.empty_cache()
@@ -585,11 +613,10 @@ def main():
                                    ("moe_slice_rows768_1023", *workloads.MOE_SLICE, False),
                                    ("moe_terminal_gemma_T2048_H4096_k8", 0, 2048, True)):
             step, nb, keep = moe_case(torch, bnd, dm, n_m, rb, rows, terminal_gemma=tg)
-            tm = timer.run(step, n_m, 20, 100)
-            sec[name] = {"tokens_per_s_kernel": rows / tm["kernel_mean_s"],
-                         "kernel_mean_us": tm["kernel_mean_s"] * 1e6,
-                         "GBps": nb / tm["kernel_mean_s"] / 1e9,
-                         "frac": nb / tm["kernel_mean_s"] / 1e9 / PEAK_HBM_GBPS,
+            tm = timer.run(step, n_m, 20, 256)
+            sec[name] = {"tokens_per_s_kernel": rows / tm["kernel_s"], **kernel_fields(tm),
+                         "GBps": nb / tm["kernel_s"] / 1e9,
+                         "frac": nb / tm["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                          "algorithmic_bytes": nb}
             del keep, step
         del dm
@@ -597,21 +624,21 @@ def main():
         log("snapshot and add_to_output (prefill sizes), the largest RSv share of 2047 rows")
         for kind in ("snapshot", "add_to_output"):
             step, nb, keep = aux_case(torch, bnd, d, n_sets, kind)
-            ta = timer.run(step, n_sets, 20, 100)
-            sec[f"{kind}_T2048_H4096_P8"] = {"kernel_mean_us": ta["kernel_mean_s"] * 1e6,
-                                             "GBps": nb / ta["kernel_mean_s"] / 1e9,
-                                             "frac": nb / ta["kernel_mean_s"] / 1e9 / PEAK_HBM_GBPS,
+            ta = timer.run(step, n_sets, 20, 256)
+            sec[f"{kind}_T2048_H4096_P8"] = {**kernel_fields(ta),
+                                             "GBps": nb / ta["kernel_s"] / 1e9,
+                                             "frac": nb / ta["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                                              "algorithmic_bytes": nb}
             del keep, step
         counts = [300, 0, 511, 256, 257, 1, 400, 322]
         rb, rows, Tr = bnd.bnd_rsv_share(counts, 2)
         dr = workloads.fold_inputs(6, Tr, 4096, 8)
         step, nb, keep = fold_case(torch, bnd, dr, n_sets, row_begin=rb, rows=rows)
-        tr = timer.run(step, n_sets, 20, 100)
+        tr = timer.run(step, n_sets, 20, 256)
         sec["rsv_share_511_of_2047_H4096_P8"] = {"row_begin": rb, "rows": rows,
-                                                  "kernel_mean_us": tr["kernel_mean_s"] * 1e6,
-                                                  "GBps": nb / tr["kernel_mean_s"] / 1e9,
-                                                  "frac": nb / tr["kernel_mean_s"] / 1e9 / PEAK_HBM_GBPS,
+                                                  **kernel_fields(tr),
+                                                  "GBps": nb / tr["kernel_s"] / 1e9,
+                                                  "frac": nb / tr["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                                                   "algorithmic_bytes": nb}
         del keep, step, dr
         torch.cuda.empty_cache()

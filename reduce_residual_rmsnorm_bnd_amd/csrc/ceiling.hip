@@ -62,7 +62,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 //   out0/out1  two device pointers to [rows, ld] bf16 operands (written; may not alias src)
 //   rows       grid size, one workgroup per row, 1 .. 2^31-1
 //   row_elems  bf16 elements per row that are streamed, a multiple of 8, row_elems <= ld
-//   threads    workgroup size, a multiple of 64 in [64, 1024]; vpt in {1, 2, 4};
+//   threads    workgroup size, a multiple of 64 in [64, 1024]; vpt in {1, 2, 4, 8};
 //              threads * vpt * 8 must cover row_elems
 // Returns 0 on success, -1 on an invalid argument (nothing launched), or the hipError_t of the
 // launch.
@@ -72,7 +72,7 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix_9r2w(
   if (!src || !out0 || !out1 || rows < 1 || rows > 0x7fffffff || row_elems < 8 || row_elems % 8 ||
       ld < row_elems || ld % 8 || row_elems * 2 > 0x7fffffff)
     return -1;
-  if (threads < 64 || threads > bnd::kMaxThreads || threads % 64 || (vpt != 1 && vpt != 2 && vpt != 4) ||
+  if (threads < 64 || threads > bnd::kMaxThreads || threads % 64 || (vpt != 1 && vpt != 2 && vpt != 4 && vpt != 8) ||
       (int64_t)threads * vpt * 8 < row_elems)
     return -1;
   MixArgs a;
@@ -88,6 +88,7 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix_9r2w(
   void* args[] = {&a};
   const void* fn = vpt == 1   ? reinterpret_cast<const void*>(&mix_kernel<1>)
                    : vpt == 2 ? reinterpret_cast<const void*>(&mix_kernel<2>)
-                              : reinterpret_cast<const void*>(&mix_kernel<4>);
+                   : vpt == 4 ? reinterpret_cast<const void*>(&mix_kernel<4>)
+                              : reinterpret_cast<const void*>(&mix_kernel<8>);
   return (int)hipLaunchKernel(fn, dim3((unsigned)rows), dim3((unsigned)threads), args, 0, stream);
 }

@@ -408,6 +408,178 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// The boundary read with one wavefront per row (64 lanes x 8 vectors: rows of
+// up to 4096 elements), for folds of partials or MoE picks.
+//
+// Used when the launch's rows just fit on the chip in one round at two waves
+// per SIMD (the 2048-row prefill boundary on 256 CUs). Three things make it
+// faster there than the multi-wave rows above, all measured on MI355X:
+//  - loads go source by source (every vector of source 0, then of source 1,
+//    ..., the residual last), so a wave streams one contiguous row of one
+//    operand at a time; vector-major order is up to 25% slower;
+//  - two loads are kept in flight per wave through a two-register ring with
+//    scheduling fences (one in flight is latency-bound, more is slower);
+//  - the norm weight is fetched right after the first source loads and kept
+//    in registers (64 VGPRs; the kernel fits 256), so after the row's sum of
+//    squares nothing waits on memory: loading the weight after the reduction
+//    leaves HBM idle at the tail of the single round and costs 7%.
+// The reduction is a wavefront DPP sum with no LDS and no barrier. The sum of
+// the sources runs in the same order per element as in load_and_fold, so the
+// residual is bitwise the same as with the other launch shapes.
+// ---------------------------------------------------------------------------
+constexpr int kWaveDepth = 2;
+
+// The row's sources, resolved before the first load: N partial rows, or N
+// expert rows with their gates (an invalid pick gets an empty resource, so its
+// loads read 0), then the residual as source N (empty when there is none).
+template <Source S, int N>
+struct RowSources {
+  Rsrc r[N + 1];
+  float g[S == Source::Moe ? N : 1];
+  __device__ __forceinline__ RowSources(const RowArgs& a, int64_t row) {
+    const int rb = a.H * 2;
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      if constexpr (S == Source::Partials) {
+        r[p] = row_rsrc(a.src[p] + row * a.ld_src, rb);
+      } else {
+        const int64_t e = a.idx[row * N + p];
+        const bool valid = e >= 0 && e < a.n_expert_rows;
+        r[p] = row_rsrc(a.experts + (valid ? e : 0) * a.ld_e, valid ? rb : 0);
+        g[p] = a.gate[row * N + p];
+      }
+    }
+    r[N] = row_rsrc(a.res + row * a.ld_res, a.has_residual ? rb : 0);
+  }
+};
+
+// Load I of the row (I = source * kWaveVpt + vector) and the pipeline that
+// consumes load I while load I + kWaveDepth is in flight.
+template <Source S, int N>
+struct WaveFold {
+  static constexpr int kLoads = (N + 1) * kWaveVpt;
+  template <int I>
+  __device__ static __forceinline__ uint4 load(const RowSources<S, N>& src, int lane) {
+    return load16(src.r[I / kWaveVpt], (lane + (I % kWaveVpt) * kWave) * 16);
+  }
+  template <int I>
+  __device__ static __forceinline__ void prologue(const RowSources<S, N>& src, int lane,
+                                                  uint4 (&ring)[kWaveDepth]) {
+    if constexpr (I < kWaveDepth && I < kLoads) {
+      ring[I] = load<I>(src, lane);
+      prologue<I + 1>(src, lane, ring);
+    }
+  }
+  template <int I>
+  __device__ static __forceinline__ void steps(const RowSources<S, N>& src, int lane, uint4 (&ring)[kWaveDepth],
+                                               float (&x)[kWaveVpt][8]) {
+    if constexpr (I < kLoads) {
+      constexpr int p = I / kWaveVpt, v = I % kWaveVpt;
+      float t[8];
+      bf16x8_to_f32(ring[I % kWaveDepth], t);
+      if constexpr (I + kWaveDepth < kLoads) ring[I % kWaveDepth] = load<I + kWaveDepth>(src, lane);
+      if constexpr (p == N) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[v][e] = t[e] + x[v][e];  // residual + contribution
+      } else if constexpr (S == Source::Moe) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[v][e] = fmaf(src.g[p], t[e], p == 0 ? 0.0f : x[v][e]);
+      } else if constexpr (p == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[v][e] = t[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[v][e] += t[e];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      steps<I + 1>(src, lane, ring, x);
+    }
+  }
+};
+
+template <Source S, int N, bool FP8>
+__global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
+  static_assert(S == Source::Partials || S == Source::Moe, "one-wave rows fold partials or MoE picks");
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  bool ok[kWaveVpt];
+#pragma unroll
+  for (int v = 0; v < kWaveVpt; ++v) ok[v] = (lane + v * kWave) < a.nvec;
+
+  const RowSources<S, N> src(a, row);
+  uint4 ring[kWaveDepth];
+  WaveFold<S, N>::template prologue<0>(src, lane, ring);
+  // the weight (L2-resident, shared by all rows) behind the first source loads
+  const Rsrc wr = row_rsrc(a.w, a.H * 4);
+  u32x4 wlo[kWaveVpt], whi[kWaveVpt];
+#pragma unroll
+  for (int v = 0; v < kWaveVpt; ++v) {
+    wlo[v] = __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + v * kWave) * 32, 0, 0);
+    whi[v] = __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + v * kWave) * 32 + 16, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float x[kWaveVpt][8];
+  WaveFold<S, N>::template steps<0>(src, lane, ring, x);
+
+  const float offset = a.gemma ? 1.0f : 0.0f;
+  float w[kWaveVpt][8];
+#pragma unroll
+  for (int v = 0; v < kWaveVpt; ++v) {
+    w[v][0] = __uint_as_float(wlo[v].x) + offset; w[v][1] = __uint_as_float(wlo[v].y) + offset;
+    w[v][2] = __uint_as_float(wlo[v].z) + offset; w[v][3] = __uint_as_float(wlo[v].w) + offset;
+    w[v][4] = __uint_as_float(whi[v].x) + offset; w[v][5] = __uint_as_float(whi[v].y) + offset;
+    w[v][6] = __uint_as_float(whi[v].z) + offset; w[v][7] = __uint_as_float(whi[v].w) + offset;
+  }
+  float ss = 0.0f, mx = 0.0f;
+#pragma unroll
+  for (int v = 0; v < kWaveVpt; ++v)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[v][e], x[v][e], ss);
+  ss = wave_sum(ss);
+  if constexpr (FP8) {
+#pragma unroll
+    for (int v = 0; v < kWaveVpt; ++v)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[v][e] * w[v][e]));
+    mx = wave_max(mx);
+  }
+  const float inv = 1.0f / sqrtf(ss / (float)a.H + a.eps);
+
+  const int row_bytes = a.H * 2;
+  const Rsrc res = row_rsrc(a.res + row * a.ld_res, row_bytes);
+#pragma unroll
+  for (int v = 0; v < kWaveVpt; ++v)
+    if (ok[v]) store16(res, (lane + v * kWave) * 16, f32_to_bf16x8(x[v]));
+  if constexpr (!FP8) {
+    const Rsrc yr = row_rsrc(a.y + row * a.ld_y, row_bytes);
+#pragma unroll
+    for (int v = 0; v < kWaveVpt; ++v) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (x[v][e] * inv) * w[v][e];
+      if (ok[v]) store16(yr, (lane + v * kWave) * 16, f32_to_bf16x8(y));
+    }
+  } else {
+    // the same scale and codes as read_kernel: max|y| = max|x w| inv exactly
+    const float amax = mx * inv;
+    const float scale = amax / 448.0f;
+    const Rsrc qr = row_rsrc(a.q + row * a.ld_q, a.H);
+#pragma unroll
+    for (int v = 0; v < kWaveVpt; ++v) {
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = (x[v][e] * w[v][e]) * inv;
+        const float u = scale > 0.0f ? y / scale : 0.0f;
+        t[e] = fminf(fmaxf(u, -448.0f), 448.0f);
+      }
+      if (ok[v]) store8(qr, (lane + v * kWave) * 8, f32_to_e4m3x8(t));
+    }
+    if (lane == 0) a.scale[row] = scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch tables
 // ---------------------------------------------------------------------------
 using KernelFn = void (*)(RowArgs);
@@ -420,6 +592,11 @@ constexpr std::array<KernelFn, sizeof...(I)> read_table(std::integer_sequence<in
 template <Source S, int VPT, bool kFold, int... I>
 constexpr std::array<KernelFn, sizeof...(I)> complete_table(std::integer_sequence<int, I...>) {
   return {{&complete_kernel<S, I + 1, VPT, kFold>...}};
+}
+
+template <Source S, bool FP8, int... I>
+constexpr std::array<KernelFn, sizeof...(I)> wave_table(std::integer_sequence<int, I...>) {
+  return {{&wave_read_kernel<S, I + 1, FP8>...}};
 }
 
 inline hipError_t launch_kernel(KernelFn fn, const RowArgs& a, const Launch& l, hipStream_t stream) {

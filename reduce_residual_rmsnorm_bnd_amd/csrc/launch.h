@@ -10,6 +10,7 @@ namespace bnd {
 constexpr int kMaxSources = 16;
 constexpr int kMaxThreads = 1024;
 constexpr int kWave = 64;
+constexpr int kWaveVpt = 8;  // vectors per lane of the one-wavefront-per-row read (H <= 4096)
 
 // Arguments of one boundary launch. Every row pointer is already offset to
 // the first row the launch processes, so a kernel addresses row i of each
@@ -45,7 +46,7 @@ struct RowArgs {
 struct Launch {
   int rows;     // grid size
   int threads;  // workgroup size, multiple of 64
-  int vpt;      // 16-byte vectors per thread: 1, 2 or 4
+  int vpt;      // 16-byte vectors per thread: 1, 2 or 4; 8 = one wavefront per row (threads = 64)
   hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
   hipEvent_t stop = nullptr;
 };

@@ -333,7 +333,8 @@ def test_rsv_share():
 
 def test_options_validation():
     for opt, bad in ((B.BND_OPT_FUSED_UNAVAILABLE, 2), (B.BND_OPT_THREADS_PER_ROW, 100),
-                     (B.BND_OPT_THREADS_PER_ROW, 2048), (B.BND_OPT_VECTORS_PER_THREAD, 3)):
+                     (B.BND_OPT_THREADS_PER_ROW, 2048), (B.BND_OPT_VECTORS_PER_THREAD, 3),
+                     (B.BND_OPT_VECTORS_PER_THREAD, 16)):
         assert L.bnd_set_option(opt, bad) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(99, 0) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(B.BND_OPT_THREADS_PER_ROW, 256) == 0
@@ -346,6 +347,30 @@ def test_launch_shape_that_cannot_cover_the_row_is_refused():
     h, o = _pending()
     st = L.bnd_fold_norm(h, o, fake(1 << 31), 1e-6, fake(1 << 30), H, None)
     assert st == B.BND_ERR_NO_PATH, L.bnd_last_error()
+    _unchanged(h)
+
+
+def test_one_wave_rows_only_where_a_kernel_exists():
+    # eight vectors per thread: one wavefront per row, for folds with H <= 4096 and 64 threads
+    assert L.bnd_set_option(B.BND_OPT_VECTORS_PER_THREAD, 8) == 0
+    assert L.bnd_get_option(B.BND_OPT_VECTORS_PER_THREAD) == 8
+    h = create(T=8, rows=8)
+    st = L.bnd_enter_norm(h, fake(1 << 28), H, fake(1 << 31), 1e-6, fake(1 << 30), H, None)
+    assert st == B.BND_ERR_NO_PATH and b"wavefront" in L.bnd_last_error()
+    assert L.bnd_stream_state(h) == B.BND_INITIAL
+    wide = 4104
+    h = create(T=8, rows=4, ld=wide, Hh=wide)
+    assert L.bnd_written(h, fake(), wide) == 0
+    o = owed_out()
+    arr = (VP * 2)(*[fake((p + 1) << 24) for p in range(2)])
+    assert L.bnd_publish_partials(h, arr, 2, wide, ctypes.byref(o)) == 0
+    st = L.bnd_fold_norm(h, o.value, fake(1 << 31), 1e-6, fake(1 << 30), wide, None)
+    assert st == B.BND_ERR_NO_PATH and b"H <=" in L.bnd_last_error()
+    _unchanged(h)
+    assert L.bnd_set_option(B.BND_OPT_THREADS_PER_ROW, 128) == 0
+    h, o = _pending()
+    st = L.bnd_fold_norm(h, o, fake(1 << 31), 1e-6, fake(1 << 30), H, None)
+    assert st == B.BND_ERR_NO_PATH and b"64 threads" in L.bnd_last_error()
     _unchanged(h)
 
 

@@ -33,7 +33,8 @@ def test_ceiling_refuses_bad_shapes():
         (src, o0, o1, 4, 4096, 4096, 32, 2),         # threads below a wavefront
         (src, o0, o1, 4, 4096, 4096, 96 + 1, 2),     # threads not a multiple of 64
         (src, o0, o1, 4, 4096, 4096, 2048, 1),       # threads above 1024
-        (src, o0, o1, 4, 4096, 4096, 256, 3),        # vectors per thread not 1, 2 or 4
+        (src, o0, o1, 4, 4096, 4096, 256, 3),        # vectors per thread not 1, 2, 4 or 8
+        (src, o0, o1, 4, 4096, 4096, 64, 16),
         (src, o0, o1, 4, 4096, 4096, 128, 2),        # 128 x 2 x 8 < 4096: cannot cover the row
         (src, o0, o1, 4, 4096, 4100, 512, 1),        # row elements not a multiple of 8
         (src, o0, o1, 4, 4092, 4096, 512, 1),        # ld shorter than the row
@@ -50,7 +51,8 @@ def test_ceiling_refuses_bad_shapes():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("rows,H,ld,threads,vpt", [(37, 4096, 4096, 256, 2), (5, 1000, 1016, 64, 2),
-                                                   (3, 8, 8, 64, 1), (9, 4096, 4104, 128, 4)])
+                                                   (3, 8, 8, 64, 1), (9, 4096, 4104, 128, 4),
+                                                   (11, 3600, 3600, 64, 8)])
 def test_ceiling_streams_the_xor(rows, H, ld, threads, vpt):
     L = _lib()
     g = torch.Generator().manual_seed(rows * 7 + vpt)

@@ -734,3 +734,99 @@ def test_snapshot_leaves_the_owed_work(orc):
     with pytest.raises(bnd.BoundaryError) as e:
         bnd.bnd_snapshot(s2, o2, Guarded(8, 1024).view)
     assert e.value.status == bnd.BND_ERR_WRONG_KIND and s2.state == bnd.BND_PENDING
+
+
+# ------------------------------------------------------------------ one wavefront per row
+
+WAVE = (64, 8)  # threads per row, vectors per thread: the one-wavefront read
+
+WAVE_SHAPES = [  # T, H, P, pad, row_begin, rows
+    (300, 4096, 8, 0, 0, None),
+    (77, 3600, 3, 8, 0, None),     # 450 vectors: the last lanes of the last vector idle
+    (5, 264, 16, 0, 0, None),      # 33 vectors: most lanes idle, sixteen sources
+    (3, 8, 1, 0, 0, None),         # one vector
+    (40, 4096, 2, 16, 7, 20),      # a slice of rows
+]
+
+
+@pytest.mark.parametrize("T,H,P,pad,rb,rows", WAVE_SHAPES)
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_wave_rows(orc, T, H, P, pad, rb, rows, fp8):
+    d = workloads.fold_inputs(300 + T + H + P, T, H, P)
+    with forced_shape(*WAVE):
+        assert_fold_matches(orc, d, f"one wave per row T={T} H={H} P={P} slice={rb}+{rows}", fp8=fp8,
+                            pad=pad, row_begin=rb, rows=rows)
+
+
+def test_wave_rows_edge_cases(orc):
+    d = workloads.fold_inputs(31, 12, 4096, 3)
+    with forced_shape(*WAVE):
+        assert_fold_matches(orc, d, "one wave per row, no residual", with_residual=False)
+        assert_fold_matches(orc, d, "one wave per row, Gemma weight", gemma=True)
+        assert_fold_matches(orc, d, "one wave per row, Gemma weight fp8", gemma=True, fp8=True)
+
+
+def test_wave_rows_residual_matches_other_shapes(orc):
+    """The residual is elementwise: bitwise the same for every launch shape; y agrees with the
+    oracle under each."""
+    d = workloads.fold_inputs(32, 64, 4096, 8)
+    with forced_shape(*WAVE):
+        a = run_fold(d)
+    with forced_shape(256, 2):
+        b = run_fold(d)
+    assert torch.equal(a["res"].view, b["res"].view)
+    diff = (bits(a["y"].view).astype(np.int32) - bits(b["y"].view).astype(np.int32))
+    assert np.abs(diff).max() <= 1, "y of two launch shapes more than one bf16 step apart"
+
+
+def test_wave_rows_moe(orc):
+    d = workloads.moe_inputs(33, 100, 4096, 16, 8)
+    idx = d["idx"].clone()
+    idx[9] = -1
+    idx[30] = d["expert_rows"].shape[0]  # out of range: contributes nothing
+    d["idx"] = idx
+    with forced_shape(*WAVE):
+        run_moe(orc, d, 0, 100, "one wave per row, MoE k=8 with out-of-range picks")
+        run_moe(orc, d, 40, 33, "one wave per row, MoE slice", gemma=True)
+    d16 = workloads.moe_inputs(34, 9, 3600, 16, 16)
+    with forced_shape(*WAVE):
+        run_moe(orc, d16, 0, 9, "one wave per row, MoE k=16 H=3600")
+
+
+def test_wave_rows_moe_over_stacked_partials_is_fold(orc):
+    d = workloads.fold_inputs(35, 24, 4096, 4)
+    T, H, P = 24, 4096, 4
+    with forced_shape(*WAVE):
+        a = run_fold(d)
+        E = torch.cat([c for c in d["partials"]], 0).to(DEV)
+        idx = torch.tensor([[p * T + t for p in range(P)] for t in range(T)], dtype=torch.int32,
+                           device=DEV).reshape(-1)
+        gate = torch.ones(T * P, dtype=torch.float32, device=DEV)
+        res = Guarded(T, H).from_host(d["residual"])
+        y = Guarded(T, H)
+        s = bnd.bnd_stream_create(T, H, res.view)
+        bnd.bnd_written(s, res.view)
+        owed = bnd.bnd_publish_moe(s, E, idx, gate, P)
+        bnd.bnd_moe_finalize_fold_norm(s, owed, d["weight"].to(DEV), d["eps"], y.view)
+        torch.cuda.synchronize()
+    assert torch.equal(y.view, a["y"].view) and torch.equal(res.view, a["res"].view)
+
+
+def test_wave_rows_refused_where_no_kernel(orc):
+    """Eight vectors per thread exists only for folds with H <= 4096: other calls refuse it
+    before launching anything."""
+    d = workloads.fold_inputs(36, 4, 4104, 2)
+    with forced_shape(*WAVE):
+        with pytest.raises(bnd.BoundaryError) as e:
+            run_fold(d)
+        assert e.value.status == bnd.BND_ERR_NO_PATH
+        res = Guarded(4, 4096)
+        y = Guarded(4, 4096)
+        s = bnd.bnd_stream_create(4, 4096, res.view)
+        with pytest.raises(bnd.BoundaryError) as e:
+            bnd.bnd_enter_norm(s, torch.zeros(4, 4096, dtype=torch.bfloat16, device=DEV),
+                               torch.ones(4096, device=DEV), 1e-6, y.view)
+        assert e.value.status == bnd.BND_ERR_NO_PATH
+    torch.cuda.synchronize()
+    res.check_guards("refused enter residual")
+    y.check_guards("refused enter y")

@@ -82,13 +82,22 @@ assert L.bnd_complete_only(h, o.value, fake(14 << 30), H, ctypes.byref(o2), None
 assert L.bnd_fold_norm(h, o2.value, w, 1e-6, y, H, None) == 0
 far = lambda k: fake(k << 36)  # 64 GiB apart: no region overlaps another
 parts2 = (VP * 8)(*[far(4 + p) for p in range(8)])
-for H2 in (8, 264, 7168, 16384, 32768):  # every launch-shape branch
-    for rows2 in (1, 300, 4096):
+for H2 in (8, 264, 4096, 7168, 16384, 32768):  # every launch-shape branch
+    for rows2 in (1, 300, 2048, 4096):  # 2048 x 4096: one wavefront per row
         h2 = VP()
         assert L.bnd_stream_create(ctypes.byref(h2), 4096, H2, 0, rows2, far(0), H2) == 0
         assert L.bnd_publish_partials(h2, parts2, 8, H2, ctypes.byref(o)) == 0
         assert L.bnd_fold_norm(h2, o.value, far(1), 1e-6, far(2), H2, None) == 0, (H2, L.bnd_last_error())
         L.bnd_stream_destroy(h2)
+h3 = VP()  # the one-wavefront rows forced, for a MoE finalize and an fp8 fold
+assert L.bnd_set_option(3, 8) == 0
+assert L.bnd_stream_create(ctypes.byref(h3), 4096, 4096, 0, 100, far(0), 4096) == 0
+assert L.bnd_publish_moe(h3, far(10), 512, 4096, far(11), far(12), 8, ctypes.byref(o)) == 0
+assert L.bnd_moe_finalize_fold_norm(h3, o.value, far(1), 1e-6, far(2), 4096, None) == 0, L.bnd_last_error()
+assert L.bnd_publish_partials(h3, parts2, 8, 4096, ctypes.byref(o)) == 0
+assert L.bnd_fold_norm_quant_fp8(h3, o.value, far(1), 1e-6, far(2), 4096, far(3), None) == 0, L.bnd_last_error()
+assert L.bnd_stream_destroy(h3) == 0
+reset()
 assert L.bnd_take_output(h) == 0 and L.bnd_stream_destroy(h) == 0
 print(f"ran {{n}} host checks and the legal-path walk clean")
 """

@@ -6,7 +6,9 @@ occupancy, so the fold and read kernels with one or two vectors per thread and u
 partial sources must stay within 64 VGPRs and never use scratch. A data-dependent branch around
 the Gemma weight offset once pushed the P = 8 fold to 100 VGPRs (half the resident rows, about
 a microsecond on the prefill boundary); this test fails on such a change before it reaches a
-benchmark.
+benchmark. The one-wavefront-per-row read (eight vectors per lane) is chosen only while a
+launch's rows fit on the chip at 8 rows per CU, so it must keep two waves per SIMD (at most
+256 VGPRs), also without scratch.
 """
 import os
 import re
@@ -24,6 +26,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, 
          "-Rpass-analysis=kernel-resource-usage"]
 
 NAME = re.compile(r"Function Name: _ZN3bnd11read_kernelILNS_6SourceE(\d)ELi(\d+)ELi(\d)ELb([01])E")
+WAVE_NAME = re.compile(r"Function Name: _ZN3bnd16wave_read_kernelILNS_6SourceE(\d)ELi(\d+)ELb([01])E")
 FIELD = re.compile(r"remark: +(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)")
 SOURCES = {0: "Partials", 1: "Moe", 2: "Input", 3: "Residual"}
 
@@ -42,6 +45,11 @@ def _resources(tmp_path, files):
                 current = (SOURCES[int(m.group(1))], int(m.group(2)), int(m.group(3)), m.group(4) == "1")
                 table[current] = {}
                 continue
+            m = WAVE_NAME.search(line)
+            if m:  # one wavefront per row: eight vectors per lane
+                current = ("Wave" + SOURCES[int(m.group(1))], int(m.group(2)), 8, m.group(3) == "1")
+                table[current] = {}
+                continue
             m = FIELD.search(line)
             if m and current is not None and m.group(1) not in table[current]:
                 table[current][m.group(1)] = int(m.group(2))
@@ -52,23 +60,34 @@ def _resources(tmp_path, files):
 def resources(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not installed")
-    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip"])
+    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip", "k_wave.hip",
+                                                       "k_wave_fp8.hip", "k_wave_moe.hip"])
 
 
 def test_every_instance_reported(resources):
     # 16 source counts x 3 vector counts x bf16/fp8 for partials; 3 x 2 each for input and residual
     assert sum(1 for k in resources if k[0] == "Partials") == 96
     assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
+    # one wavefront per row: partials bf16 and fp8, MoE bf16, 16 source counts each
+    assert sum(1 for k in resources if k[0].startswith("Wave")) == 48
+
+
+def test_one_wave_rows_keep_two_waves_per_simd(resources):
+    low = {k: v["VGPRs"] for k, v in resources.items()
+           if k[0].startswith("Wave") and (v["VGPRs"] > 256 or v["Occupancy [waves/SIMD]"] < 2)}
+    assert not low, f"one-wavefront rows above 256 VGPRs: {low}"
 
 
 def test_fold_kernels_fit_eight_waves_per_simd(resources):
     over = {k: v["VGPRs"] for k, v in resources.items()
-            if k[2] <= 2 and (k[0] != "Partials" or k[1] <= 8) and v["VGPRs"] > 64}
+            if k[2] <= 2 and k[0] in ("Partials", "Input", "Residual") and (k[0] != "Partials" or k[1] <= 8)
+            and v["VGPRs"] > 64}
     assert not over, f"kernels above 64 VGPRs (fewer than 8 waves per SIMD): {over}"
 
 
-def test_prefill_fold_register_use(resources):
-    # the prefill boundary's kernel (P = 8, two vectors per thread), bf16 and fp8 outputs
+def test_two_vector_fold_register_use(resources):
+    # the P = 8 fold with two vectors per thread, bf16 and fp8 outputs: prefill batches above
+    # 8 rows per CU and rows up to H = 16384
     for fp8 in (False, True):
         r = resources[("Partials", 8, 2, fp8)]
         assert r["VGPRs"] <= 64 and r["Occupancy [waves/SIMD]"] == 8, r
