@@ -34,18 +34,30 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 1 << 30          # >= 4x the 256 MB Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["kernels.h", "launch.h", "k_partials.hip", "k_moe.hip", "k_read.hip",
-                  "k_complete.hip", "k_wave.hip", "k_wave_fp8.hip", "k_wave_moe.hip", "host.cpp"]
+                  "k_complete.hip", "k_wave.hip", "host.cpp"]
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+# C++ comments, string and character literals, in source order: the literals are matched so that
+# a "//" inside one is not taken for a comment
+_CXX_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def code_text(src: str) -> str:
+    """The source with comments removed and whitespace runs collapsed: what the compiler sees."""
+    src = _CXX_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
+    """sha256 of the kernel and launch sources' code (comments and layout excluded)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "reduce_residual_rmsnorm_bnd_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "reduce_residual_rmsnorm_bnd_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -573,7 +585,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "kernel": "bnd_fold_norm's kernel (one wavefront per row at 2048 rows x 4096 on "
-                               "256 CUs: wave_read_kernel<Partials, P=8, bf16>)",
+                               "256 CUs: wave_read_kernel<Partials, 8 vectors per lane, bf16>, P=8)",
                      "algorithmic_bytes": nbytes,
                      "kernel_mean_us": t["kernel_s"] * 1e6,
                      "kernel_timing": "the smaller of two HIP-event means over the timed region: "

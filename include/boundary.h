@@ -274,9 +274,9 @@ typedef enum bnd_option {
   BND_OPT_FUSED_UNAVAILABLE = 1,
   /* Launch shape overrides for tuning; 0 = automatic. Threads per row: a
    * multiple of 64 in [64, 1024]. Vectors (of 8 elements) per thread: 1, 2
-   * or 4, or 8 for one wavefront per row (64 threads; folds of partials or
-   * MoE picks with H <= 4096 only). A shape that cannot cover H, or 8 for
-   * any other call, fails with NO_PATH. */
+   * or 4, or 8 or 14 for one wavefront per row (64 threads; folds of
+   * partials or MoE picks with H <= 4096 or H <= 7168 only). A shape that
+   * cannot cover H, or 8 or 14 for any other call, fails with NO_PATH. */
   BND_OPT_THREADS_PER_ROW = 2,
   BND_OPT_VECTORS_PER_THREAD = 3
 } bnd_option;

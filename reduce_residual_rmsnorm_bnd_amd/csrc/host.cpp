@@ -167,31 +167,38 @@ int compute_units() {
 //  - workgroups of at least 256 threads are rounded up to whole multiples of
 //    256 so every SIMD of the CU gets the same number of waves (7- or 5-wave
 //    workgroups measured 3-6% slower than 8- or 4-wave ones);
-//  - a fold of partials or MoE picks with bf16 output whose rows hold
-//    449..512 vectors (H = 3592..4096) and whose row count is above 6 and at
-//    most 8 rows per CU runs one wavefront per row (vpt = 8, 64 threads): the
-//    kernel needs about 180 VGPRs, so 8 such rows fit on a CU and the launch
-//    is one round; at 2048 rows x 4096 it is 7% faster than two vectors per
-//    thread (P = 8) and 9% faster for k = 8 MoE picks, equal at 1536 rows, and
-//    slower once the rows need a second round (3072 rows: 9% slower) or leave
-//    CUs short of waves (1024 rows: 30% slower). With fp8 output it is 1%
-//    slower at 2048 rows, so fp8 folds take it only when forced.
+//  - a fold of partials or MoE picks (bf16 or fp8 output) runs one wavefront
+//    per row (64 threads) when its rows hold 449..512 vectors (H = 3592..4096;
+//    8 vectors per lane, 124..153 VGPRs: at least three waves per SIMD) and
+//    the launch has more than 6 and at most 12 rows per CU, or 833..896
+//    vectors (H = 6664..7168; 14 vectors per lane, 178..255 VGPRs: two waves
+//    per SIMD) and more than 6 and at most 8 rows per CU: within those ranges
+//    all rows are resident in one round. Against the
+//    shapes above at 2048 rows: 7-9% faster at H = 4096 (bf16, fp8 and MoE
+//    picks) and 7% at H = 7168; 1-3% faster at 1536 rows; slower at 1024 rows
+//    and below (too few waves per CU: 17-87% slower) and once the rows need a
+//    second round (H = 7168 at 2560 rows: 15% slower; H = 4096 from 4096 rows:
+//    up to 4% slower).
 int round_threads(int need) {
   const int unit = need >= 256 ? 4 * bnd::kWave : bnd::kWave;
   return ((need + unit - 1) / unit) * unit;
 }
 
 // wave_ok: a one-wavefront kernel exists for the call (folds of partials or
-// MoE picks); wave_auto: the automatic choice may take it (bf16 output).
-bnd_status choose_launch(int64_t H, int64_t rows, bool wave_ok, bool wave_auto, Launch* l) {
+// MoE picks).
+bnd_status choose_launch(int64_t H, int64_t rows, bool wave_ok, Launch* l) {
   const int nvec = (int)(H / 8);
   int vpt = g_vpt_override.load();
   int threads = g_threads_override.load();
   const int64_t cus = compute_units();
+  const bool one_round_8 = rows > 6 * cus && rows <= 12 * cus;
+  const bool one_round_14 = rows > 6 * cus && rows <= 8 * cus;
   if (vpt == 0) {
-    if (wave_ok && wave_auto && nvec > (bnd::kWaveVpt - 1) * bnd::kWave && nvec <= bnd::kWaveVpt * bnd::kWave &&
-        rows > 6 * cus && rows <= 8 * cus) {
+    if (wave_ok && nvec > (bnd::kWaveVpt - 1) * bnd::kWave && nvec <= bnd::kWaveVpt * bnd::kWave && one_round_8) {
       vpt = bnd::kWaveVpt;
+    } else if (wave_ok && nvec > (bnd::kWaveVptWide - 1) * bnd::kWave && nvec <= bnd::kWaveVptWide * bnd::kWave &&
+               one_round_14) {
+      vpt = bnd::kWaveVptWide;
     } else if (nvec <= 256) {
       vpt = 1;
     } else if (nvec <= 1024 &&
@@ -201,19 +208,21 @@ bnd_status choose_launch(int64_t H, int64_t rows, bool wave_ok, bool wave_auto, 
       vpt = nvec <= 2048 ? 2 : 4;
     }
   }
-  if (vpt == bnd::kWaveVpt) {
+  if (vpt == bnd::kWaveVpt || vpt == bnd::kWaveVptWide) {
     if (!wave_ok)
-      return fail(BND_ERR_NO_PATH, "8 vectors per thread (one wavefront per row) only folds partials or MoE picks");
-    if (nvec > bnd::kWaveVpt * bnd::kWave)
-      return fail(BND_ERR_NO_PATH, "8 vectors per thread (one wavefront per row) needs H <= %d",
-                  bnd::kWaveVpt * bnd::kWave * 8);
+      return fail(BND_ERR_NO_PATH, "%d vectors per thread (one wavefront per row) only folds partials or MoE picks",
+                  vpt);
+    if (nvec > vpt * bnd::kWave)
+      return fail(BND_ERR_NO_PATH, "%d vectors per thread (one wavefront per row) needs H <= %d", vpt,
+                  vpt * bnd::kWave * 8);
     if (threads != 0 && threads != bnd::kWave)
-      return fail(BND_ERR_NO_PATH, "8 vectors per thread (one wavefront per row) needs 64 threads, not %d", threads);
+      return fail(BND_ERR_NO_PATH, "%d vectors per thread (one wavefront per row) needs 64 threads, not %d", vpt,
+                  threads);
     threads = bnd::kWave;
   }
   if (threads == 0) threads = round_threads((nvec + vpt - 1) / vpt);
-  if (vpt != 1 && vpt != 2 && vpt != 4 && vpt != bnd::kWaveVpt)
-    return fail(BND_ERR_NO_PATH, "vectors per thread %d: need 1, 2, 4 or 8", vpt);
+  if (vpt != 1 && vpt != 2 && vpt != 4 && vpt != bnd::kWaveVpt && vpt != bnd::kWaveVptWide)
+    return fail(BND_ERR_NO_PATH, "vectors per thread %d: need 1, 2, 4, 8 or 14", vpt);
   if (threads < bnd::kWave || threads > bnd::kMaxThreads || threads % bnd::kWave != 0)
     return fail(BND_ERR_NO_PATH, "threads per row %d: need a multiple of 64 in [64, 1024]", threads);
   if ((int64_t)threads * vpt < nvec)
@@ -361,8 +370,8 @@ bnd_status bnd_set_option(bnd_option opt, int64_t value) {
       g_threads_override.store((int)value);
       return ok();
     case BND_OPT_VECTORS_PER_THREAD:
-      if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8)
-        return fail(BND_ERR_INVALID_ARG, "vectors per thread: 0, 1, 2, 4 or 8");
+      if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8 && value != 14)
+        return fail(BND_ERR_INVALID_ARG, "vectors per thread: 0, 1, 2, 4, 8 or 14");
       g_vpt_override.store((int)value);
       return ok();
   }
@@ -499,7 +508,7 @@ bnd_status bnd_enter_norm(bnd_stream* s, const void* x, int64_t ld_x, const floa
     return fail(BND_ERR_INVALID_ARG, "x partly overlaps the residual storage");
   if (any) {
     Launch l;
-    if ((st = choose_launch(s->H, s->rows, false, false, &l))) return st;
+    if ((st = choose_launch(s->H, s->rows, false, &l))) return st;
     RowArgs a = base_args(s);
     a.w = w;
     a.eps = eps;
@@ -546,7 +555,7 @@ static bnd_status fold_read(bnd_stream* s, bnd_owed owed, bnd_kind kind, bool fp
     if ((st = check_output_disjoint(s, fp8 ? (i ? "scale" : "q") : "y", outs[i], true))) return st;
   if (any) {
     Launch l;
-    if ((st = choose_launch(s->H, s->rows, fold, !fp8, &l))) return st;
+    if ((st = choose_launch(s->H, s->rows, fold, &l))) return st;
     RowArgs a = base_args(s);
     a.w = w;
     a.eps = eps;
@@ -612,7 +621,7 @@ static bnd_status complete_into(bnd_stream* s, bnd_owed owed, bool with_extra, c
   }
   if (any) {
     Launch l;
-    if ((st = choose_launch(s->H, s->rows, false, false, &l))) return st;
+    if ((st = choose_launch(s->H, s->rows, false, &l))) return st;
     RowArgs a = base_args(s);
     pending_args(s, &a);
     a.extra = extra_rows;
@@ -665,7 +674,7 @@ bnd_status bnd_snapshot(bnd_stream* s, bnd_owed owed, void* out, int64_t ld_out,
   if ((st = check_output_disjoint(s, "out", rows_range(out, s->rows, ld_out, s->H, 2), true))) return st;
   if (any) {
     Launch l;
-    if ((st = choose_launch(s->H, s->rows, false, false, &l))) return st;
+    if ((st = choose_launch(s->H, s->rows, false, &l))) return st;
     RowArgs a = base_args(s);
     a.y = static_cast<uint16_t*>(out);
     a.ld_y = ld_out;

@@ -1,26 +1,33 @@
-// Boundary reads with one wavefront per row (64 lanes x 8 vectors): the
-// dispatcher, and folds of P plain partials with bf16 output, P = 1..16.
-// fp8 output and MoE picks are instantiated in k_wave_fp8.hip and
-// k_wave_moe.hip (compiled in parallel).
+// Boundary reads with one wavefront per row (64 lanes x 8 or 14 vectors):
+// folds of P plain partials with bf16 or fp8 output, and MoE finalize folds
+// of k gathered picks with bf16 output; P and k (1..16) are runtime values.
 #include "kernels.h"
 
 namespace bnd {
 
-KernelFn wave_kernel_partials_fp8(int n);
-KernelFn wave_kernel_moe(int n);
-
 namespace {
-using Seq = std::make_integer_sequence<int, kMaxSources>;
-constexpr std::array<KernelFn, kMaxSources> kPartialsBf16 = wave_table<Source::Partials, false>(Seq{});
+// [vectors per lane: 8, 14][partials bf16, partials fp8, MoE bf16]
+constexpr KernelFn kWaveKernels[2][3] = {
+    {&wave_read_kernel<Source::Partials, kWaveVpt, false>, &wave_read_kernel<Source::Partials, kWaveVpt, true>,
+     &wave_read_kernel<Source::Moe, kWaveVpt, false>},
+    {&wave_read_kernel<Source::Partials, kWaveVptWide, false>,
+     &wave_read_kernel<Source::Partials, kWaveVptWide, true>, &wave_read_kernel<Source::Moe, kWaveVptWide, false>}};
 }  // namespace
 
 hipError_t launch_read_wave(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
-  if (l.vpt != kWaveVpt || l.threads != kWave || a.nvec > kWave * kWaveVpt || n < 1 || n > kMaxSources)
+  const bool wide = l.vpt == kWaveVptWide;
+  if ((l.vpt != kWaveVpt && !wide) || l.threads != kWave || a.nvec > kWave * l.vpt || n < 1 || n > kMaxSources)
     return hipErrorInvalidValue;
+  int kind;
   if (src == Source::Partials)
-    return launch_kernel(fp8 ? wave_kernel_partials_fp8(n) : kPartialsBf16[n - 1], a, l, stream);
-  if (src == Source::Moe && !fp8) return launch_kernel(wave_kernel_moe(n), a, l, stream);
-  return hipErrorInvalidValue;
+    kind = fp8 ? 1 : 0;
+  else if (src == Source::Moe && !fp8)
+    kind = 2;
+  else
+    return hipErrorInvalidValue;
+  RowArgs b = a;
+  b.nsrc = n;
+  return launch_kernel(kWaveKernels[wide ? 1 : 0][kind], b, l, stream);
 }
 
 }  // namespace bnd

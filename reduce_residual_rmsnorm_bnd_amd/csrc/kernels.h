@@ -38,7 +38,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Row access through buffer resources. Every row operand gets a resource whose
 // base is the row and whose size is the row's bytes, so each access is
 // bounds-checked by the hardware (an out-of-range load returns 0 and an
-// out-of-range store is dropped) on top of the explicit lane guards.
+// out-of-range store is dropped); read_kernel also guards its stores by lane,
+// the one-wavefront read relies on the resource alone.
 // Cache policy: rows are read exactly once, so loads are non-temporal (nt);
 // stores carry sc1 (write-through past the XCD's L2). Both measured faster on
 // MI355X than the default policy for this 9:2 read:write stream.
@@ -359,6 +360,8 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
     // (max_h |x_h w_h|) inv: the scale is fp32(max|y| / 448) of these y.
     const float amax = mx * inv;
     const float scale = amax / 448.0f;
+    // one reciprocal per row and a multiply per element, as in wave_read_kernel
+    const float rcp = scale > 0.0f ? 1.0f / scale : 0.0f;
     const Rsrc qr = row_rsrc(a.q + row * a.ld_q, a.H);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
@@ -366,8 +369,7 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float y = (x[v][e] * w[v][e]) * inv;
-        const float u = scale > 0.0f ? y / scale : 0.0f;
-        t[e] = fminf(fmaxf(u, -448.0f), 448.0f);
+        t[e] = fminf(fmaxf(y * rcp, -448.0f), 448.0f);
       }
       if (ok[v]) store8(qr, (tid + v * nthr) * 8, f32_to_e4m3x8(t));
     }
@@ -408,172 +410,181 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// The boundary read with one wavefront per row (64 lanes x 8 vectors: rows of
-// up to 4096 elements), for folds of partials or MoE picks.
+// The boundary read with one wavefront per row, for folds of partials or MoE
+// picks: 64 lanes x VPT vectors (VPT = 8: rows of up to 4096 elements, 124..153
+// VGPRs; VPT = 14: up to 7168, 178..255 VGPRs, two waves per SIMD).
 //
-// Used when the launch's rows just fit on the chip in one round at two waves
-// per SIMD (the 2048-row prefill boundary on 256 CUs). Three things make it
-// faster there than the multi-wave rows above, all measured on MI355X:
+// Used when a launch's rows just fit on the chip in one round (on 256 CUs:
+// the 2048-row prefill, quantised and MoE boundaries). What makes it faster
+// there than the multi-wave rows of read_kernel, all measured on MI355X:
 //  - loads go source by source (every vector of source 0, then of source 1,
 //    ..., the residual last), so a wave streams one contiguous row of one
 //    operand at a time; vector-major order is up to 25% slower;
-//  - two loads are kept in flight per wave through a two-register ring with
-//    scheduling fences (one in flight is latency-bound, more is slower);
-//  - the norm weight is fetched right after the first source loads and kept
-//    in registers (64 VGPRs; the kernel fits 256), so after the row's sum of
-//    squares nothing waits on memory: loading the weight after the reduction
-//    leaves HBM idle at the tail of the single round and costs 7%.
+//  - two loads are kept in flight per wave through a two-register ring (one
+//    in flight is latency-bound, more is slower);
+//  - each vector is finished during the residual pass, so nothing but a few
+//    multiplies and the stores follow the row's reduction: the residual is
+//    stored at once, x^2 and |x w| are accumulated, and only x w is kept (the
+//    weight vector is loaded together with the residual's). The row then
+//    holds one set of 8 * VPT floats, not x and w both. Loading the weight
+//    after the reduction, or quantising with a full division per element,
+//    leaves HBM idle at the tail of the single round (7% and 10% slower).
 // The reduction is a wavefront DPP sum with no LDS and no barrier. The sum of
 // the sources runs in the same order per element as in load_and_fold, so the
-// residual is bitwise the same as with the other launch shapes.
+// residual is bitwise the same as with read_kernel; y = (x w) inv, and the
+// fp8 codes are those of (x w) inv times the reciprocal of the row's scale.
 // ---------------------------------------------------------------------------
 constexpr int kWaveDepth = 2;
 
-// The row's sources, resolved before the first load: N partial rows, or N
-// expert rows with their gates (an invalid pick gets an empty resource, so its
-// loads read 0), then the residual as source N (empty when there is none).
-template <Source S, int N>
-struct RowSources {
-  Rsrc r[N + 1];
-  float g[S == Source::Moe ? N : 1];
-  __device__ __forceinline__ RowSources(const RowArgs& a, int64_t row) {
-    const int rb = a.H * 2;
-#pragma unroll
-    for (int p = 0; p < N; ++p) {
-      if constexpr (S == Source::Partials) {
-        r[p] = row_rsrc(a.src[p] + row * a.ld_src, rb);
-      } else {
-        const int64_t e = a.idx[row * N + p];
-        const bool valid = e >= 0 && e < a.n_expert_rows;
-        r[p] = row_rsrc(a.experts + (valid ? e : 0) * a.ld_e, valid ? rb : 0);
-        g[p] = a.gate[row * N + p];
-      }
-    }
-    r[N] = row_rsrc(a.res + row * a.ld_res, a.has_residual ? rb : 0);
-  }
+// One source row of the fold: its resource (empty for an invalid MoE pick or a
+// missing residual, so its loads read 0) and, for MoE, its gate.
+struct RowSource {
+  Rsrc r;
+  float g;
 };
 
-// Load I of the row (I = source * kWaveVpt + vector) and the pipeline that
-// consumes load I while load I + kWaveDepth is in flight.
-template <Source S, int N>
-struct WaveFold {
-  static constexpr int kLoads = (N + 1) * kWaveVpt;
-  template <int I>
-  __device__ static __forceinline__ uint4 load(const RowSources<S, N>& src, int lane) {
-    return load16(src.r[I / kWaveVpt], (lane + (I % kWaveVpt) * kWave) * 16);
+template <Source S>
+__device__ __forceinline__ RowSource row_source(const RowArgs& a, int64_t row, int p) {
+  const int rb = a.H * 2;
+  if (p == a.nsrc) return {row_rsrc(a.res + row * a.ld_res, a.has_residual ? rb : 0), 1.0f};
+  if constexpr (S == Source::Partials) {
+    return {row_rsrc(a.src[p] + row * a.ld_src, rb), 1.0f};
+  } else {
+    const int64_t e = a.idx[row * a.nsrc + p];
+    const bool valid = e >= 0 && e < a.n_expert_rows;
+    return {row_rsrc(a.experts + (valid ? e : 0) * a.ld_e, valid ? rb : 0), a.gate[row * a.nsrc + p]};
   }
-  template <int I>
-  __device__ static __forceinline__ void prologue(const RowSources<S, N>& src, int lane,
-                                                  uint4 (&ring)[kWaveDepth]) {
-    if constexpr (I < kWaveDepth && I < kLoads) {
-      ring[I] = load<I>(src, lane);
-      prologue<I + 1>(src, lane, ring);
-    }
-  }
-  template <int I>
-  __device__ static __forceinline__ void steps(const RowSources<S, N>& src, int lane, uint4 (&ring)[kWaveDepth],
-                                               float (&x)[kWaveVpt][8]) {
-    if constexpr (I < kLoads) {
-      constexpr int p = I / kWaveVpt, v = I % kWaveVpt;
-      float t[8];
-      bf16x8_to_f32(ring[I % kWaveDepth], t);
-      if constexpr (I + kWaveDepth < kLoads) ring[I % kWaveDepth] = load<I + kWaveDepth>(src, lane);
-      if constexpr (p == N) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[v][e] = t[e] + x[v][e];  // residual + contribution
-      } else if constexpr (S == Source::Moe) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[v][e] = fmaf(src.g[p], t[e], p == 0 ? 0.0f : x[v][e]);
-      } else if constexpr (p == 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[v][e] = t[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[v][e] += t[e];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      steps<I + 1>(src, lane, ring, x);
-    }
-  }
-};
+}
 
-template <Source S, int N, bool FP8>
+// Keeps a step's arithmetic at its place in the pipeline: the empty asm reads
+// and writes the eight sums, so they are computed before it, and the
+// scheduling fence after it keeps later loads behind it. (A fence alone does
+// not stop the compiler from sinking the adds towards their later uses.)
+__device__ __forceinline__ void pin8(float (&x)[8]) {
+  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
+}
+
+__device__ __forceinline__ void load_weight8(const Rsrc& wr, int vec, u32x4& lo, u32x4& hi) {
+  // the weight is shared by all rows: default cache policy, it stays in L2
+  lo = __builtin_amdgcn_raw_buffer_load_b128(wr, vec * 32, 0, 0);
+  hi = __builtin_amdgcn_raw_buffer_load_b128(wr, vec * 32 + 16, 0, 0);
+}
+
+// The pipeline over one source row: step v consumes the ring slot of vector v
+// and refills it with the load two vectors ahead, which for the last two
+// vectors is the next source's first two. VPT is even, so the slot of every
+// load is its vector index mod 2, whatever the source.
+template <Source S, int VPT, bool kFirst>
+__device__ __forceinline__ void fold_source(const RowSource& cur, const RowSource& next, int lane,
+                                            uint4 (&ring)[kWaveDepth], float (&x)[VPT][8]) {
+  static_assert(VPT % kWaveDepth == 0, "ring slots follow the vector index");
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    float t[8];
+    bf16x8_to_f32(ring[v % kWaveDepth], t);
+    ring[v % kWaveDepth] = v + kWaveDepth < VPT ? load16(cur.r, (lane + (v + kWaveDepth) * kWave) * 16)
+                                                : load16(next.r, (lane + (v + kWaveDepth - VPT) * kWave) * 16);
+    if constexpr (S == Source::Moe) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[v][e] = fmaf(cur.g, t[e], kFirst ? 0.0f : x[v][e]);
+    } else if constexpr (kFirst) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[v][e] = t[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[v][e] += t[e];
+    }
+    pin8(x[v]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <Source S, int VPT, bool FP8>
 __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
   static_assert(S == Source::Partials || S == Source::Moe, "one-wave rows fold partials or MoE picks");
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
-  bool ok[kWaveVpt];
-#pragma unroll
-  for (int v = 0; v < kWaveVpt; ++v) ok[v] = (lane + v * kWave) < a.nvec;
-
-  const RowSources<S, N> src(a, row);
-  uint4 ring[kWaveDepth];
-  WaveFold<S, N>::template prologue<0>(src, lane, ring);
-  // the weight (L2-resident, shared by all rows) behind the first source loads
+  const int n = a.nsrc;
   const Rsrc wr = row_rsrc(a.w, a.H * 4);
-  u32x4 wlo[kWaveVpt], whi[kWaveVpt];
-#pragma unroll
-  for (int v = 0; v < kWaveVpt; ++v) {
-    wlo[v] = __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + v * kWave) * 32, 0, 0);
-    whi[v] = __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + v * kWave) * 32 + 16, 0, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  float x[kWaveVpt][8];
-  WaveFold<S, N>::template steps<0>(src, lane, ring, x);
-
+  const Rsrc res = row_rsrc(a.res + row * a.ld_res, a.H * 2);
   const float offset = a.gemma ? 1.0f : 0.0f;
-  float w[kWaveVpt][8];
+
+  uint4 ring[kWaveDepth];
+  u32x4 wlo[kWaveDepth], whi[kWaveDepth];
+  RowSource cur = row_source<S>(a, row, 0);
+  RowSource next = row_source<S>(a, row, 1);
 #pragma unroll
-  for (int v = 0; v < kWaveVpt; ++v) {
-    w[v][0] = __uint_as_float(wlo[v].x) + offset; w[v][1] = __uint_as_float(wlo[v].y) + offset;
-    w[v][2] = __uint_as_float(wlo[v].z) + offset; w[v][3] = __uint_as_float(wlo[v].w) + offset;
-    w[v][4] = __uint_as_float(whi[v].x) + offset; w[v][5] = __uint_as_float(whi[v].y) + offset;
-    w[v][6] = __uint_as_float(whi[v].z) + offset; w[v][7] = __uint_as_float(whi[v].w) + offset;
+  for (int v = 0; v < kWaveDepth; ++v) ring[v] = load16(cur.r, (lane + v * kWave) * 16);
+  // the weights of the residual pass's first vectors, held until then
+#pragma unroll
+  for (int v = 0; v < kWaveDepth; ++v) load_weight8(wr, lane + v * kWave, wlo[v], whi[v]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  float x[VPT][8];
+  fold_source<S, VPT, true>(cur, next, lane, ring, x);
+  for (int p = 1; p < n; ++p) {
+    cur = next;
+    next = row_source<S>(a, row, p + 1);  // p + 1 == n: the residual
+    fold_source<S, VPT, false>(cur, next, lane, ring, x);
   }
+
+  // The residual pass: each vector is finished here. The residual is stored at
+  // once (lanes past the end of the row address beyond the row resource and
+  // are dropped), x^2 and |x w| are accumulated and only x w is kept, so the
+  // row never holds x and w together.
   float ss = 0.0f, mx = 0.0f;
 #pragma unroll
-  for (int v = 0; v < kWaveVpt; ++v)
+  for (int v = 0; v < VPT; ++v) {
+    float t[8];
+    bf16x8_to_f32(ring[v % kWaveDepth], t);
+    const u32x4 lo = wlo[v % kWaveDepth], hi = whi[v % kWaveDepth];
+    if (v + kWaveDepth < VPT) {
+      ring[v % kWaveDepth] = load16(next.r, (lane + (v + kWaveDepth) * kWave) * 16);
+      load_weight8(wr, lane + (v + kWaveDepth) * kWave, wlo[v % kWaveDepth], whi[v % kWaveDepth]);
+    }
+    const float w[8] = {__uint_as_float(lo.x) + offset, __uint_as_float(lo.y) + offset,
+                        __uint_as_float(lo.z) + offset, __uint_as_float(lo.w) + offset,
+                        __uint_as_float(hi.x) + offset, __uint_as_float(hi.y) + offset,
+                        __uint_as_float(hi.z) + offset, __uint_as_float(hi.w) + offset};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(x[v][e], x[v][e], ss);
-  ss = wave_sum(ss);
-  if constexpr (FP8) {
+    for (int e = 0; e < 8; ++e) x[v][e] = t[e] + x[v][e];  // residual + contribution
+    store16(res, (lane + v * kWave) * 16, f32_to_bf16x8(x[v]));
 #pragma unroll
-    for (int v = 0; v < kWaveVpt; ++v)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[v][e] * w[v][e]));
-    mx = wave_max(mx);
+    for (int e = 0; e < 8; ++e) {
+      ss = fmaf(x[v][e], x[v][e], ss);
+      x[v][e] = x[v][e] * w[e];
+      mx = fmaxf(mx, fabsf(x[v][e]));
+    }
+    pin8(x[v]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const float inv = 1.0f / sqrtf(ss / (float)a.H + a.eps);
 
-  const int row_bytes = a.H * 2;
-  const Rsrc res = row_rsrc(a.res + row * a.ld_res, row_bytes);
-#pragma unroll
-  for (int v = 0; v < kWaveVpt; ++v)
-    if (ok[v]) store16(res, (lane + v * kWave) * 16, f32_to_bf16x8(x[v]));
+  ss = wave_sum(ss);
+  if constexpr (FP8) mx = wave_max(mx);
+  const float inv = 1.0f / sqrtf(ss / (float)a.H + a.eps);
   if constexpr (!FP8) {
-    const Rsrc yr = row_rsrc(a.y + row * a.ld_y, row_bytes);
+    const Rsrc yr = row_rsrc(a.y + row * a.ld_y, a.H * 2);
 #pragma unroll
-    for (int v = 0; v < kWaveVpt; ++v) {
+    for (int v = 0; v < VPT; ++v) {
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (x[v][e] * inv) * w[v][e];
-      if (ok[v]) store16(yr, (lane + v * kWave) * 16, f32_to_bf16x8(y));
+      for (int e = 0; e < 8; ++e) y[e] = x[v][e] * inv;
+      store16(yr, (lane + v * kWave) * 16, f32_to_bf16x8(y));
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    // the same scale and codes as read_kernel: max|y| = max|x w| inv exactly
+    // max_h |y_h| = (max_h |x_h w_h|) inv exactly (rounding is monotone)
     const float amax = mx * inv;
     const float scale = amax / 448.0f;
+    const float rcp = scale > 0.0f ? 1.0f / scale : 0.0f;
     const Rsrc qr = row_rsrc(a.q + row * a.ld_q, a.H);
 #pragma unroll
-    for (int v = 0; v < kWaveVpt; ++v) {
+    for (int v = 0; v < VPT; ++v) {
       float t[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y = (x[v][e] * w[v][e]) * inv;
-        const float u = scale > 0.0f ? y / scale : 0.0f;
-        t[e] = fminf(fmaxf(u, -448.0f), 448.0f);
-      }
-      if (ok[v]) store8(qr, (lane + v * kWave) * 8, f32_to_e4m3x8(t));
+      for (int e = 0; e < 8; ++e) t[e] = fminf(fmaxf((x[v][e] * inv) * rcp, -448.0f), 448.0f);
+      store8(qr, (lane + v * kWave) * 8, f32_to_e4m3x8(t));
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (lane == 0) a.scale[row] = scale;
   }
@@ -592,11 +603,6 @@ constexpr std::array<KernelFn, sizeof...(I)> read_table(std::integer_sequence<in
 template <Source S, int VPT, bool kFold, int... I>
 constexpr std::array<KernelFn, sizeof...(I)> complete_table(std::integer_sequence<int, I...>) {
   return {{&complete_kernel<S, I + 1, VPT, kFold>...}};
-}
-
-template <Source S, bool FP8, int... I>
-constexpr std::array<KernelFn, sizeof...(I)> wave_table(std::integer_sequence<int, I...>) {
-  return {{&wave_read_kernel<S, I + 1, FP8>...}};
 }
 
 inline hipError_t launch_kernel(KernelFn fn, const RowArgs& a, const Launch& l, hipStream_t stream) {

@@ -10,7 +10,10 @@ namespace bnd {
 constexpr int kMaxSources = 16;
 constexpr int kMaxThreads = 1024;
 constexpr int kWave = 64;
-constexpr int kWaveVpt = 8;  // vectors per lane of the one-wavefront-per-row read (H <= 4096)
+// vectors per lane of the one-wavefront-per-row read: 8 for rows of up to 4096
+// elements, 14 for rows of up to 7168
+constexpr int kWaveVpt = 8;
+constexpr int kWaveVptWide = 14;
 
 // Arguments of one boundary launch. Every row pointer is already offset to
 // the first row the launch processes, so a kernel addresses row i of each
@@ -41,12 +44,13 @@ struct RowArgs {
   int has_residual;                  // 0: fold with r = 0 (Pending without a residual)
   int gemma;                         // 1: the norm weight is an offset from one, y = x inv (1 + w)
   int copy_input;                    // enter: store x_in into the residual storage
+  int nsrc;                          // one-wavefront read: number of partials or MoE picks
 };
 
 struct Launch {
   int rows;     // grid size
   int threads;  // workgroup size, multiple of 64
-  int vpt;      // 16-byte vectors per thread: 1, 2 or 4; 8 = one wavefront per row (threads = 64)
+  int vpt;      // 16-byte vectors per thread: 1, 2 or 4; 8 or 14 = one wavefront per row (threads = 64)
   hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
   hipEvent_t stop = nullptr;
 };

@@ -374,6 +374,25 @@ def test_one_wave_rows_only_where_a_kernel_exists():
     _unchanged(h)
 
 
+def test_wide_one_wave_rows_only_where_a_kernel_exists():
+    # fourteen vectors per thread: one wavefront per row, for folds with H <= 7168
+    assert L.bnd_set_option(B.BND_OPT_VECTORS_PER_THREAD, 14) == 0
+    assert L.bnd_get_option(B.BND_OPT_VECTORS_PER_THREAD) == 14
+    h = create(T=8, rows=8)
+    st = L.bnd_enter_norm(h, fake(1 << 28), H, fake(1 << 31), 1e-6, fake(1 << 30), H, None)
+    assert st == B.BND_ERR_NO_PATH and b"wavefront" in L.bnd_last_error()
+    assert L.bnd_stream_state(h) == B.BND_INITIAL
+    wide = 7176
+    h = create(T=8, rows=4, ld=wide, Hh=wide)
+    assert L.bnd_written(h, fake(), wide) == 0
+    o = owed_out()
+    arr = (VP * 2)(*[fake((p + 1) << 24) for p in range(2)])
+    assert L.bnd_publish_partials(h, arr, 2, wide, ctypes.byref(o)) == 0
+    st = L.bnd_fold_norm(h, o.value, fake(1 << 31), 1e-6, fake(1 << 30), wide, None)
+    assert st == B.BND_ERR_NO_PATH and b"H <= 7168" in L.bnd_last_error()
+    _unchanged(h)
+
+
 def test_enter_validation():
     h = create(T=8, rows=8)
     w = fake(1 << 31)

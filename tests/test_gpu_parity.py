@@ -738,41 +738,60 @@ def test_snapshot_leaves_the_owed_work(orc):
 
 # ------------------------------------------------------------------ one wavefront per row
 
-WAVE = (64, 8)  # threads per row, vectors per thread: the one-wavefront read
+WAVE = (64, 8)        # threads per row, vectors per thread: the one-wavefront read, H <= 4096
+WAVE_WIDE = (64, 14)  # the same for rows of up to 7168 elements
 
-WAVE_SHAPES = [  # T, H, P, pad, row_begin, rows
-    (300, 4096, 8, 0, 0, None),
-    (77, 3600, 3, 8, 0, None),     # 450 vectors: the last lanes of the last vector idle
-    (5, 264, 16, 0, 0, None),      # 33 vectors: most lanes idle, sixteen sources
-    (3, 8, 1, 0, 0, None),         # one vector
-    (40, 4096, 2, 16, 7, 20),      # a slice of rows
+WAVE_SHAPES = [  # vectors per lane, T, H, P, pad, row_begin, rows
+    (8, 300, 4096, 8, 0, 0, None),
+    (8, 77, 3600, 3, 8, 0, None),     # 450 vectors: the last lanes of the last vector idle
+    (8, 5, 264, 16, 0, 0, None),      # 33 vectors: most lanes idle, sixteen sources
+    (8, 3, 8, 1, 0, 0, None),         # one vector
+    (8, 40, 4096, 2, 16, 7, 20),      # a slice of rows
+    (14, 300, 7168, 8, 0, 0, None),
+    (14, 61, 6680, 5, 8, 0, None),    # 835 vectors: ragged last vector
+    (14, 9, 4104, 16, 0, 0, None),    # just above the narrow kernel's rows, sixteen sources
+    (14, 3, 8, 1, 0, 0, None),
+    (14, 40, 7168, 2, 16, 11, 25),
 ]
 
 
-@pytest.mark.parametrize("T,H,P,pad,rb,rows", WAVE_SHAPES)
+@pytest.mark.parametrize("vpt,T,H,P,pad,rb,rows", WAVE_SHAPES)
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-def test_wave_rows(orc, T, H, P, pad, rb, rows, fp8):
+def test_wave_rows(orc, vpt, T, H, P, pad, rb, rows, fp8):
     d = workloads.fold_inputs(300 + T + H + P, T, H, P)
-    with forced_shape(*WAVE):
-        assert_fold_matches(orc, d, f"one wave per row T={T} H={H} P={P} slice={rb}+{rows}", fp8=fp8,
-                            pad=pad, row_begin=rb, rows=rows)
+    with forced_shape(64, vpt):
+        assert_fold_matches(orc, d, f"one wave per row x{vpt} T={T} H={H} P={P} slice={rb}+{rows}",
+                            fp8=fp8, pad=pad, row_begin=rb, rows=rows)
 
 
-def test_wave_rows_edge_cases(orc):
-    d = workloads.fold_inputs(31, 12, 4096, 3)
-    with forced_shape(*WAVE):
+@pytest.mark.parametrize("shape,H", [(WAVE, 4096), (WAVE_WIDE, 7168)], ids=["x8", "x14"])
+def test_wave_rows_edge_cases(orc, shape, H):
+    d = workloads.fold_inputs(31, 12, H, 3)
+    with forced_shape(*shape):
         assert_fold_matches(orc, d, "one wave per row, no residual", with_residual=False)
+        assert_fold_matches(orc, d, "one wave per row, no residual fp8", with_residual=False, fp8=True)
         assert_fold_matches(orc, d, "one wave per row, Gemma weight", gemma=True)
         assert_fold_matches(orc, d, "one wave per row, Gemma weight fp8", gemma=True, fp8=True)
+    # zero rows: y = 0, scale 0 and +0 codes; a large outlier row
+    d["partials"] = [c.clone() for c in d["partials"]]
+    d["residual"] = d["residual"].clone()
+    for c in d["partials"]:
+        c[2].zero_()
+        c[5, 17] = 3.0e4
+    d["residual"][2].zero_()
+    with forced_shape(*shape):
+        assert_fold_matches(orc, d, "one wave per row, zero and outlier rows")
+        assert_fold_matches(orc, d, "one wave per row, zero and outlier rows fp8", fp8=True)
 
 
-def test_wave_rows_residual_matches_other_shapes(orc):
+@pytest.mark.parametrize("shape,H", [(WAVE, 4096), (WAVE_WIDE, 7168)], ids=["x8", "x14"])
+def test_wave_rows_residual_matches_other_shapes(orc, shape, H):
     """The residual is elementwise: bitwise the same for every launch shape; y agrees with the
     oracle under each."""
-    d = workloads.fold_inputs(32, 64, 4096, 8)
-    with forced_shape(*WAVE):
+    d = workloads.fold_inputs(32, 64, H, 8)
+    with forced_shape(*shape):
         a = run_fold(d)
-    with forced_shape(256, 2):
+    with forced_shape(512, 2):
         b = run_fold(d)
     assert torch.equal(a["res"].view, b["res"].view)
     diff = (bits(a["y"].view).astype(np.int32) - bits(b["y"].view).astype(np.int32))
@@ -791,6 +810,16 @@ def test_wave_rows_moe(orc):
     d16 = workloads.moe_inputs(34, 9, 3600, 16, 16)
     with forced_shape(*WAVE):
         run_moe(orc, d16, 0, 9, "one wave per row, MoE k=16 H=3600")
+    dw = workloads.moe_inputs(37, 70, 7168, 16, 8)
+    idx = dw["idx"].clone()
+    idx[3] = -5
+    dw["idx"] = idx
+    with forced_shape(*WAVE_WIDE):
+        run_moe(orc, dw, 0, 70, "one wave per row x14, MoE k=8 H=7168")
+        run_moe(orc, dw, 21, 30, "one wave per row x14, MoE slice", gemma=True)
+    dr = workloads.moe_inputs(38, 6, 5000, 8, 3)
+    with forced_shape(*WAVE_WIDE):
+        run_moe(orc, dr, 0, 6, "one wave per row x14, MoE k=3 H=5000")
 
 
 def test_wave_rows_moe_over_stacked_partials_is_fold(orc):
@@ -813,10 +842,15 @@ def test_wave_rows_moe_over_stacked_partials_is_fold(orc):
 
 
 def test_wave_rows_refused_where_no_kernel(orc):
-    """Eight vectors per thread exists only for folds with H <= 4096: other calls refuse it
-    before launching anything."""
+    """One wavefront per row exists only for folds with H <= 4096 (8 vectors per lane) or
+    H <= 7168 (14): other calls refuse it before launching anything."""
     d = workloads.fold_inputs(36, 4, 4104, 2)
     with forced_shape(*WAVE):
+        with pytest.raises(bnd.BoundaryError) as e:
+            run_fold(d)
+        assert e.value.status == bnd.BND_ERR_NO_PATH
+    d = workloads.fold_inputs(39, 4, 7176, 2)
+    with forced_shape(*WAVE_WIDE):
         with pytest.raises(bnd.BoundaryError) as e:
             run_fold(d)
         assert e.value.status == bnd.BND_ERR_NO_PATH

@@ -6,9 +6,9 @@ occupancy, so the fold and read kernels with one or two vectors per thread and u
 partial sources must stay within 64 VGPRs and never use scratch. A data-dependent branch around
 the Gemma weight offset once pushed the P = 8 fold to 100 VGPRs (half the resident rows, about
 a microsecond on the prefill boundary); this test fails on such a change before it reaches a
-benchmark. The one-wavefront-per-row read (eight vectors per lane) is chosen only while a
-launch's rows fit on the chip at 8 rows per CU, so it must keep two waves per SIMD (at most
-256 VGPRs), also without scratch.
+benchmark. The one-wavefront-per-row read (8 or 14 vectors per lane, the source count a runtime
+argument) is chosen only while a launch's rows fit on the chip in one round at two waves per
+SIMD, so it must stay within 256 VGPRs, also without scratch.
 """
 import os
 import re
@@ -46,8 +46,8 @@ def _resources(tmp_path, files):
                 table[current] = {}
                 continue
             m = WAVE_NAME.search(line)
-            if m:  # one wavefront per row: eight vectors per lane
-                current = ("Wave" + SOURCES[int(m.group(1))], int(m.group(2)), 8, m.group(3) == "1")
+            if m:  # one wavefront per row: (kind, runtime source count, vectors per lane, fp8)
+                current = ("Wave" + SOURCES[int(m.group(1))], 0, int(m.group(2)), m.group(3) == "1")
                 table[current] = {}
                 continue
             m = FIELD.search(line)
@@ -60,16 +60,17 @@ def _resources(tmp_path, files):
 def resources(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not installed")
-    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip", "k_wave.hip",
-                                                       "k_wave_fp8.hip", "k_wave_moe.hip"])
+    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip", "k_wave.hip"])
 
 
 def test_every_instance_reported(resources):
     # 16 source counts x 3 vector counts x bf16/fp8 for partials; 3 x 2 each for input and residual
     assert sum(1 for k in resources if k[0] == "Partials") == 96
     assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
-    # one wavefront per row: partials bf16 and fp8, MoE bf16, 16 source counts each
-    assert sum(1 for k in resources if k[0].startswith("Wave")) == 48
+    # one wavefront per row: partials bf16 and fp8, MoE bf16, at 8 and 14 vectors per lane
+    waves = sorted((k[0], k[2], k[3]) for k in resources if k[0].startswith("Wave"))
+    assert waves == sorted((kind, vpt, fp8) for vpt in (8, 14)
+                           for kind, fp8 in (("WavePartials", False), ("WavePartials", True), ("WaveMoe", False))), waves
 
 
 def test_one_wave_rows_keep_two_waves_per_simd(resources):
