@@ -443,16 +443,37 @@ struct RowSource {
   float g;
 };
 
+// A MoE row's picks: lane j < k holds the index and gate of pick j, fetched
+// with one load each when the row starts, so resolving a pick later is a
+// register read (v_readlane), not a dependent memory access. Lanes >= k read 0.
+struct RowPicks {
+  int idx = 0;
+  float gate = 0.0f;
+};
+
 template <Source S>
-__device__ __forceinline__ RowSource row_source(const RowArgs& a, int64_t row, int p) {
+__device__ __forceinline__ RowPicks row_picks(const RowArgs& a, int64_t row, int lane) {
+  RowPicks k;
+  if constexpr (S == Source::Moe) {
+    const Rsrc ir = row_rsrc(a.idx + row * a.nsrc, a.nsrc * 4);
+    const Rsrc gr = row_rsrc(a.gate + row * a.nsrc, a.nsrc * 4);
+    k.idx = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, lane * 4, 0, 0);
+    k.gate = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, lane * 4, 0, 0));
+  }
+  return k;
+}
+
+template <Source S>
+__device__ __forceinline__ RowSource row_source(const RowArgs& a, const RowPicks& picks, int64_t row, int p) {
   const int rb = a.H * 2;
   if (p == a.nsrc) return {row_rsrc(a.res + row * a.ld_res, a.has_residual ? rb : 0), 1.0f};
   if constexpr (S == Source::Partials) {
     return {row_rsrc(a.src[p] + row * a.ld_src, rb), 1.0f};
   } else {
-    const int64_t e = a.idx[row * a.nsrc + p];
+    const int64_t e = __builtin_amdgcn_readlane(picks.idx, p);
+    const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(picks.gate), p));
     const bool valid = e >= 0 && e < a.n_expert_rows;
-    return {row_rsrc(a.experts + (valid ? e : 0) * a.ld_e, valid ? rb : 0), a.gate[row * a.nsrc + p]};
+    return {row_rsrc(a.experts + (valid ? e : 0) * a.ld_e, valid ? rb : 0), g};
   }
 }
 
@@ -511,8 +532,9 @@ __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
 
   uint4 ring[kWaveDepth];
   u32x4 wlo[kWaveDepth], whi[kWaveDepth];
-  RowSource cur = row_source<S>(a, row, 0);
-  RowSource next = row_source<S>(a, row, 1);
+  const RowPicks picks = row_picks<S>(a, row, lane);
+  RowSource cur = row_source<S>(a, picks, row, 0);
+  RowSource next = row_source<S>(a, picks, row, 1);
 #pragma unroll
   for (int v = 0; v < kWaveDepth; ++v) ring[v] = load16(cur.r, (lane + v * kWave) * 16);
   // the weights of the residual pass's first vectors, held until then
@@ -524,7 +546,7 @@ __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
   fold_source<S, VPT, true>(cur, next, lane, ring, x);
   for (int p = 1; p < n; ++p) {
     cur = next;
-    next = row_source<S>(a, row, p + 1);  // p + 1 == n: the residual
+    next = row_source<S>(a, picks, row, p + 1);  // p + 1 == n: the residual
     fold_source<S, VPT, false>(cur, next, lane, ring, x);
   }
 
