@@ -10,8 +10,10 @@ synchronisations); the roofline block reports the kernel's algorithmic bytes
 over its average duration from HIP events recorded on the launch stream.
 
 Secondary measurements (the quantised read, the MoE finalize over all rows
-and over the reduce-scatter share, the decode chain eager and as a HIP graph,
-a streaming kernel with the fold's 9:2 read:write mix and no arithmetic as an
+and over the reduce-scatter share, complete_only, snapshot and add_to_output,
+the unfused fallback beside the fused fold, a variable-size share, the decode
+chain eager and as a HIP graph next to an empty kernel's launch cost, and a
+streaming kernel with the fold's 9:2 read:write mix and no arithmetic as an
 achievable-bandwidth context figure) and the oracle's CPU baseline go into the
 same JSON line.
 """
@@ -164,8 +166,17 @@ class Timed:
         }
 
 
-def kernel_fields(t) -> dict:
-    return {"kernel_us": t["kernel_s"] * 1e6,
+def launch_desc(bnd) -> dict:
+    """The shape of this thread's last launch through the library, as the bench reports it."""
+    rows, threads, vpt = bnd.last_launch_shape()
+    one_wave = vpt in (8, 14)
+    return {"workgroups": rows, "threads": threads, "vectors_per_thread": vpt,
+            "rows_per_workgroup": 1, "one_wavefront_per_row": one_wave}
+
+
+def kernel_fields(t, bnd) -> dict:
+    """Per-launch figures of a timed run, with the launch shape it used."""
+    return {"launch": launch_desc(bnd), "kernel_us": t["kernel_s"] * 1e6,
             "dispatch_event_mean_us": t["dispatch_event_mean_s"] * 1e6,
             "interval_us_per_launch": t["interval_mean_s"] * 1e6}
 
@@ -269,46 +280,61 @@ def moe_case(torch, bnd, d, n_sets, row_begin=0, rows=None, terminal_gemma=False
 
 
 def aux_case(torch, bnd, d, n_sets, kind):
-    """snapshot or add_to_output over the prefill workload: each step publishes the partials,
-    runs the call into a separate output, then marks the residual written again (host-only)
-    so the next step can publish."""
+    """snapshot, add_to_output or complete_only over the prefill workload: each step publishes
+    the partials, runs the call into a separate output, then marks the residual written again
+    (host-only) so the next step can publish. kind "unfused" is the fallback of a refused fused
+    fold, two launches per step: complete_only into a bf16 buffer, then a one-source fold_norm of
+    that buffer (the stream ends Written)."""
     T, H, P = d["T"], d["H"], d["P"]
     dev = torch.device("cuda:0")
     L = bnd.lib()
     base_parts = [c.to(dev) for c in d["partials"]]
     base_res = d["residual"].to(dev)
     extra0 = d["residual"].to(dev)  # any [T, H] bf16 tensor serves as the extra contribution
+    w = d["weight"].to(dev)
     sets = []
     for s_i in range(n_sets):
         parts = base_parts if s_i == 0 else [c.clone() for c in base_parts]
         res = base_res.clone()
-        extra = extra0.clone()
+        extra = extra0.clone() if kind == "add_to_output" else None
         st = bnd.bnd_stream_create(T, H, res)
         bnd.bnd_written(st, res)
         out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        y = torch.empty(T, H, dtype=torch.bfloat16, device=dev) if kind == "unfused" else None
         arr = (ctypes.c_void_p * P)(*[c.data_ptr() for c in parts])
-        sets.append((st, parts, res, extra, out, arr))
+        sets.append((st, parts, res, extra, out, y, arr))
     owed = ctypes.c_uint64()
     new = ctypes.c_uint64()
+    eps = ctypes.c_float(d["eps"])
+    wptr = ctypes.c_void_p(w.data_ptr())
     hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def step(i, ev0, ev1):
-        st, parts, res, extra, out, arr = sets[i]
+        st, parts, res, extra, out, y, arr = sets[i]
         rc = L.bnd_publish_partials(st.handle, arr, P, H, ctypes.byref(owed))
         if ev0 is not None:
             rc |= L.bnd_time_next_launch(ev0, ev1)
         if kind == "snapshot":
             rc |= L.bnd_snapshot(st.handle, owed.value, ctypes.c_void_p(out.data_ptr()), H, hs)
-        else:
+        elif kind == "add_to_output":
             rc |= L.bnd_add_to_output(st.handle, owed.value, ctypes.c_void_p(extra.data_ptr()), H,
                                       ctypes.c_void_p(out.data_ptr()), H, ctypes.byref(new), hs)
-        rc |= L.bnd_written(st.handle, ctypes.c_void_p(res.data_ptr()), H)
+        else:  # complete_only, or the first launch of the unfused fallback
+            rc |= L.bnd_complete_only(st.handle, owed.value, ctypes.c_void_p(out.data_ptr()), H,
+                                      ctypes.byref(new), hs)
+        if kind == "unfused":
+            rc |= L.bnd_fold_norm(st.handle, new.value, wptr, eps, ctypes.c_void_p(y.data_ptr()), H, hs)
+        else:
+            rc |= L.bnd_written(st.handle, ctypes.c_void_p(res.data_ptr()), H)
         if rc:
             raise RuntimeError(L.bnd_last_error().decode())
 
     el = T * H
-    nbytes = (P + 1) * el * 2 + el * 2
-    return step, nbytes, (sets, base_parts)
+    reads = {"snapshot": P + 1, "add_to_output": P + 1, "complete_only": P}
+    # the unfused pair moves the fused fold's bytes plus one bf16 [T, H] write and its re-read
+    nbytes = ((P + 1) * el * 2 + 2 * el * 2 + H * 4 + 2 * el * 2 if kind == "unfused"
+              else reads[kind] * el * 2 + el * 2)
+    return step, nbytes, (sets, base_parts, w)
 
 
 def decode_chain(torch, bnd, workloads, T, reps_eager, reps_graph, H=4096, P=4, n_b=96):
@@ -369,6 +395,50 @@ def decode_chain(torch, bnd, workloads, T, reps_eager, reps_graph, H=4096, P=4, 
     return {"T": T, "us_per_boundary_eager": eager * 1e6, "us_per_boundary_graph": graph * 1e6,
             "tokens_per_s_graph": T / graph, "algorithmic_bytes_per_boundary": bytes_b,
             "GBps_graph": bytes_b / graph / 1e9}
+
+
+def launch_floor(torch, n_launches=97, reps_eager=20, reps_graph=50, workgroups=1, threads=512):
+    """An empty kernel (libboundary_ceiling.so) launched back to back as many times as the decode
+    chain launches, eager and replayed from a HIP graph: the per-launch cost with no work, the
+    floor under the decode boundary's time per launch. One 512-thread workgroup is the launch
+    shape of a one-row fold at H = 4096."""
+    from reduce_residual_rmsnorm_bnd_amd import _build
+
+    L = ctypes.CDLL(_build.CEILING_LIB_PATH)
+    L.bnd_ceiling_empty.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    L.bnd_ceiling_empty.restype = ctypes.c_int
+
+    def chain():
+        hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(n_launches):
+            if L.bnd_ceiling_empty(workgroups, threads, hs):
+                raise RuntimeError("empty kernel launch failed")
+
+    for _ in range(3):
+        chain()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps_eager):
+        chain()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / (reps_eager * n_launches)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        chain()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps_graph):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = (time.perf_counter() - t0) / (reps_graph * n_launches)
+    return {"launches": n_launches, "workgroups": workgroups, "threads": threads,
+            "us_per_launch_eager": eager * 1e6, "us_per_launch_graph": graph * 1e6}
 
 
 def copy_ceiling(torch, n_bytes=1 << 30, reps=20):
@@ -563,6 +633,7 @@ def main():
     step, nbytes, keep = fold_case(torch, bnd, d, n_sets)
     log(f"timing {args.steps} steps over {n_sets} rotating sets")
     t = timer.run(step, n_sets, args.warmup, args.steps)
+    shape = launch_desc(bnd)
     achieved = nbytes / t["kernel_s"] / 1e9
     traffic = traffic_from_profiles("prefill T=2048 H=4096 P=8")
     result = {
@@ -584,8 +655,12 @@ def main():
                    "device_memory": device_memory_info()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "bnd_fold_norm's kernel (one wavefront per row at 2048 rows x 4096 on "
-                               "256 CUs: wave_read_kernel<Partials, 8 vectors per lane, bf16>, P=8)",
+                     "kernel": ("bnd_fold_norm's kernel, "
+                                + (f"wave_read_kernel<Partials, {shape['vectors_per_thread']} vectors per lane, "
+                                   "bf16 out> (one wavefront per row)" if shape["one_wavefront_per_row"] else
+                                   f"read_kernel<Partials, P=8, {shape['vectors_per_thread']} vectors per thread, "
+                                   f"bf16 out> ({shape['threads']} threads per row)")),
+                     "launch": shape,
                      "algorithmic_bytes": nbytes,
                      "kernel_mean_us": t["kernel_s"] * 1e6,
                      "kernel_timing": "the smaller of two HIP-event means over the timed region: "
@@ -612,7 +687,7 @@ def main():
         n_q = max(2, -(-ROTATE_BYTES // ((dq["P"] + 2) * dq["T"] * dq["H"] * 2 + dq["T"] * dq["H"])))
         step, nb, keep = fold_case(torch, bnd, dq, n_q, fp8=True)
         tq = timer.run(step, n_q, 20, 256)
-        sec["fp8_T2048_H7168_P8"] = {"tokens_per_s_kernel": 2048 / tq["kernel_s"], **kernel_fields(tq),
+        sec["fp8_T2048_H7168_P8"] = {"tokens_per_s_kernel": 2048 / tq["kernel_s"], **kernel_fields(tq, bnd),
                                      "GBps": nb / tq["kernel_s"] / 1e9,
                                      "frac": nb / tq["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                                      "algorithmic_bytes": nb}
@@ -626,29 +701,38 @@ def main():
                                    ("moe_terminal_gemma_T2048_H4096_k8", 0, 2048, True)):
             step, nb, keep = moe_case(torch, bnd, dm, n_m, rb, rows, terminal_gemma=tg)
             tm = timer.run(step, n_m, 20, 256)
-            sec[name] = {"tokens_per_s_kernel": rows / tm["kernel_s"], **kernel_fields(tm),
+            sec[name] = {"tokens_per_s_kernel": rows / tm["kernel_s"], **kernel_fields(tm, bnd),
                          "GBps": nb / tm["kernel_s"] / 1e9,
                          "frac": nb / tm["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                          "algorithmic_bytes": nb}
             del keep, step
         del dm
         torch.cuda.empty_cache()
-        log("snapshot and add_to_output (prefill sizes), the largest RSv share of 2047 rows")
-        for kind in ("snapshot", "add_to_output"):
+        log("complete_only, snapshot and add_to_output (prefill sizes), the unfused fallback, "
+            "the largest RSv share of 2047 rows")
+        for kind in ("complete_only", "snapshot", "add_to_output"):
             step, nb, keep = aux_case(torch, bnd, d, n_sets, kind)
             ta = timer.run(step, n_sets, 20, 256)
-            sec[f"{kind}_T2048_H4096_P8"] = {**kernel_fields(ta),
+            sec[f"{kind}_T2048_H4096_P8"] = {**kernel_fields(ta, bnd),
                                              "GBps": nb / ta["kernel_s"] / 1e9,
                                              "frac": nb / ta["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                                              "algorithmic_bytes": nb}
             del keep, step
+        step, nb, keep = aux_case(torch, bnd, d, n_sets, "unfused")
+        unfused_us = back_to_back_us(torch, lambda i: step(i, None, None), n_sets)
+        sec["unfused_fallback_T2048_H4096_P8"] = {
+            "launches_per_step": 2, "us_per_step_back_to_back": unfused_us,
+            "fused_fold_us_back_to_back": fold_us,
+            "unfused_over_fused": unfused_us / fold_us if fold_us else None,
+            "algorithmic_bytes": nb, "GBps": nb / unfused_us / 1e3}
+        del keep, step
         counts = [300, 0, 511, 256, 257, 1, 400, 322]
         rb, rows, Tr = bnd.bnd_rsv_share(counts, 2)
         dr = workloads.fold_inputs(6, Tr, 4096, 8)
         step, nb, keep = fold_case(torch, bnd, dr, n_sets, row_begin=rb, rows=rows)
         tr = timer.run(step, n_sets, 20, 256)
         sec["rsv_share_511_of_2047_H4096_P8"] = {"row_begin": rb, "rows": rows,
-                                                  **kernel_fields(tr),
+                                                  **kernel_fields(tr, bnd),
                                                   "GBps": nb / tr["kernel_s"] / 1e9,
                                                   "frac": nb / tr["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                                                   "algorithmic_bytes": nb}
@@ -656,6 +740,7 @@ def main():
         torch.cuda.empty_cache()
         log("decode chain (1 enter + 96 folds), eager and graph")
         sec["decode"] = [decode_chain(torch, bnd, workloads, T, 20, 50) for T in (1, 8, 32, 128)]
+        sec["launch_floor_empty_kernel"] = launch_floor(torch)
         torch.cuda.empty_cache()
         sec["copy_ceiling_1GiB"] = copy_ceiling(torch)
         result["secondary"] = sec

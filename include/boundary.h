@@ -274,15 +274,23 @@ typedef enum bnd_option {
   BND_OPT_FUSED_UNAVAILABLE = 1,
   /* Launch shape overrides for tuning; 0 = automatic. Threads per row: a
    * multiple of 64 in [64, 1024]. Vectors (of 8 elements) per thread: 1, 2
-   * or 4, or 8 or 14 for one wavefront per row (64 threads; folds of
-   * partials or MoE picks with H <= 4096 or H <= 7168 only). A shape that
-   * cannot cover H, or 8 or 14 for any other call, fails with NO_PATH. */
+   * or 4, or 8 or 14 for one wavefront per row (64 threads; H <= 4096 or
+   * H <= 7168; only calls that take owed partials or MoE picks: the folds,
+   * complete_only, add_to_output, and snapshot of a Pending stream). A shape
+   * that cannot cover H, or 8 or 14 for any other call, fails with NO_PATH. */
   BND_OPT_THREADS_PER_ROW = 2,
   BND_OPT_VECTORS_PER_THREAD = 3
 } bnd_option;
 
 BND_API bnd_status bnd_set_option(bnd_option opt, int64_t value);
 BND_API int64_t bnd_get_option(bnd_option opt);
+
+/* The launch shape of the calling thread's last kernel launch through this
+ * library: workgroups (one per row), threads per workgroup and 16-byte vectors
+ * per thread (8 or 14: one wavefront per row). All 0 before the thread's
+ * first launch; a call that launches nothing (an error, zero rows) leaves the
+ * previous values. Any pointer may be NULL. Always BND_OK. */
+BND_API bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_thread);
 
 /* Timing: the calling thread's next kernel launch records `start_event` and
  * `stop_event` (hipEvent_t, created by the caller) from its own dispatch

@@ -10,4 +10,5 @@ from .boundary import *  # noqa: F401,F403
 from .boundary import BoundaryError, Stream, lib, SYMBOLS  # noqa: F401
 
 __all__ = [n for n in dir() if n.startswith(("bnd_", "BND_"))] + [
-    "BoundaryError", "Stream", "lib", "SYMBOLS", "set_option", "get_option", "status_name"]
+    "BoundaryError", "Stream", "lib", "SYMBOLS", "set_option", "get_option", "status_name",
+    "last_launch_shape"]

@@ -48,7 +48,7 @@ SYMBOLS = [
     "bnd_stream_has_residual", "bnd_stream_set_norm_form", "bnd_publish_partials", "bnd_publish_moe", "bnd_enter_norm",
     "bnd_fold_norm", "bnd_fold_norm_quant_fp8", "bnd_moe_finalize_fold_norm", "bnd_complete_only",
     "bnd_add_to_output", "bnd_snapshot", "bnd_rsv_share", "bnd_written", "bnd_take_output", "bnd_status_str", "bnd_last_error", "bnd_version",
-    "bnd_set_option", "bnd_get_option", "bnd_time_next_launch",
+    "bnd_set_option", "bnd_get_option", "bnd_last_launch_shape", "bnd_time_next_launch",
 ]
 
 _lib = None
@@ -91,6 +91,7 @@ def _declare(lib):
         "bnd_version": (c.c_char_p, []),
         "bnd_set_option": (st, [c.c_int, i64]),
         "bnd_get_option": (i64, [c.c_int]),
+        "bnd_last_launch_shape": (st, [c.POINTER(i64), c.POINTER(i32), c.POINTER(i32)]),
         "bnd_time_next_launch": (st, [vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -126,6 +127,13 @@ def set_option(opt: int, value: int) -> None:
 
 def get_option(opt: int) -> int:
     return lib().bnd_get_option(opt)
+
+
+def last_launch_shape() -> tuple[int, int, int]:
+    """(workgroups, threads per workgroup, vectors per thread) of this thread's last launch."""
+    rows, threads, vpt = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().bnd_last_launch_shape(ctypes.byref(rows), ctypes.byref(threads), ctypes.byref(vpt)))
+    return rows.value, threads.value, vpt.value
 
 
 def _hip_stream(hip_stream):

@@ -6,8 +6,9 @@
 // buffer resources and cache policy (non-temporal loads, sc1 stores) as the fold. The loaded
 // vectors are combined with XOR so that every load is consumed and every store depends on all
 // nine. Its rate on a device is what that memory system delivers for this 9:2 read:write stream
-// in this layout; the fold is compared with it as context. Built into its own library
-// (libboundary_ceiling.so); the boundary library does not contain it.
+// in this layout; the fold is compared with it as context. A second, empty kernel gives the
+// cost of a launch with no work, the floor under the per-boundary time of small batches. Built
+// into its own library (libboundary_ceiling.so); the boundary library does not contain it.
 #include "kernels.h"
 
 namespace {
@@ -53,6 +54,8 @@ __global__ __launch_bounds__(bnd::kMaxThreads) void mix_kernel(const MixArgs a) 
   }
 }
 
+__global__ __launch_bounds__(bnd::kMaxThreads) void empty_kernel() {}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
@@ -91,4 +94,15 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix_9r2w(
                    : vpt == 4 ? reinterpret_cast<const void*>(&mix_kernel<4>)
                               : reinterpret_cast<const void*>(&mix_kernel<8>);
   return (int)hipLaunchKernel(fn, dim3((unsigned)rows), dim3((unsigned)threads), args, 0, stream);
+}
+
+// Launches the empty kernel once on `stream`: `workgroups` (1 .. 2^31-1) workgroups of `threads`
+// (a multiple of 64 in [64, 1024]) that do nothing. Returns 0 on success, -1 on an invalid
+// argument (nothing launched), or the hipError_t of the launch.
+extern "C" __attribute__((visibility("default"))) int bnd_ceiling_empty(int64_t workgroups, int threads,
+                                                                        hipStream_t stream) {
+  if (workgroups < 1 || workgroups > 0x7fffffff || threads < 64 || threads > bnd::kMaxThreads || threads % 64)
+    return -1;
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&empty_kernel), dim3((unsigned)workgroups),
+                              dim3((unsigned)threads), nullptr, 0, stream);
 }

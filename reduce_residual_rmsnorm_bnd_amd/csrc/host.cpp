@@ -63,6 +63,8 @@ std::atomic<int> g_threads_override{0};
 std::atomic<int> g_vpt_override{0};
 thread_local hipEvent_t g_time_start = nullptr;  // consumed by the thread's next launch
 thread_local hipEvent_t g_time_stop = nullptr;
+thread_local Launch g_chosen;       // the shape of the launch being prepared
+thread_local Launch g_last_launch;  // the shape of the thread's last launch
 
 bnd_status fail(bnd_status st, const char* fmt, ...) {
   char buf[512];
@@ -167,37 +169,54 @@ int compute_units() {
 //  - workgroups of at least 256 threads are rounded up to whole multiples of
 //    256 so every SIMD of the CU gets the same number of waves (7- or 5-wave
 //    workgroups measured 3-6% slower than 8- or 4-wave ones);
-//  - a fold of partials or MoE picks (bf16 or fp8 output) runs one wavefront
-//    per row (64 threads) when its rows hold 449..512 vectors (H = 3592..4096;
-//    8 vectors per lane, 124..153 VGPRs: at least three waves per SIMD) and
-//    the launch has more than 6 and at most 12 rows per CU, or 833..896
-//    vectors (H = 6664..7168; 14 vectors per lane, 178..255 VGPRs: two waves
-//    per SIMD) and more than 6 and at most 8 rows per CU: within those ranges
-//    all rows are resident in one round. Against the
-//    shapes above at 2048 rows: 7-9% faster at H = 4096 (bf16, fp8 and MoE
-//    picks) and 7% at H = 7168; 1-3% faster at 1536 rows; slower at 1024 rows
-//    and below (too few waves per CU: 17-87% slower) and once the rows need a
-//    second round (H = 7168 at 2560 rows: 15% slower; H = 4096 from 4096 rows:
-//    up to 4% slower).
+//  - a call that takes owed partials or MoE picks (the folds with bf16 or
+//    fp8 output, complete_only, add_to_output, snapshot) runs one wavefront per
+//    row (64 threads) when its rows hold 449..512 vectors (H = 3592..4096, 8
+//    vectors per lane) or 833..896 (H = 6664..7168, 14 per lane), the launch
+//    has at least 6 rows per CU, and all its rows are resident at once: at
+//    most as many rows per CU as the kernel's occupancy allows (its VGPRs set
+//    it: 92..153 VGPRs hold 12 to 20 rows per CU, 146..255 hold 8 or 12).
+//    Against the shapes above: 5-12% faster at 2048 rows for every such call
+//    at H = 4096 and H = 7168, 1-7% faster at 1536 rows (6 per CU), 17-87%
+//    slower at 1024 rows and below (too few waves per CU), and once the rows
+//    need a second round slower (up to 15%) or equal; faster again wherever
+//    larger batches still fit in one round (up to 4096 rows at H = 4096 for the
+//    completes, 3072 at H = 7168).
 int round_threads(int need) {
   const int unit = need >= 256 ? 4 * bnd::kWave : bnd::kWave;
   return ((need + unit - 1) / unit) * unit;
 }
 
-// wave_ok: a one-wavefront kernel exists for the call (folds of partials or
-// MoE picks).
-bnd_status choose_launch(int64_t H, int64_t rows, bool wave_ok, Launch* l) {
+// The call's one-wavefront kernels: whether they exist, and the rows per CU
+// each width holds at once (0: never taken automatically).
+struct WaveFit {
+  bool ok = false;
+  int rows_per_cu_8 = 0;
+  int rows_per_cu_14 = 0;
+};
+
+WaveFit wave_fit_read(bnd::Source src, bool fp8) {
+  return {true, bnd::wave_read_rows_per_cu(src, fp8, bnd::kWaveVpt),
+          bnd::wave_read_rows_per_cu(src, fp8, bnd::kWaveVptWide)};
+}
+
+WaveFit wave_fit_complete(bnd::Source src, bnd::Tail tail) {
+  return {true, bnd::wave_complete_rows_per_cu(src, tail, bnd::kWaveVpt),
+          bnd::wave_complete_rows_per_cu(src, tail, bnd::kWaveVptWide)};
+}
+
+bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l) {
   const int nvec = (int)(H / 8);
   int vpt = g_vpt_override.load();
   int threads = g_threads_override.load();
   const int64_t cus = compute_units();
-  const bool one_round_8 = rows > 6 * cus && rows <= 12 * cus;
-  const bool one_round_14 = rows > 6 * cus && rows <= 8 * cus;
   if (vpt == 0) {
-    if (wave_ok && nvec > (bnd::kWaveVpt - 1) * bnd::kWave && nvec <= bnd::kWaveVpt * bnd::kWave && one_round_8) {
+    const bool many = rows >= 6 * cus;
+    if (many && nvec > (bnd::kWaveVpt - 1) * bnd::kWave && nvec <= bnd::kWaveVpt * bnd::kWave &&
+        rows <= wave.rows_per_cu_8 * cus) {
       vpt = bnd::kWaveVpt;
-    } else if (wave_ok && nvec > (bnd::kWaveVptWide - 1) * bnd::kWave && nvec <= bnd::kWaveVptWide * bnd::kWave &&
-               one_round_14) {
+    } else if (many && nvec > (bnd::kWaveVptWide - 1) * bnd::kWave && nvec <= bnd::kWaveVptWide * bnd::kWave &&
+               rows <= wave.rows_per_cu_14 * cus) {
       vpt = bnd::kWaveVptWide;
     } else if (nvec <= 256) {
       vpt = 1;
@@ -209,9 +228,9 @@ bnd_status choose_launch(int64_t H, int64_t rows, bool wave_ok, Launch* l) {
     }
   }
   if (vpt == bnd::kWaveVpt || vpt == bnd::kWaveVptWide) {
-    if (!wave_ok)
-      return fail(BND_ERR_NO_PATH, "%d vectors per thread (one wavefront per row) only folds partials or MoE picks",
-                  vpt);
+    if (!wave.ok)
+      return fail(BND_ERR_NO_PATH,
+                  "%d vectors per thread (one wavefront per row) only takes the owed partials or MoE picks", vpt);
     if (nvec > vpt * bnd::kWave)
       return fail(BND_ERR_NO_PATH, "%d vectors per thread (one wavefront per row) needs H <= %d", vpt,
                   vpt * bnd::kWave * 8);
@@ -234,6 +253,7 @@ bnd_status choose_launch(int64_t H, int64_t rows, bool wave_ok, Launch* l) {
   l->vpt = vpt;
   l->start = g_time_start;
   l->stop = g_time_stop;
+  g_chosen = *l;
   return BND_OK;
 }
 
@@ -295,6 +315,7 @@ bnd_status launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(BND_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   g_time_start = nullptr;
   g_time_stop = nullptr;
+  g_last_launch = g_chosen;
   return BND_OK;
 }
 
@@ -351,6 +372,13 @@ const char* bnd_status_str(bnd_status st) {
 const char* bnd_last_error(void) { return g_last_error.c_str(); }
 
 const char* bnd_version(void) { return "libboundary 0.1 (gfx950)"; }
+
+bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_thread) {
+  if (rows) *rows = g_last_launch.rows;
+  if (threads) *threads = g_last_launch.threads;
+  if (vectors_per_thread) *vectors_per_thread = g_last_launch.vpt;
+  return ok();
+}
 
 bnd_status bnd_time_next_launch(void* start_event, void* stop_event) {
   g_time_start = static_cast<hipEvent_t>(start_event);
@@ -508,7 +536,7 @@ bnd_status bnd_enter_norm(bnd_stream* s, const void* x, int64_t ld_x, const floa
     return fail(BND_ERR_INVALID_ARG, "x partly overlaps the residual storage");
   if (any) {
     Launch l;
-    if ((st = choose_launch(s->H, s->rows, false, &l))) return st;
+    if ((st = choose_launch(s->H, s->rows, WaveFit{}, &l))) return st;
     RowArgs a = base_args(s);
     a.w = w;
     a.eps = eps;
@@ -554,8 +582,11 @@ static bnd_status fold_read(bnd_stream* s, bnd_owed owed, bnd_kind kind, bool fp
   for (int i = 0; i < n_out; ++i)
     if ((st = check_output_disjoint(s, fp8 ? (i ? "scale" : "q") : "y", outs[i], true))) return st;
   if (any) {
+    // a fold reads the owed partials or picks; a Written stream's read, the stored residual
+    const Source src = !fold ? Source::Residual : kind == BND_KIND_MOE ? Source::Moe : Source::Partials;
+    const int n = !fold ? 0 : kind == BND_KIND_MOE ? s->k : s->nsrc;
     Launch l;
-    if ((st = choose_launch(s->H, s->rows, fold, &l))) return st;
+    if ((st = choose_launch(s->H, s->rows, fold ? wave_fit_read(src, fp8) : WaveFit{}, &l))) return st;
     RowArgs a = base_args(s);
     a.w = w;
     a.eps = eps;
@@ -564,13 +595,7 @@ static bnd_status fold_read(bnd_stream* s, bnd_owed owed, bnd_kind kind, bool fp
     a.q = q;
     a.ld_q = ld_q;
     a.scale = scale;
-    Source src = Source::Residual;
-    int n = 0;
-    if (fold) {
-      pending_args(s, &a);
-      src = kind == BND_KIND_MOE ? Source::Moe : Source::Partials;
-      n = kind == BND_KIND_MOE ? s->k : s->nsrc;
-    }
+    if (fold) pending_args(s, &a);
     if ((st = launch_status(bnd::launch_read(src, n, fp8, a, l, (hipStream_t)hip_stream), name))) return st;
   }
   become_written(s);
@@ -621,14 +646,15 @@ static bnd_status complete_into(bnd_stream* s, bnd_owed owed, bool with_extra, c
   }
   if (any) {
     Launch l;
-    if ((st = choose_launch(s->H, s->rows, false, &l))) return st;
+    const Source src = s->kind == BND_KIND_MOE ? Source::Moe : Source::Partials;
+    const bnd::Tail tail = with_extra ? bnd::Tail::Extra : bnd::Tail::None;
+    if ((st = choose_launch(s->H, s->rows, wave_fit_complete(src, tail), &l))) return st;
     RowArgs a = base_args(s);
     pending_args(s, &a);
     a.extra = extra_rows;
     a.ld_extra = ld_extra;
     a.y = static_cast<uint16_t*>(out);
     a.ld_y = ld_out;
-    const Source src = s->kind == BND_KIND_MOE ? Source::Moe : Source::Partials;
     const int n = s->kind == BND_KIND_MOE ? s->k : s->nsrc;
     if ((st = launch_status(bnd::launch_complete(src, n, false, a, l, (hipStream_t)hip_stream), name)))
       return st;
@@ -674,7 +700,8 @@ bnd_status bnd_snapshot(bnd_stream* s, bnd_owed owed, void* out, int64_t ld_out,
   if ((st = check_output_disjoint(s, "out", rows_range(out, s->rows, ld_out, s->H, 2), true))) return st;
   if (any) {
     Launch l;
-    if ((st = choose_launch(s->H, s->rows, false, &l))) return st;
+    const WaveFit fit = s->state == BND_PENDING ? wave_fit_complete(Source::Partials, bnd::Tail::Residual) : WaveFit{};
+    if ((st = choose_launch(s->H, s->rows, fit, &l))) return st;
     RowArgs a = base_args(s);
     a.y = static_cast<uint16_t*>(out);
     a.ld_y = ld_out;

@@ -12,19 +12,30 @@ constexpr KernelFn kWaveKernels[2][3] = {
      &wave_read_kernel<Source::Moe, kWaveVpt, false>},
     {&wave_read_kernel<Source::Partials, kWaveVptWide, false>,
      &wave_read_kernel<Source::Partials, kWaveVptWide, true>, &wave_read_kernel<Source::Moe, kWaveVptWide, false>}};
+
+// the table slot of a call, or -1 when it has no one-wavefront kernel
+int wave_kind(Source src, bool fp8) {
+  if (src == Source::Partials) return fp8 ? 1 : 0;
+  if (src == Source::Moe && !fp8) return 2;
+  return -1;
+}
+
+std::atomic<int> g_rows_per_cu[2][3];  // 0: not read yet, -1: unknown
 }  // namespace
+
+int wave_read_rows_per_cu(Source src, bool fp8, int vpt) {
+  const int kind = wave_kind(src, fp8);
+  if (kind < 0 || (vpt != kWaveVpt && vpt != kWaveVptWide)) return 0;
+  const int w = vpt == kWaveVptWide ? 1 : 0;
+  return occupancy_rows(kWaveKernels[w][kind], g_rows_per_cu[w][kind]);
+}
 
 hipError_t launch_read_wave(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
   const bool wide = l.vpt == kWaveVptWide;
   if ((l.vpt != kWaveVpt && !wide) || l.threads != kWave || a.nvec > kWave * l.vpt || n < 1 || n > kMaxSources)
     return hipErrorInvalidValue;
-  int kind;
-  if (src == Source::Partials)
-    kind = fp8 ? 1 : 0;
-  else if (src == Source::Moe && !fp8)
-    kind = 2;
-  else
-    return hipErrorInvalidValue;
+  const int kind = wave_kind(src, fp8);
+  if (kind < 0) return hipErrorInvalidValue;
   RowArgs b = a;
   b.nsrc = n;
   return launch_kernel(kWaveKernels[wide ? 1 : 0][kind], b, l, stream);

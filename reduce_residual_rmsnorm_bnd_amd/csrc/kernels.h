@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include <array>
+#include <atomic>
 #include <utility>
 
 #include "launch.h"
@@ -495,6 +496,22 @@ __device__ __forceinline__ void load_weight8(const Rsrc& wr, int vec, u32x4& lo,
 // and refills it with the load two vectors ahead, which for the last two
 // vectors is the next source's first two. VPT is even, so the slot of every
 // load is its vector index mod 2, whatever the source.
+// One source vector into the running sum: a MoE pick adds g * t (the first
+// with a zero start), a partial adds t (the first is copied).
+template <Source S, bool kFirst>
+__device__ __forceinline__ void add_source(float g, const float (&t)[8], float (&x)[8]) {
+  if constexpr (S == Source::Moe) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = fmaf(g, t[e], kFirst ? 0.0f : x[e]);
+  } else if constexpr (kFirst) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = t[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += t[e];
+  }
+}
+
 template <Source S, int VPT, bool kFirst>
 __device__ __forceinline__ void fold_source(const RowSource& cur, const RowSource& next, int lane,
                                             uint4 (&ring)[kWaveDepth], float (&x)[VPT][8]) {
@@ -505,16 +522,7 @@ __device__ __forceinline__ void fold_source(const RowSource& cur, const RowSourc
     bf16x8_to_f32(ring[v % kWaveDepth], t);
     ring[v % kWaveDepth] = v + kWaveDepth < VPT ? load16(cur.r, (lane + (v + kWaveDepth) * kWave) * 16)
                                                 : load16(next.r, (lane + (v + kWaveDepth - VPT) * kWave) * 16);
-    if constexpr (S == Source::Moe) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[v][e] = fmaf(cur.g, t[e], kFirst ? 0.0f : x[v][e]);
-    } else if constexpr (kFirst) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[v][e] = t[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[v][e] += t[e];
-    }
+    add_source<S, kFirst>(cur.g, t, x[v]);
     pin8(x[v]);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -613,6 +621,84 @@ __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// complete_only, add_to_output and snapshot with one wavefront per row: the
+// pipeline of wave_read_kernel over the P partials or k picks, then the tail:
+// nothing, the extra row (add_to_output) or the residual (snapshot); the last
+// source's pass stores each finished vector at once. The sums run in
+// complete_kernel's order, including the zero that stands for the residual
+// when nothing is folded (0 + s turns a -0 sum into +0), so the output is
+// bitwise the same under both kernels.
+// ---------------------------------------------------------------------------
+
+// Source p of a complete: p < n a partial or pick, p == n the tail row when
+// there is one; any other p is an empty row (its loads read 0).
+template <Source S, Tail kTail>
+__device__ __forceinline__ RowSource complete_source(const RowArgs& a, const RowPicks& picks, int64_t row, int p) {
+  if (p < a.nsrc || (kTail == Tail::Residual && p == a.nsrc)) return row_source<S>(a, picks, row, p);
+  const bool extra = kTail == Tail::Extra && p == a.nsrc;
+  return {row_rsrc(extra ? a.extra + row * a.ld_extra : a.res, extra ? a.H * 2 : 0), 1.0f};
+}
+
+// The last source's pass: add it and store every vector as soon as it is final.
+template <Source S, int VPT, bool kFirst, Tail kTail>
+__device__ __forceinline__ void store_source(const RowSource& cur, int lane, uint4 (&ring)[kWaveDepth],
+                                             float (&x)[VPT][8], const Rsrc& out) {
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    float t[8];
+    bf16x8_to_f32(ring[v % kWaveDepth], t);
+    if (v + kWaveDepth < VPT) ring[v % kWaveDepth] = load16(cur.r, (lane + (v + kWaveDepth) * kWave) * 16);
+    if constexpr (kTail == Tail::Extra) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[v][e] = (0.0f + x[v][e]) + t[e];
+    } else if constexpr (kTail == Tail::Residual) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[v][e] = t[e] + x[v][e];
+    } else {
+      add_source<S, kFirst>(cur.g, t, x[v]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[v][e] = 0.0f + x[v][e];
+    }
+    store16(out, (lane + v * kWave) * 16, f32_to_bf16x8(x[v]));
+    pin8(x[v]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <Source S, int VPT, Tail kTail>
+__global__ __launch_bounds__(kWave) void wave_complete_kernel(const RowArgs a) {
+  static_assert(S == Source::Partials || S == Source::Moe, "one-wave rows complete partials or MoE picks");
+  static_assert(kTail != Tail::Residual || S == Source::Partials, "a snapshot folds partials");
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int n = a.nsrc;
+  const int folded = kTail != Tail::None ? n : n - 1;  // sources before the stored one
+  const Rsrc out = row_rsrc(a.y + row * a.ld_y, a.H * 2);
+  const RowPicks picks = row_picks<S>(a, row, lane);
+
+  uint4 ring[kWaveDepth];
+  RowSource cur = complete_source<S, kTail>(a, picks, row, 0);
+  RowSource next = complete_source<S, kTail>(a, picks, row, 1);
+#pragma unroll
+  for (int v = 0; v < kWaveDepth; ++v) ring[v] = load16(cur.r, (lane + v * kWave) * 16);
+  __builtin_amdgcn_sched_barrier(0);
+
+  float x[VPT][8];
+  if (kTail == Tail::None && folded == 0) {  // one partial or pick and nothing after it
+    store_source<S, VPT, true, Tail::None>(cur, lane, ring, x, out);
+    return;
+  }
+  fold_source<S, VPT, true>(cur, next, lane, ring, x);
+  for (int p = 1; p < folded; ++p) {
+    cur = next;
+    next = complete_source<S, kTail>(a, picks, row, p + 1);
+    fold_source<S, VPT, false>(cur, next, lane, ring, x);
+  }
+  cur = next;
+  store_source<S, VPT, false, kTail>(cur, lane, ring, x, out);
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch tables
 // ---------------------------------------------------------------------------
 using KernelFn = void (*)(RowArgs);
@@ -638,5 +724,21 @@ inline hipError_t launch_kernel(KernelFn fn, const RowArgs& a, const Launch& l, 
 }
 
 inline int vpt_slot(int vpt) { return vpt == 1 ? 0 : vpt == 2 ? 1 : vpt == 4 ? 2 : -1; }
+
+// Workgroups of a one-wavefront kernel that a compute unit holds at once (its
+// occupancy, which its VGPR count sets), asked of the runtime once and kept in
+// `cache` (0: not asked yet, -1: the runtime could not tell; returns 0 then).
+inline int occupancy_rows(KernelFn fn, std::atomic<int>& cache) {
+  int n = cache.load();
+  if (n == 0) {
+    int blocks = 0;
+    n = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(fn), kWave, 0) ==
+                    hipSuccess && blocks > 0
+            ? blocks
+            : -1;
+    cache.store(n);
+  }
+  return n > 0 ? n : 0;
+}
 
 }  // namespace bnd

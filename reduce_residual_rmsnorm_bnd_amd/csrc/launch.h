@@ -48,14 +48,18 @@ struct RowArgs {
 };
 
 struct Launch {
-  int rows;     // grid size
-  int threads;  // workgroup size, multiple of 64
-  int vpt;      // 16-byte vectors per thread: 1, 2 or 4; 8 or 14 = one wavefront per row (threads = 64)
+  int rows = 0;     // grid size
+  int threads = 0;  // workgroup size, multiple of 64
+  int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; 8 or 14 = one wavefront per row (threads = 64)
   hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
   hipEvent_t stop = nullptr;
 };
 
 enum class Source { Partials, Moe, Input, Residual };
+
+// What a complete adds after the owed partials or picks: nothing
+// (complete_only), the extra row (add_to_output) or the residual (snapshot).
+enum class Tail { None, Extra, Residual };
 
 // fold_norm / fold_norm_quant_fp8 / moe_finalize_fold_norm / enter / written read.
 // n = number of sources (partials P or MoE picks k), ignored for Input/Residual.
@@ -66,5 +70,12 @@ hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Laun
 // With fold, y <- bf16(residual + sum) (snapshot); Residual with n = 0 copies the residual.
 hipError_t launch_complete(Source src, int n, bool fold, const RowArgs& a, const Launch& l,
                            hipStream_t stream);
+
+// Rows of one launch that a compute unit of the current device holds at once
+// with the one-wavefront read or complete kernel of vpt (8 or 14) vectors per
+// lane (its occupancy in 64-thread workgroups, from the HIP runtime, read once
+// per kernel); 0 when no such kernel exists or the runtime cannot tell.
+int wave_read_rows_per_cu(Source src, bool fp8, int vpt);
+int wave_complete_rows_per_cu(Source src, Tail tail, int vpt);
 
 }  // namespace bnd

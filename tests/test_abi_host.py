@@ -63,7 +63,7 @@ def owed_out():
 
 def test_library_exports_every_declared_symbol():
     decl = re.findall(r"^BND_API\s+[\w\s\*]+?\b(bnd_\w+)\s*\(", open(HEADER).read(), flags=re.M)
-    assert len(decl) == len(set(decl)) == 24
+    assert len(decl) == len(set(decl)) == 25
     assert sorted(decl) == sorted(B.SYMBOLS)
     for name in decl:
         assert hasattr(L, name), name
@@ -416,3 +416,21 @@ def test_binding_rejects_bad_tensors_before_the_library():
     assert e.value.status == bnd.BND_ERR_NOT_STARTED
     bnd.bnd_take_output(s)
     s.destroy()
+
+
+def test_last_launch_shape_before_any_launch():
+    # a fresh thread has launched nothing: all zero; NULL pointers are allowed
+    import threading
+
+    got = {}
+
+    def probe():
+        rows, threads, vpt = ctypes.c_int64(-1), ctypes.c_int(-1), ctypes.c_int(-1)
+        got["st"] = L.bnd_last_launch_shape(ctypes.byref(rows), ctypes.byref(threads), ctypes.byref(vpt))
+        got["shape"] = (rows.value, threads.value, vpt.value)
+        got["null"] = L.bnd_last_launch_shape(None, None, None)
+
+    t = threading.Thread(target=probe)
+    t.start()
+    t.join()
+    assert got == {"st": 0, "shape": (0, 0, 0), "null": 0}

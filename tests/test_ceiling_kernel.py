@@ -19,6 +19,8 @@ def _lib():
     L.bnd_ceiling_mix_9r2w.argtypes = [ctypes.POINTER(VP), VP, VP, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, VP]
     L.bnd_ceiling_mix_9r2w.restype = ctypes.c_int
+    L.bnd_ceiling_empty.argtypes = [ctypes.c_int64, ctypes.c_int, VP]
+    L.bnd_ceiling_empty.restype = ctypes.c_int
     return L
 
 
@@ -47,6 +49,16 @@ def test_ceiling_refuses_bad_shapes():
         assert L.bnd_ceiling_mix_9r2w(*args, None) == -1, args
     src[4] = a + 2  # a misaligned source
     assert L.bnd_ceiling_mix_9r2w(src, o0, o1, 4, 4096, 4096, 512, 1, None) == -1
+    for wg, threads in ((0, 64), (1, 32), (1, 100), (1, 2048), (1 << 31, 64)):
+        assert L.bnd_ceiling_empty(wg, threads, None) == -1, (wg, threads)
+
+
+@pytest.mark.gpu
+def test_empty_kernel_launches():
+    L = _lib()
+    assert L.bnd_ceiling_empty(1, 512, torch.cuda.current_stream().cuda_stream) == 0
+    assert L.bnd_ceiling_empty(300, 64, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
 
 
 @pytest.mark.gpu

@@ -864,3 +864,178 @@ def test_wave_rows_refused_where_no_kernel(orc):
     torch.cuda.synchronize()
     res.check_guards("refused enter residual")
     y.check_guards("refused enter y")
+
+
+# ------------------------------------------------------------------ one wavefront per row: complete
+
+def _complete(d, kind, *, row_begin=0, rows=None, extra=None, moe=False, with_residual=True):
+    """complete_only / add_to_output / snapshot through the library under the current launch
+    shape; returns the guarded output and residual buffers."""
+    T, H = d["T"], d["H"]
+    rows = T - row_begin if rows is None else rows
+    res = Guarded(rows, H)
+    if with_residual:
+        res.from_host(d["residual"][row_begin:row_begin + rows])
+    out = Guarded(rows, H)
+    s = bnd.bnd_stream_create(T, H, res.view, row_begin, rows)
+    if with_residual:
+        bnd.bnd_written(s, res.view)
+    if moe:
+        E, idx, gate = _moe_device(d)
+        owed = bnd.bnd_publish_moe(s, E, idx, gate, d["k"])
+    else:
+        owed = bnd.bnd_publish_partials(s, [c.to(DEV) for c in d["partials"]])
+    before = res.view.clone()
+    if kind == "complete_only":
+        bnd.bnd_complete_only(s, owed, out.view)
+    elif kind == "add_to_output":
+        bnd.bnd_add_to_output(s, owed, extra.to(DEV), out.view)
+    else:
+        bnd.bnd_snapshot(s, owed, out.view)
+    torch.cuda.synchronize()
+    out.check_guards(f"{kind} out")
+    res.check_guards(f"{kind} residual")
+    assert torch.equal(res.view, before), f"{kind} must not touch the residual"
+    return out
+
+
+def _oracle_complete(orc, d, kind, *, row_begin=0, rows=None, extra=None, moe=False, with_residual=True):
+    T = d["T"]
+    rows = T - row_begin if rows is None else rows
+    ex = None if extra is None else bits(extra)
+    if moe:
+        c = orc.complete_moe(bits(d["expert_rows"]), d["idx"].numpy(), d["gate"].numpy(), d["k"],
+                             row_begin=row_begin, rows=rows, extra=ex)
+        return c["s_exact"], c["mag"]
+    parts = [bits(c) for c in d["partials"]]
+    if kind == "snapshot":
+        r = bits(d["residual"][row_begin:row_begin + rows]) if with_residual else None
+        c = orc.snapshot(parts, r, row_begin=row_begin, rows=rows)
+        return c["x_exact"], c["mag"]
+    c = orc.complete_partials(parts, row_begin=row_begin, rows=rows, extra=ex)
+    return c["s_exact"], c["mag"]
+
+
+WAVE_COMPLETE_SHAPES = [  # shape, T, H, P, row_begin, rows
+    (WAVE, 50, 4096, 8, 0, None),
+    (WAVE, 21, 3600, 1, 3, 15),      # one source: the stored pass is the only pass; ragged rows
+    (WAVE_WIDE, 30, 7168, 8, 0, None),
+    (WAVE_WIDE, 17, 6680, 3, 5, 9),
+]
+
+
+@pytest.mark.parametrize("shape,T,H,P,rb,rows", WAVE_COMPLETE_SHAPES)
+@pytest.mark.parametrize("kind", ["complete_only", "add_to_output", "snapshot"])
+def test_wave_complete(orc, kind, shape, T, H, P, rb, rows):
+    """The one-wavefront complete against the oracle, and bitwise against the multi-wave shape
+    (the sums run in the same order)."""
+    d = workloads.fold_inputs(400 + T + P, T, H, P)
+    extra = (workloads.to_bf16(workloads.normal_f32(400 + T, 12345, (T, H), 0.0, 0.25))
+             if kind == "add_to_output" else None)
+    what = f"one wave per row x{shape[1]} {kind} T={T} H={H} P={P} slice={rb}+{rows}"
+    print(f"\n  {what}", flush=True)
+    with forced_shape(*shape):
+        a = _complete(d, kind, row_begin=rb, rows=rows, extra=extra)
+    b = _complete(d, kind, row_begin=rb, rows=rows, extra=extra)  # the automatic shape
+    ex, mag = _oracle_complete(orc, d, kind, row_begin=rb, rows=rows, extra=extra)
+    tolerance.check_bf16(bits(a.view), ex, mag, what)
+    assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16)), f"{what}: differs from the other shape"
+
+
+@pytest.mark.parametrize("shape,H", [(WAVE, 4096), (WAVE_WIDE, 7168)], ids=["x8", "x14"])
+def test_wave_complete_moe(orc, shape, H):
+    d = workloads.moe_inputs(410, 40, H, 16, 8)
+    idx = d["idx"].clone()
+    idx[5] = -1
+    idx[77] = d["expert_rows"].shape[0]
+    d["idx"] = idx
+    extra = workloads.to_bf16(workloads.normal_f32(410, 12345, (40, H), 0.0, 0.25))
+    for kind, ex in (("complete_only", None), ("add_to_output", extra)):
+        what = f"one wave per row x{shape[1]} MoE {kind} H={H}"
+        with forced_shape(*shape):
+            a = _complete(d, kind, row_begin=4, rows=30, extra=ex, moe=True)
+        b = _complete(d, kind, row_begin=4, rows=30, extra=ex, moe=True)
+        e, mag = _oracle_complete(orc, d, kind, row_begin=4, rows=30, extra=ex, moe=True)
+        tolerance.check_bf16(bits(a.view), e, mag, what)
+        assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16)), what
+    d1 = workloads.moe_inputs(411, 6, H, 4, 1)  # one pick: the stored pass is the only pass
+    with forced_shape(*shape):
+        a = _complete(d1, "complete_only", moe=True)
+    e, mag = _oracle_complete(orc, d1, "complete_only", moe=True)
+    tolerance.check_bf16(bits(a.view), e, mag, "one wave per row MoE k=1 complete_only")
+
+
+@pytest.mark.parametrize("shape,H", [(WAVE, 4096), (WAVE_WIDE, 7168)], ids=["x8", "x14"])
+def test_wave_complete_edge_cases(orc, shape, H):
+    d = workloads.fold_inputs(412, 12, H, 4)
+    # signed zeros: sums of -0 store +0 under both shapes
+    d["partials"] = [c.clone() for c in d["partials"]]
+    for c in d["partials"]:
+        c[3].fill_(-0.0)
+    with forced_shape(*shape):
+        a = _complete(d, "complete_only")
+    b = _complete(d, "complete_only")
+    assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16))
+    assert int((a.view[3].view(torch.int16) != 0).sum()) == 0, "a sum of -0 stores +0"
+    # a snapshot of a Pending stream without a residual is bf16(s)
+    with forced_shape(*shape):
+        a = _complete(d, "snapshot", with_residual=False)
+    e, mag = _oracle_complete(orc, d, "snapshot", with_residual=False)
+    tolerance.check_bf16(bits(a.view), e, mag, "snapshot without a residual")
+    # a snapshot of a Written stream copies the residual: no one-wavefront kernel, refused
+    res = Guarded(12, H).from_host(d["residual"])
+    out = Guarded(12, H)
+    s = bnd.bnd_stream_create(12, H, res.view)
+    bnd.bnd_written(s, res.view)
+    with forced_shape(*shape):
+        with pytest.raises(bnd.BoundaryError) as e:
+            bnd.bnd_snapshot(s, bnd.BND_OWED_NONE, out.view)
+    assert e.value.status == bnd.BND_ERR_NO_PATH
+    torch.cuda.synchronize()
+    out.check_guards("refused snapshot")
+    assert int((out.view.view(torch.int16) != CANARY16).sum()) == 0, "a refused call wrote its output"
+
+
+def test_automatic_launch_shapes():
+    """The launch shapes the library picks for the benchmarked workloads on a 256-CU MI355X:
+    one wavefront per row where a launch's rows fit on the chip in one round."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("shape expectations are for 256 compute units")
+    w = torch.ones(7168, device=DEV)
+
+    def fold(T, H, P, fp8=False, kind="fold"):
+        res = torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
+        parts = [torch.zeros(T, H, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+        s = bnd.bnd_stream_create(T, H, res)
+        bnd.bnd_written(s, res)
+        owed = bnd.bnd_publish_partials(s, parts)
+        if kind == "complete_only":
+            bnd.bnd_complete_only(s, owed, torch.empty(T, H, dtype=torch.bfloat16, device=DEV))
+        elif kind == "snapshot":
+            bnd.bnd_snapshot(s, owed, torch.empty(T, H, dtype=torch.bfloat16, device=DEV))
+        elif fp8:
+            bnd.bnd_fold_norm_quant_fp8(s, owed, w[:H], 1e-6, torch.empty(T, H, dtype=torch.uint8, device=DEV),
+                                        torch.empty(T, dtype=torch.float32, device=DEV))
+        else:
+            bnd.bnd_fold_norm(s, owed, w[:H], 1e-6, torch.empty(T, H, dtype=torch.bfloat16, device=DEV))
+        torch.cuda.synchronize()
+        return bnd.last_launch_shape()
+
+    assert fold(2048, 4096, 8) == (2048, 64, 8)                   # prefill boundary
+    assert fold(2048, 7168, 8, fp8=True) == (2048, 64, 14)        # quantised boundary
+    assert fold(2048, 4096, 8, kind="complete_only") == (2048, 64, 8)
+    assert fold(2048, 7168, 8, kind="snapshot") == (2048, 64, 14)
+    assert fold(1536, 4096, 8) == (1536, 64, 8)                   # 6 rows per CU
+    assert fold(1024, 4096, 8)[2] == 1                            # too few rows per CU
+    assert fold(128, 4096, 4)[2] == 1                             # a decode boundary
+    d = workloads.moe_inputs(5, 2048, 4096, 16, 8)
+    E, idx, gate = _moe_device(d)
+    for rb, rows, shape in ((0, 2048, (2048, 64, 8)), (768, 256, (256, 512, 1))):
+        res = torch.zeros(rows, 4096, dtype=torch.bfloat16, device=DEV)
+        s = bnd.bnd_stream_create(2048, 4096, res, rb, rows)
+        bnd.bnd_written(s, res)
+        owed = bnd.bnd_publish_moe(s, E, idx, gate, 8)
+        bnd.bnd_moe_finalize_fold_norm(s, owed, w[:4096], 1e-6, torch.empty(rows, 4096, dtype=torch.bfloat16,
+                                                                             device=DEV))
+        torch.cuda.synchronize()
+        assert bnd.last_launch_shape() == shape, (rb, rows)

@@ -28,6 +28,8 @@ hipError_t launch_read(Source, int, bool, const RowArgs&, const Launch&, hipStre
 hipError_t launch_complete(Source, int, bool, const RowArgs&, const Launch&, hipStream_t) {
   return hipSuccess;
 }
+int wave_read_rows_per_cu(Source, bool, int vpt) { return vpt == 8 ? 12 : 8; }
+int wave_complete_rows_per_cu(Source, Tail, int vpt) { return vpt == 8 ? 16 : 8; }
 }  // namespace bnd
 """
 

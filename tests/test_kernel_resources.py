@@ -6,9 +6,10 @@ occupancy, so the fold and read kernels with one or two vectors per thread and u
 partial sources must stay within 64 VGPRs and never use scratch. A data-dependent branch around
 the Gemma weight offset once pushed the P = 8 fold to 100 VGPRs (half the resident rows, about
 a microsecond on the prefill boundary); this test fails on such a change before it reaches a
-benchmark. The one-wavefront-per-row read (8 or 14 vectors per lane, the source count a runtime
-argument) is chosen only while a launch's rows fit on the chip in one round at two waves per
-SIMD, so it must stay within 256 VGPRs, also without scratch.
+benchmark. The one-wavefront-per-row read and complete kernels (8 or 14 vectors per lane, the
+source count a runtime argument) are chosen only while a launch's rows fit on the chip in one
+round, counted from their occupancy; they must keep at least two waves per SIMD (at most 256
+VGPRs), also without scratch.
 """
 import os
 import re
@@ -27,6 +28,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, 
 
 NAME = re.compile(r"Function Name: _ZN3bnd11read_kernelILNS_6SourceE(\d)ELi(\d+)ELi(\d)ELb([01])E")
 WAVE_NAME = re.compile(r"Function Name: _ZN3bnd16wave_read_kernelILNS_6SourceE(\d)ELi(\d+)ELb([01])E")
+WAVE_COMPLETE_NAME = re.compile(r"Function Name: _ZN3bnd20wave_complete_kernelILNS_6SourceE(\d)ELi(\d+)ELNS_4TailE(\d)E")
+ANY_NAME = re.compile(r"Function Name: ")
+TAILS = {0: "None", 1: "Extra", 2: "Residual"}
 FIELD = re.compile(r"remark: +(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)")
 SOURCES = {0: "Partials", 1: "Moe", 2: "Input", 3: "Residual"}
 
@@ -50,6 +54,15 @@ def _resources(tmp_path, files):
                 current = ("Wave" + SOURCES[int(m.group(1))], 0, int(m.group(2)), m.group(3) == "1")
                 table[current] = {}
                 continue
+            m = WAVE_COMPLETE_NAME.search(line)
+            if m:  # one-wavefront complete: (kind, tail, vectors per lane, False)
+                current = ("WaveComplete" + SOURCES[int(m.group(1))], TAILS[int(m.group(3))], int(m.group(2)),
+                           False)
+                table[current] = {}
+                continue
+            if ANY_NAME.search(line):  # a kernel this test does not track
+                current = None
+                continue
             m = FIELD.search(line)
             if m and current is not None and m.group(1) not in table[current]:
                 table[current][m.group(1)] = int(m.group(2))
@@ -60,7 +73,7 @@ def _resources(tmp_path, files):
 def resources(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not installed")
-    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip", "k_wave.hip"])
+    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip", "k_wave.hip", "k_complete.hip"])
 
 
 def test_every_instance_reported(resources):
@@ -68,9 +81,17 @@ def test_every_instance_reported(resources):
     assert sum(1 for k in resources if k[0] == "Partials") == 96
     assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
     # one wavefront per row: partials bf16 and fp8, MoE bf16, at 8 and 14 vectors per lane
-    waves = sorted((k[0], k[2], k[3]) for k in resources if k[0].startswith("Wave"))
+    waves = sorted((k[0], k[2], k[3]) for k in resources if k[0] in ("WavePartials", "WaveMoe"))
     assert waves == sorted((kind, vpt, fp8) for vpt in (8, 14)
                            for kind, fp8 in (("WavePartials", False), ("WavePartials", True), ("WaveMoe", False))), waves
+
+
+def test_one_wave_completes_reported(resources):
+    # partials with no tail, the extra row or the residual; MoE picks with no tail or the extra row
+    got = sorted((k[0], k[1], k[2]) for k in resources if k[0].startswith("WaveComplete"))
+    assert got == sorted((kind, tail, vpt) for vpt in (8, 14) for kind, tail in (
+        ("WaveCompletePartials", "None"), ("WaveCompletePartials", "Extra"), ("WaveCompletePartials", "Residual"),
+        ("WaveCompleteMoe", "None"), ("WaveCompleteMoe", "Extra"))), got
 
 
 def test_one_wave_rows_keep_two_waves_per_simd(resources):
