@@ -19,6 +19,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -203,6 +204,27 @@ WaveFit wave_fit_read(bnd::Source src, bool fp8) {
 WaveFit wave_fit_complete(bnd::Source src, bnd::Tail tail) {
   return {true, bnd::wave_complete_rows_per_cu(src, tail, bnd::kWaveVpt),
           bnd::wave_complete_rows_per_cu(src, tail, bnd::kWaveVptWide)};
+}
+
+// The device queries the launch heuristic needs (CU count, the one-wavefront
+// kernels' occupancy), made once per process when the first stream is created,
+// so that no hot call asks the runtime anything but to launch (a hot call may
+// run under HIP graph capture).
+void warm_launch_queries() {
+  static std::once_flag once;
+  std::call_once(once, [] {
+    compute_units();
+    for (int w : {bnd::kWaveVpt, bnd::kWaveVptWide}) {
+      for (bool fp8 : {false, true}) {
+        bnd::wave_read_rows_per_cu(Source::Partials, fp8, w);
+        bnd::wave_read_rows_per_cu(Source::Moe, fp8, w);
+      }
+      for (bnd::Tail t : {bnd::Tail::None, bnd::Tail::Extra, bnd::Tail::Residual}) {
+        bnd::wave_complete_rows_per_cu(Source::Partials, t, w);
+        bnd::wave_complete_rows_per_cu(Source::Moe, t, w);
+      }
+    }
+  });
 }
 
 bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l) {
@@ -425,6 +447,7 @@ bnd_status bnd_stream_create(bnd_stream** out, int64_t T, int64_t H, int64_t row
   bnd_status st = check_hidden(H);
   if (st) return st;
   if ((st = check_rows_tensor("residual", residual, ld_res, H, rows > 0))) return st;
+  warm_launch_queries();
   bnd_stream* s = new (std::nothrow) bnd_stream;
   if (!s) return fail(BND_ERR_INVALID_ARG, "out of host memory");
   memset(s, 0, sizeof *s);
