@@ -507,6 +507,46 @@ def stream_ceiling(torch, T: int, H: int, fold_us: float):
             "fold_back_to_back_us": fold_us, "fold_time_over_ceiling_time": fold_us / shapes[best]}
 
 
+def gather_ceiling(torch, dm, moe_us: float):
+    """The gathering 9:2 stream (libboundary_ceiling.so: eight rows read through the MoE
+    workload's own index, the ninth by row, two rows written, no arithmetic) over rotating copies
+    of the expert rows, beside the MoE finalize timed the same way."""
+    from reduce_residual_rmsnorm_bnd_amd import _build
+
+    L = ctypes.CDLL(_build.CEILING_LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.bnd_ceiling_gather_9r2w.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int,
+                                          ctypes.c_int, vp]
+    T, H, k = dm["T"], dm["H"], dm["k"]
+    if k != 8:
+        raise ValueError("the gathering stream reads eight rows")
+    E0 = dm["expert_rows"].to("cuda:0")
+    idx = dm["idx"].to("cuda:0")
+    nbytes = 11 * T * H * 2
+    n_sets = max(2, -(-ROTATE_BYTES // nbytes))
+    sets = []
+    for s_i in range(n_sets):
+        E = E0 if s_i == 0 else E0.clone()
+        bufs = [torch.zeros(T, H, dtype=torch.bfloat16, device="cuda:0") for _ in range(3)]
+        sets.append((E, bufs))
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    shapes = {}
+    for threads, vpt in ((64, 8), (256, 2), (512, 1)):
+        def launch(i, threads=threads, vpt=vpt):
+            E, (s8, o0, o1) = sets[i]
+            rc = L.bnd_ceiling_gather_9r2w(vp(E.data_ptr()), E.shape[0], vp(idx.data_ptr()), vp(s8.data_ptr()),
+                                           vp(o0.data_ptr()), vp(o1.data_ptr()), T, H, H, threads, vpt, stream)
+            if rc:
+                raise RuntimeError(f"gather ceiling launch failed: {rc}")
+        shapes[f"{threads}x{vpt}"] = back_to_back_us(torch, launch, n_sets)
+    best = min(shapes, key=shapes.get)
+    del sets, E0
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us_per_launch_by_shape": shapes, "best_shape": best,
+            "GBps": nbytes / shapes[best] / 1e3, "frac": nbytes / shapes[best] / 1e3 / PEAK_HBM_GBPS,
+            "moe_back_to_back_us": moe_us, "moe_time_over_ceiling_time": moe_us / shapes[best]}
+
+
 def device_memory_info():
     """Memory clock and bus width as the HIP runtime reports them, and the peak they imply."""
     hip = ctypes.CDLL("libamdhip64.so.7")
@@ -696,6 +736,7 @@ def main():
         log("MoE finalize (T=2048 H=4096 k=8), full rows and rows 768..1023")
         dm = workloads.moe()
         n_m = max(2, -(-ROTATE_BYTES // (dm["T"] * (dm["k"] + 3) * dm["H"] * 2)))
+        moe_us = None
         for name, rb, rows, tg in (("moe_full_T2048_H4096_k8", 0, 2048, False),
                                    ("moe_slice_rows768_1023", *workloads.MOE_SLICE, False),
                                    ("moe_terminal_gemma_T2048_H4096_k8", 0, 2048, True)):
@@ -705,7 +746,12 @@ def main():
                          "GBps": nb / tm["kernel_s"] / 1e9,
                          "frac": nb / tm["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                          "algorithmic_bytes": nb}
+            if name == "moe_full_T2048_H4096_k8":
+                moe_us = back_to_back_us(torch, lambda i: step(i, None, None), n_m)
             del keep, step
+        torch.cuda.empty_cache()
+        log("gathering 9:2 streaming ceiling (the MoE finalize's loads and stores without arithmetic)")
+        sec["gather_ceiling_9r2w_T2048_H4096_k8"] = gather_ceiling(torch, dm, moe_us)
         del dm
         torch.cuda.empty_cache()
         log("complete_only, snapshot and add_to_output (prefill sizes), the unfused fallback, "

@@ -21,6 +21,9 @@ def _lib():
     L.bnd_ceiling_mix_9r2w.restype = ctypes.c_int
     L.bnd_ceiling_empty.argtypes = [ctypes.c_int64, ctypes.c_int, VP]
     L.bnd_ceiling_empty.restype = ctypes.c_int
+    L.bnd_ceiling_gather_9r2w.argtypes = [VP, ctypes.c_int64, VP, VP, VP, VP, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int, VP]
+    L.bnd_ceiling_gather_9r2w.restype = ctypes.c_int
     return L
 
 
@@ -51,6 +54,18 @@ def test_ceiling_refuses_bad_shapes():
     assert L.bnd_ceiling_mix_9r2w(src, o0, o1, 4, 4096, 4096, 512, 1, None) == -1
     for wg, threads in ((0, 64), (1, 32), (1, 100), (1, 2048), (1 << 31, 64)):
         assert L.bnd_ceiling_empty(wg, threads, None) == -1, (wg, threads)
+    E, idx, s8 = VP(a), VP(a + (30 << 24)), VP(a + (31 << 24))
+    bad_gather = [
+        (None, 64, idx, s8, o0, o1, 4, 4096, 4096, 64, 8),    # no source rows
+        (E, 0, idx, s8, o0, o1, 4, 4096, 4096, 64, 8),        # empty source rows
+        (E, 64, None, s8, o0, o1, 4, 4096, 4096, 64, 8),      # no index
+        (E, 64, VP(a + 2), s8, o0, o1, 4, 4096, 4096, 64, 8),  # misaligned index
+        (E, 64, idx, VP(a + 8), o0, o1, 4, 4096, 4096, 64, 8),  # misaligned ninth source
+        (E, 64, idx, s8, o0, o1, 0, 4096, 4096, 64, 8),       # no rows
+        (E, 64, idx, s8, o0, o1, 4, 4096, 4096, 64, 4),       # 64 x 4 x 8 < 4096
+    ]
+    for args in bad_gather:
+        assert L.bnd_ceiling_gather_9r2w(*args, None) == -1, args
 
 
 @pytest.mark.gpu
@@ -84,3 +99,32 @@ def test_ceiling_streams_the_xor(rows, H, ld, threads, vpt):
         o = o.cpu()
         assert torch.equal(o[:, :H], expect[:, :H])
         assert bool((o[:, H:] == 7).all())
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,H,threads,vpt", [(37, 4096, 64, 8), (5, 1000, 128, 1), (9, 4096, 256, 2)])
+def test_gather_streams_the_xor(rows, H, threads, vpt):
+    L = _lib()
+    g = torch.Generator().manual_seed(rows + vpt)
+    n_src = 3 * rows
+    E = torch.randint(-32768, 32768, (n_src, H), dtype=torch.int16, generator=g)
+    s8 = torch.randint(-32768, 32768, (rows, H), dtype=torch.int16, generator=g)
+    idx = torch.randint(0, n_src, (rows * 8,), dtype=torch.int32, generator=g)
+    idx[3] = -1          # outside the rows: reads zeros
+    idx[11] = n_src
+    dE, ds8, didx = E.to("cuda:0"), s8.to("cuda:0"), idx.to("cuda:0")
+    out = [torch.full((rows, H), 7, dtype=torch.int16, device="cuda:0") for _ in range(2)]
+    print(f"\n  gather ceiling rows={rows} H={H} {threads}x{vpt}", flush=True)
+    rc = L.bnd_ceiling_gather_9r2w(dE.data_ptr(), n_src, didx.data_ptr(), ds8.data_ptr(), out[0].data_ptr(),
+                                   out[1].data_ptr(), rows, H, H, threads, vpt,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    expect = s8.clone()
+    for t in range(rows):
+        for j in range(8):
+            e = int(idx[t * 8 + j])
+            if 0 <= e < n_src:
+                expect[t] ^= E[e]
+    for o in out:
+        assert torch.equal(o.cpu(), expect)
