@@ -25,8 +25,9 @@
  *     captured into a HIP graph. A bnd_stream is a small host object.
  *   - bf16 tensors are row-major [rows, H] with a leading dimension `ld` in
  *     elements: row t starts at base + t*ld. Bases must be 16-byte aligned
- *     and ld a multiple of 8 with ld >= H. H must be a multiple of 8 in
- *     [8, BND_MAX_HIDDEN]. Weights are fp32 [H], 16-byte aligned.
+ *     and ld a multiple of 8 with H <= ld <= BND_MAX_LD. H must be a
+ *     multiple of 8 in [8, BND_MAX_HIDDEN]. Weights are fp32 [H], 16-byte
+ *     aligned. T and the MoE expert-row count are at most BND_MAX_ROWS.
  *   - Reduced inputs (partials, expert index, gates) are indexed by GLOBAL
  *     token row 0..T-1. The residual and every output (y, q, scale, out,
  *     x of enter) are indexed by SLICE row: global row row_begin + i lives at
@@ -64,8 +65,10 @@
 extern "C" {
 #endif
 
-#define BND_MAX_SOURCES 16   /* partials P and MoE picks k: 1..16 */
-#define BND_MAX_HIDDEN 32768 /* H: multiple of 8 in [8, 32768] */
+#define BND_MAX_SOURCES 16        /* partials P and MoE picks k: 1..16 */
+#define BND_MAX_HIDDEN 32768      /* H: multiple of 8 in [8, 32768] */
+#define BND_MAX_ROWS 2147483647   /* T and expert rows: one launch grid, the int32 index range */
+#define BND_MAX_LD 2147483647     /* leading dimensions, in elements */
 
 /* Stream states, guide section "Residual stream" (state table). */
 typedef enum bnd_state {
@@ -121,7 +124,7 @@ typedef uint64_t bnd_owed;
  * chosen from; no later call queries the device, so every hot call may run
  * under HIP graph capture.
  * Errors: INVALID_ARG (out == NULL, T < 0, bad slice, residual NULL with
- * rows > 0, misaligned, ld_res), NO_PATH (H). */
+ * rows > 0, misaligned, ld_res), NO_PATH (H, T > BND_MAX_ROWS). */
 BND_API bnd_status bnd_stream_create(bnd_stream** out, int64_t T, int64_t H, int64_t row_begin,
                              int64_t rows, void* residual, int64_t ld_res);
 

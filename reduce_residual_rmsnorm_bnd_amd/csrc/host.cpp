@@ -103,11 +103,12 @@ struct Range {
   uintptr_t lo = 0, hi = 0;
 };
 
+// Unsigned arithmetic: with rows, ld <= 2^31 - 1 and elem <= 4 the extent stays below 2^64.
 Range rows_range(const void* base, int64_t rows, int64_t ld, int64_t width, int64_t elem) {
   Range r;
   if (!base || rows <= 0 || width <= 0) return r;
   r.lo = reinterpret_cast<uintptr_t>(base);
-  r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + width) * elem);
+  r.hi = r.lo + ((uintptr_t)(rows - 1) * (uintptr_t)ld + (uintptr_t)width) * (uintptr_t)elem;
   return r;
 }
 
@@ -127,9 +128,9 @@ bnd_status check_rows_tensor(const char* what, const void* p, int64_t ld, int64_
   if (!needed) return BND_OK;
   if (!p) return fail(BND_ERR_INVALID_ARG, "%s is NULL", what);
   if (!aligned(p, 16)) return fail(BND_ERR_INVALID_ARG, "%s is not 16-byte aligned", what);
-  if (ld < H || ld % 8 != 0)
-    return fail(BND_ERR_INVALID_ARG, "%s leading dimension %lld: need a multiple of 8, >= H = %lld",
-                what, (long long)ld, (long long)H);
+  if (ld < H || ld % 8 != 0 || ld > BND_MAX_LD)
+    return fail(BND_ERR_INVALID_ARG, "%s leading dimension %lld: need a multiple of 8 in [H = %lld, %lld]",
+                what, (long long)ld, (long long)H, (long long)BND_MAX_LD);
   return BND_OK;
 }
 
@@ -441,9 +442,11 @@ bnd_status bnd_stream_create(bnd_stream** out, int64_t T, int64_t H, int64_t row
                              void* residual, int64_t ld_res) {
   if (!out) return fail(BND_ERR_INVALID_ARG, "out is NULL");
   if (T < 0) return fail(BND_ERR_INVALID_ARG, "T = %lld < 0", (long long)T);
-  if (row_begin < 0 || rows < 0 || row_begin + rows > T)
-    return fail(BND_ERR_INVALID_ARG, "slice [%lld, %lld) is not inside [0, %lld)", (long long)row_begin,
-                (long long)(row_begin + rows), (long long)T);
+  if (T > BND_MAX_ROWS) return fail(BND_ERR_NO_PATH, "T = %lld: at most %lld token rows", (long long)T,
+                                    (long long)BND_MAX_ROWS);
+  if (row_begin < 0 || rows < 0 || row_begin > T || rows > T - row_begin)
+    return fail(BND_ERR_INVALID_ARG, "slice of %lld rows from %lld is not inside [0, %lld)", (long long)rows,
+                (long long)row_begin, (long long)T);
   bnd_status st = check_hidden(H);
   if (st) return st;
   if ((st = check_rows_tensor("residual", residual, ld_res, H, rows > 0))) return st;
@@ -518,7 +521,9 @@ bnd_status bnd_publish_moe(bnd_stream* s, const void* expert_rows, int64_t n_row
   if (!owed) return fail(BND_ERR_INVALID_ARG, "owed is NULL");
   if (s->state == BND_PENDING) return fail(BND_ERR_PENDING, "a contribution is already pending; fold it first");
   if (k < 1 || k > BND_MAX_SOURCES) return fail(BND_ERR_NO_PATH, "k = %d: need 1..%d picks", k, BND_MAX_SOURCES);
-  if (n_rows < 0) return fail(BND_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows < 0 || n_rows > BND_MAX_ROWS)
+    return fail(BND_ERR_INVALID_ARG, "n_rows = %lld: need 0..%lld (int32 row indices)", (long long)n_rows,
+                (long long)BND_MAX_ROWS);
   if (s->rows > 0) {
     bnd_status st = check_rows_tensor("expert rows", expert_rows, ld, s->H, n_rows > 0);
     if (st) return st;
@@ -592,7 +597,8 @@ static bnd_status fold_read(bnd_stream* s, bnd_owed owed, bnd_kind kind, bool fp
   if (fp8) {
     if (any) {
       if (!q || !aligned(q, 8)) return fail(BND_ERR_INVALID_ARG, "q is NULL or not 8-byte aligned");
-      if (ld_q < s->H || ld_q % 8 != 0) return fail(BND_ERR_INVALID_ARG, "ld_q: need a multiple of 8, >= H");
+      if (ld_q < s->H || ld_q % 8 != 0 || ld_q > BND_MAX_LD)
+        return fail(BND_ERR_INVALID_ARG, "ld_q: need a multiple of 8 in [H, BND_MAX_LD]");
       if (!scale || !aligned(scale, 4)) return fail(BND_ERR_INVALID_ARG, "scale is NULL or misaligned");
     }
     outs[n_out++] = rows_range(q, s->rows, ld_q, s->H, 1);

@@ -434,3 +434,28 @@ def test_last_launch_shape_before_any_launch():
     t.start()
     t.join()
     assert got == {"st": 0, "shape": (0, 0, 0), "null": 0}
+
+
+def test_size_limits_without_overflow():
+    """Rows, slices and leading dimensions at and past their limits are refused before any
+    arithmetic on them can overflow (the sanitizer build runs this too)."""
+    h = VP()
+    big = 2**62
+    max_rows = 2**31 - 1
+    assert L.bnd_stream_create(ctypes.byref(h), 2**31, H, 0, 0, None, H) == B.BND_ERR_NO_PATH
+    assert L.bnd_stream_create(ctypes.byref(h), 2**63 - 1, H, big, big, fake(), H) == B.BND_ERR_NO_PATH
+    assert L.bnd_stream_create(ctypes.byref(h), max_rows, H, big, big, fake(), H) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_stream_create(ctypes.byref(h), max_rows, H, max_rows, 1, fake(), H) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_stream_create(ctypes.byref(h), 8, H, 0, 8, fake(), 2**31) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_stream_create(ctypes.byref(h), 8, H, 0, 8, fake(), 2**31 - 8) == B.BND_OK
+    L.bnd_stream_destroy(h)
+    # the largest stream: a full slice of 2^31 - 1 rows at the largest leading dimension
+    assert L.bnd_stream_create(ctypes.byref(h), max_rows, H, 0, max_rows, fake(), 2**31 - 8) == B.BND_OK
+    assert L.bnd_written(h, fake(), 2**31 - 8) == B.BND_OK
+    o = owed_out()
+    arr = (VP * 2)(fake(1 << 44), fake(2 << 44))
+    assert L.bnd_publish_partials(h, arr, 2, 2**31, ctypes.byref(o)) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_publish_moe(h, fake(1 << 44), 2**31, H, fake(3 << 44), fake(4 << 44), 8,
+                             ctypes.byref(o)) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_stream_state(h) == B.BND_WRITTEN
+    L.bnd_stream_destroy(h)
