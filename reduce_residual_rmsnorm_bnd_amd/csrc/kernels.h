@@ -26,6 +26,7 @@
 
 #include <array>
 #include <atomic>
+#include <type_traits>
 #include <utility>
 
 #include "launch.h"
@@ -103,6 +104,20 @@ __device__ __forceinline__ uint2 f32_to_e4m3x8(const float f[8]) {
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
+
+// The e4m3 inputs of eight y values of a row: y / scale, clamped to +-448.
+// `rcp` is 1 / scale, and multiplying by it stands in for the division (one
+// reciprocal per row); a zero scale (a zero row) has rcp = 0 and gives +0
+// codes. A scale below 2^-128, which only a row of tiny (subnormal) weights
+// reaches, has no finite reciprocal: such a row takes kDivide, since y * inf
+// would give +-448 for small y and NaN for y = 0.
+template <bool kDivide>
+__device__ __forceinline__ void fp8_inputs(const float (&y)[8], float scale, float rcp, float (&t)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = fminf(fmaxf(kDivide ? y[e] / scale : y[e] * rcp, -448.0f), 448.0f);
+}
+
+__device__ __forceinline__ bool fp8_divide(float rcp) { return !(rcp <= 3.40282347e38f); }
 
 // ---------------------------------------------------------------------------
 // wave64 reductions (DPP). Lanes are in four rows of 16: a butterfly inside
@@ -361,19 +376,22 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
     // (max_h |x_h w_h|) inv: the scale is fp32(max|y| / 448) of these y.
     const float amax = mx * inv;
     const float scale = amax / 448.0f;
-    // one reciprocal per row and a multiply per element, as in wave_read_kernel
     const float rcp = scale > 0.0f ? 1.0f / scale : 0.0f;
     const Rsrc qr = row_rsrc(a.q + row * a.ld_q, a.H);
+    const auto codes = [&](auto divide) {
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      float t[8];
+      for (int v = 0; v < VPT; ++v) {
+        float y[8], t[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y = (x[v][e] * w[v][e]) * inv;
-        t[e] = fminf(fmaxf(y * rcp, -448.0f), 448.0f);
+        for (int e = 0; e < 8; ++e) y[e] = (x[v][e] * w[v][e]) * inv;
+        fp8_inputs<decltype(divide)::value>(y, scale, rcp, t);
+        if (ok[v]) store8(qr, (tid + v * nthr) * 8, f32_to_e4m3x8(t));
       }
-      if (ok[v]) store8(qr, (tid + v * nthr) * 8, f32_to_e4m3x8(t));
-    }
+    };
+    if (fp8_divide(rcp))  // uniform across the row
+      codes(std::true_type{});
+    else
+      codes(std::false_type{});
     if (tid == 0) a.scale[row] = scale;
   }
 }
@@ -608,14 +626,21 @@ __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
     const float scale = amax / 448.0f;
     const float rcp = scale > 0.0f ? 1.0f / scale : 0.0f;
     const Rsrc qr = row_rsrc(a.q + row * a.ld_q, a.H);
+    const auto codes = [&](auto divide) {
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      float t[8];
+      for (int v = 0; v < VPT; ++v) {
+        float y[8], t[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = fminf(fmaxf((x[v][e] * inv) * rcp, -448.0f), 448.0f);
-      store8(qr, (lane + v * kWave) * 8, f32_to_e4m3x8(t));
-      __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int e = 0; e < 8; ++e) y[e] = x[v][e] * inv;
+        fp8_inputs<decltype(divide)::value>(y, scale, rcp, t);
+        store8(qr, (lane + v * kWave) * 8, f32_to_e4m3x8(t));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (fp8_divide(rcp))  // uniform across the row
+      codes(std::true_type{});
+    else
+      codes(std::false_type{});
     if (lane == 0) a.scale[row] = scale;
   }
 }

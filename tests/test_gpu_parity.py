@@ -1039,3 +1039,26 @@ def test_automatic_launch_shapes():
                                                                              device=DEV))
         torch.cuda.synchronize()
         assert bnd.last_launch_shape() == shape, (rb, rows)
+
+
+@pytest.mark.parametrize("shape", [(512, 2), (576, 1), (64, 14)], ids=["512x2", "576x1", "wave"])
+def test_fp8_subnormal_scale(orc, shape):
+    """A row whose scale is subnormal has no finite reciprocal; the kernels divide by such a
+    scale instead of multiplying by 1/scale, which would give +-448 codes for every nonzero y
+    and NaN (a -448 code) for zeros. Rows of 1, 0.5 and 0 with random signs, weights 2^-130
+    and eps = 0 put the scale near 1800 * 2^-149; the oracle fixes the codes."""
+    T, H, P = 6, 4104, 2
+    d = workloads.fold_inputs(500, T, H, P)
+    sign = torch.where(d["residual"] >= 0, 1.0, -1.0)
+    mag = torch.tensor([1.0, 0.5, 0.0]).repeat(H // 3)
+    d["residual"] = (sign * mag).to(torch.bfloat16)
+    d["partials"] = [torch.zeros_like(c) for c in d["partials"]]
+    d["weight"] = torch.full((H,), 2.0 ** -130, dtype=torch.float32)
+    d["eps"] = 0.0
+    assert float(d["weight"][0]) == 2.0 ** -130, "the host keeps the subnormal weight"
+    with forced_shape(*shape):
+        got, ref = assert_fold_matches(orc, d, f"subnormal scale {shape[0]}x{shape[1]}", fp8=True)
+    assert np.all(ref["scale"] > 0) and np.all(ref["scale"] < np.float32(2.0 ** -126)), "scales are subnormal"
+    q = got["q"].view.cpu().numpy()
+    assert np.all(q[:, 2::3] == 0), "a zero element must give code +0"
+    assert np.all(q[:, 1::3] & 0x7F != 0x7E), "half-size elements must not saturate"
