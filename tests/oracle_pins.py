@@ -180,9 +180,13 @@ def pin_bruteforce_fold(o):
 
 def pin_bruteforce_fp8(o):
     eps = 1e-6
-    for seed, T, H, P in [(21, 3, 16, 2), (22, 2, 8, 3), (23, 4, 16, 1)]:
+    for seed, T, H, P in [(21, 3, 16, 2), (22, 2, 8, 3), (23, 4, 16, 1), (24, 3, 16, 2)]:
         parts, res, w = _tiny_fold_case(seed, T, H, P, wide=(seed == 22))
+        if seed == 24:  # subnormal weights: the scale is subnormal too (below 2^-128)
+            w = (w * np.float32(2.0 ** -130)).astype(np.float32)
         out = o.fold_norm(parts, res, w, eps, fp8=True)
+        if seed == 24:
+            assert np.all((out["scale"] > 0) & (out["scale"] < np.float32(2.0 ** -128))), out["scale"]
         for i in range(T):
             s = _exact_contrib_partials(parts, i, H)
             _, _, y = exact.boundary_row(res[i], s, list(w), eps)
