@@ -1,0 +1,173 @@
+"""AddressSanitizer builds (host code only, g++/gcc) of the state machine and the oracle.
+
+Two standalone programs, so no sanitizer runtime has to be injected into Python:
+
+* the host state machine (host.cpp) linked with launch functions that return success without
+  launching, driven through every legal transition with non-empty slices and fake,
+  never-dereferenced device addresses, plus the refused calls;
+* the oracle (oracle.c) on small rows held in heap buffers of exactly the sizes its callers
+  pass, so any read or write past an operand is reported.
+
+Both abort on the first report (and on undefined behaviour).
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "reduce_residual_rmsnorm_bnd_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+ORACLE_SRC = os.path.join(ROOT, "oracle", "oracle.c")
+SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g", "-O1"]
+ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1", UBSAN_OPTIONS="halt_on_error=1")
+
+pytestmark = pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not installed")
+
+HOST_DRIVER = r"""
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdint.h>
+#include "boundary.h"
+#include "launch.h"
+
+namespace bnd {
+hipError_t launch_read(Source, int, bool, const RowArgs&, const Launch&, hipStream_t) { return hipSuccess; }
+hipError_t launch_complete(Source, int, bool, const RowArgs&, const Launch&, hipStream_t) { return hipSuccess; }
+int wave_read_rows_per_cu(Source, bool, int vpt) { return vpt == 8 ? 12 : 8; }
+int wave_complete_rows_per_cu(Source, Tail, int vpt) { return vpt == 8 ? 16 : 8; }
+}  // namespace bnd
+
+static int fails = 0;
+#define EXPECT(c) do { if (!(c)) { printf("line %d: %s: %s\n", __LINE__, #c, bnd_last_error()); ++fails; } } while (0)
+static void* fake(uint64_t k) { return (void*)(uintptr_t)(0x7F0000000000ull + (k << 36)); }
+
+int main() {
+  const int64_t H = 4096;
+  bnd_owed o = BND_OWED_NONE, o2 = BND_OWED_NONE;
+  const void* parts[8];
+  for (int p = 0; p < 8; ++p) parts[p] = fake(4 + p);
+  for (int64_t rows : {0, 1, 300, 2048}) {
+    bnd_stream* s = nullptr;
+    EXPECT(bnd_stream_create(&s, 4096, H, 0, rows, fake(0), H) == BND_OK);
+    EXPECT(bnd_fold_norm(s, BND_OWED_NONE, (const float*)fake(1), 1e-6f, fake(2), H, nullptr) == BND_ERR_NOT_STARTED);
+    EXPECT(bnd_enter_norm(s, fake(3), H, (const float*)fake(1), 1e-6f, fake(2), H, nullptr) == BND_OK);
+    EXPECT(bnd_publish_partials(s, parts, 8, H, &o) == BND_OK);
+    EXPECT(bnd_take_output(s) == BND_ERR_PENDING);
+    EXPECT(bnd_snapshot(s, o, fake(20), H, nullptr) == BND_OK);
+    EXPECT(bnd_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr) == BND_OK);
+    EXPECT(bnd_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr) == BND_ERR_FOREIGN_OUTPUT);
+    EXPECT(bnd_publish_partials(s, parts, 8, H, &o) == BND_OK);
+    EXPECT(bnd_fold_norm_quant_fp8(s, o, (const float*)fake(1), 1e-6f, (uint8_t*)fake(21), H, (float*)fake(22),
+                                   nullptr) == BND_OK);
+    EXPECT(bnd_publish_partials(s, parts, 8, H, &o) == BND_OK);
+    EXPECT(bnd_add_to_output(s, o, fake(23), H, fake(24), H, &o2, nullptr) == BND_OK);
+    EXPECT(bnd_complete_only(s, o2, fake(25), H, &o, nullptr) == BND_OK);
+    EXPECT(bnd_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr) == BND_OK);
+    EXPECT(bnd_publish_moe(s, fake(26), 16384, H, (const int32_t*)fake(27), (const float*)fake(28), 8, &o) == BND_OK);
+    EXPECT(bnd_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr) == BND_ERR_WRONG_KIND);
+    EXPECT(bnd_stream_set_norm_form(s, BND_NORM_GEMMA) == BND_OK);
+    EXPECT(bnd_moe_finalize_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr) == BND_OK);
+    EXPECT(bnd_written(s, fake(0), H) == BND_OK);
+    EXPECT(bnd_take_output(s) == BND_OK);
+    EXPECT(bnd_stream_destroy(s) == BND_OK);
+  }
+  for (int64_t Hs : {8, 264, 7168, 16384, 32768}) {  // the other launch-shape branches
+    bnd_stream* s = nullptr;
+    EXPECT(bnd_stream_create(&s, 2048, Hs, 0, 2048, fake(0), Hs) == BND_OK);
+    EXPECT(bnd_publish_partials(s, parts, 8, Hs, &o) == BND_OK);
+    EXPECT(bnd_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), Hs, nullptr) == BND_OK);
+    EXPECT(bnd_stream_destroy(s) == BND_OK);
+  }
+  int64_t counts[4] = {3, 0, 5, 2}, b = 0, n = 0, t = 0;
+  EXPECT(bnd_rsv_share(counts, 4, 2, &b, &n, &t) == BND_OK && b == 3 && n == 5 && t == 10);
+  int64_t r = 0; int th = 0, v = 0;
+  EXPECT(bnd_last_launch_shape(&r, &th, &v) == BND_OK && r == 2048);
+  printf("host walk: %d failures\n", fails);
+  return fails ? 1 : 0;
+}
+"""
+
+ORACLE_DRIVER = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include "oracle.c"
+
+/* every operand in its own heap block of exactly the bytes the call may touch */
+static void* take(size_t bytes) { void* p = malloc(bytes ? bytes : 1); if (p) memset(p, 0, bytes); return p; }
+
+int main(void) {
+  const int64_t T = 5, H = 24, rows = 3, rb = 2, ld = 32;  /* padded rows: ld > H */
+  enum { P = 3, K = 2, NE = 7 };
+  uint16_t* parts[P];
+  for (int p = 0; p < P; ++p) {
+    parts[p] = take(((T - 1) * ld + H) * 2);
+    for (int64_t i = 0; i < (T - 1) * ld + H; ++i) parts[p][i] = orc_bf16_round((double)((i * 7 + p) % 13) - 6.0);
+  }
+  uint16_t* res = take(((rows - 1) * ld + H) * 2);
+  for (int64_t i = 0; i < (rows - 1) * ld + H; ++i) res[i] = orc_bf16_round(0.25 * (double)(i % 9));
+  float* w = take(H * 4);
+  for (int64_t h = 0; h < H; ++h) w[h] = 1.0f + 0.01f * (float)h;
+  uint16_t* res_out = take(((rows - 1) * ld + H) * 2);
+  uint16_t* y = take(((rows - 1) * ld + H) * 2);
+  uint8_t* q = take((rows - 1) * ld + H);
+  float* scale = take(rows * 4);
+  double* xe = take(rows * H * 8);
+  double* ye = take(rows * H * 8);
+  double* mag = take(rows * H * 8);
+  int rc = 0;
+  rc |= orc_fold_norm(rows, H, rb, P, (const uint16_t* const*)parts, ld, res, ld, w, 1e-6f, 0, res_out, ld, y,
+                      ld, NULL, 0, NULL, xe, ye, mag);
+  rc |= orc_fold_norm(rows, H, rb, P, (const uint16_t* const*)parts, ld, NULL, 0, w, 1e-6f, 1, res_out, ld, NULL,
+                      0, q, ld, scale, xe, ye, mag);
+  rc |= orc_enter_norm(rows, H, res, ld, w, 1e-6f, 0, res_out, ld, y, ld, ye);
+  rc |= orc_written_norm(rows, H, res, ld, w, 0.0f, 1, y, ld, ye);
+  uint16_t* extra = take(((T - 1) * ld + H) * 2);
+  rc |= orc_complete_partials(rows, H, rb, P, (const uint16_t* const*)parts, ld, extra, ld, y, ld, xe, mag);
+  rc |= orc_snapshot(rows, H, rb, P, (const uint16_t* const*)parts, ld, res, ld, y, ld, xe, mag);
+  rc |= orc_snapshot(rows, H, 0, 0, NULL, ld, res, ld, y, ld, xe, mag);
+  uint16_t* E = take(((NE - 1) * ld + H) * 2);
+  for (int64_t i = 0; i < (NE - 1) * ld + H; ++i) E[i] = orc_bf16_round(0.5 * (double)(i % 5));
+  int32_t* idx = take(T * K * 4);
+  float* gate = take(T * K * 4);
+  for (int i = 0; i < T * K; ++i) { idx[i] = (i * 3) % (NE + 2) - 1; gate[i] = 0.5f; }  /* some out of range */
+  rc |= orc_moe_fold_norm(rows, H, rb, K, E, ld, NE, idx, gate, res, ld, w, 1e-6f, 0, res_out, ld, y, ld, NULL, 0,
+                          NULL, xe, ye, mag);
+  rc |= orc_moe_fold_norm(rows, H, rb, K, E, ld, NE, idx, gate, NULL, 0, w, 1e-6f, 0, res_out, ld, NULL, 0, q, ld,
+                          scale, xe, ye, mag);
+  rc |= orc_complete_moe(rows, H, rb, K, E, ld, NE, idx, gate, extra, ld, y, ld, xe, mag);
+  for (int c = 0; c < 256; ++c)
+    if ((c & 0x7F) != 0x7F) rc |= orc_e4m3_round(orc_e4m3_value((uint8_t)c)) != (uint8_t)c && (c & 0x7F) != 0;
+  for (int p = 0; p < P; ++p) free(parts[p]);
+  free(res); free(w); free(res_out); free(y); free(q); free(scale); free(xe); free(ye); free(mag);
+  free(extra); free(E); free(idx); free(gate);
+  printf("oracle walk: rc %d\n", rc);
+  return rc ? 1 : 0;
+}
+"""
+
+
+def _run(exe):
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300, env=ENV)
+    assert out.returncode == 0, out.stdout[-3000:] + out.stderr[-6000:]
+    return out.stdout
+
+
+def test_host_state_machine_under_asan(tmp_path):
+    src = tmp_path / "host_walk.cpp"
+    src.write_text(HOST_DRIVER)
+    exe = tmp_path / "host_walk"
+    subprocess.check_call(["g++", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I", INCLUDE,
+                           "-I", CSRC, *SAN, "-o", str(exe), str(src), os.path.join(CSRC, "host.cpp"),
+                           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"])
+    assert "host walk: 0 failures" in _run(exe)
+
+
+def test_oracle_under_asan(tmp_path):
+    src = tmp_path / "oracle_walk.c"
+    src.write_text(ORACLE_DRIVER)
+    exe = tmp_path / "oracle_walk"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.dirname(ORACLE_SRC), *SAN, "-o", str(exe), str(src),
+                           "-lm"])
+    assert "oracle walk: rc 0" in _run(exe)
