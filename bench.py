@@ -600,7 +600,9 @@ def cpu_threads_baseline(workloads, d, budget_s: float, threads: int):
             el = time.perf_counter() - t0
             if el >= budget_s:
                 break
+    nbytes = (d["P"] + 3) * T * d["H"] * 2 + d["H"] * 4
     return {"value": passes * T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "GBps": passes * nbytes / el / 1e9,
             "sample": f"{passes} passes of the full prefill boundary split into {threads} row "
                       f"chunks in {el:.1f} s, fp64", "cpu": cpu_model()}
 
@@ -630,7 +632,10 @@ def cpu_baseline(workloads, d, budget_s: float):
     finally:
         os.sched_setaffinity(0, allowed)
     med = sorted(times)[len(times) // 2]
-    return {"value": d["T"] / med, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    T, H, P = d["T"], d["H"], d["P"]
+    nbytes = (P + 3) * T * H * 2 + H * 4  # the fold's algorithmic bytes, as for the kernel
+    return {"value": T / med, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "GBps": nbytes / med / 1e9,
             "sample": f"{len(times)} passes of the full prefill boundary (2048 rows x 4096, P=8) "
                       f"in {el:.1f} s, one thread pinned to core {core}, fp64; rate of the "
                       f"median pass", "cpu": cpu_model()}
