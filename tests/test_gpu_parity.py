@@ -1062,3 +1062,49 @@ def test_fp8_subnormal_scale(orc, shape):
     q = got["q"].view.cpu().numpy()
     assert np.all(q[:, 2::3] == 0), "a zero element must give code +0"
     assert np.all(q[:, 1::3] & 0x7F != 0x7E), "half-size elements must not saturate"
+
+
+# ------------------------------------------------------------------ seeded random cases
+
+def _random_case(i):
+    """Case i of the seeded sweep: kind, sizes, slice, launch shape (one the host accepts)."""
+    rng = np.random.default_rng(7000 + i)
+    kind = ["fold", "fp8", "moe", "complete_only", "add_to_output", "snapshot"][i % 6]
+    H = int(rng.choice([8, 64, 264, 1000, 2048, 3600, 4096, 4104, 5000, 7168, 8192]))
+    T = int(rng.integers(1, 97))
+    rb = int(rng.integers(0, T))
+    rows = int(rng.integers(1, T - rb + 1))
+    P = int(rng.integers(1, 17))
+    gemma = bool(rng.integers(0, 2)) and kind in ("fold", "fp8", "moe")
+    nvec = H // 8
+    shapes = [(0, 0)]
+    for th, v in ((64, 8), (128, 4), (256, 2), (256, 4), (512, 1), (512, 2), (1024, 1), (1024, 2)):
+        if th * v >= nvec:
+            shapes.append((th, v))
+    if nvec <= 512:
+        shapes.append((64, 8))
+    if nvec <= 896:
+        shapes.append((64, 14))
+    shape = shapes[int(rng.integers(0, len(shapes)))]
+    return kind, T, H, P, rb, rows, gemma, shape
+
+
+@pytest.mark.parametrize("i", range(36))
+def test_random_cases(orc, i):
+    kind, T, H, P, rb, rows, gemma, shape = _random_case(i)
+    what = f"case {i}: {kind} T={T} H={H} P/k={P} slice={rb}+{rows} gemma={gemma} shape={shape[0]}x{shape[1]}"
+    print(f"\n  {what}", flush=True)
+    with forced_shape(*shape):
+        if kind in ("fold", "fp8"):
+            d = workloads.fold_inputs(8000 + i, T, H, P)
+            assert_fold_matches(orc, d, what, fp8=kind == "fp8", row_begin=rb, rows=rows, gemma=gemma)
+        elif kind == "moe":
+            d = workloads.moe_inputs(8000 + i, T, H, max(P, 2), P)
+            run_moe(orc, d, rb, rows, what, gemma=gemma)
+        else:
+            d = workloads.fold_inputs(8000 + i, T, H, P)
+            extra = (workloads.to_bf16(workloads.normal_f32(8000 + i, 12345, (T, H), 0.0, 0.25))
+                     if kind == "add_to_output" else None)
+            a = _complete(d, kind, row_begin=rb, rows=rows, extra=extra)
+            e, mag = _oracle_complete(orc, d, kind, row_begin=rb, rows=rows, extra=extra)
+            tolerance.check_bf16(bits(a.view), e, mag, what)
