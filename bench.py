@@ -473,38 +473,43 @@ def back_to_back_us(torch, launch, n_sets: int, reps: int = 300, warmup: int = 2
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def stream_ceiling(torch, T: int, H: int, fold_us: float):
-    """The 9:2 streaming kernel (libboundary_ceiling.so: the fold's rows, loads and stores, no
-    arithmetic) over rotating sets of the prefill shape, for four launch shapes; compared with
-    the fold timed the same way (back-to-back launches) in the same process."""
+def stream_ceiling(torch, T: int, H: int, n_src: int, n_out: int, kernel_us: dict):
+    """The arithmetic-free streaming kernel (libboundary_ceiling.so: n_src row reads and n_out row
+    writes per row, the boundary kernels' rows, resources and cache policy) over rotating sets of
+    [T, H] rows, for four launch shapes; beside it the boundary calls with the same mix, timed the
+    same way (back-to-back launches) in the same process (`kernel_us`: name -> us)."""
     from reduce_residual_rmsnorm_bnd_amd import _build
 
     L = ctypes.CDLL(_build.CEILING_LIB_PATH)
     vp = ctypes.c_void_p
-    L.bnd_ceiling_mix_9r2w.argtypes = [ctypes.POINTER(vp), vp, vp, ctypes.c_int64, ctypes.c_int64,
-                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp]
-    nbytes = 11 * T * H * 2
+    L.bnd_ceiling_mix.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp]
+    nbytes = (n_src + n_out) * T * H * 2
     n_sets = max(2, -(-ROTATE_BYTES // nbytes))
     sets = []
     for _ in range(n_sets):
-        bufs = [torch.zeros(T, H, dtype=torch.bfloat16, device="cuda:0") for _ in range(11)]
-        sets.append((bufs, (vp * 9)(*[b.data_ptr() for b in bufs[:9]]), vp(bufs[9].data_ptr()),
-                     vp(bufs[10].data_ptr())))
+        bufs = [torch.zeros(T, H, dtype=torch.bfloat16, device="cuda:0") for _ in range(n_src + n_out)]
+        sets.append((bufs, (vp * n_src)(*[b.data_ptr() for b in bufs[:n_src]]), vp(bufs[n_src].data_ptr()),
+                     vp(bufs[n_src + 1].data_ptr()) if n_out == 2 else vp()))
     stream = vp(torch.cuda.current_stream().cuda_stream)
     shapes = {}
     for threads, vpt in ((256, 2), (512, 1), (128, 4), (64, 8)):
         def launch(i, threads=threads, vpt=vpt):
             _, src, o0, o1 = sets[i]
-            rc = L.bnd_ceiling_mix_9r2w(src, o0, o1, T, H, H, threads, vpt, stream)
+            rc = L.bnd_ceiling_mix(src, n_src, o0, o1, T, H, H, threads, vpt, stream)
             if rc:
                 raise RuntimeError(f"ceiling launch failed: {rc}")
         shapes[f"{threads}x{vpt}"] = back_to_back_us(torch, launch, n_sets)
     best = min(shapes, key=shapes.get)
     del sets
     torch.cuda.empty_cache()
-    return {"bytes": nbytes, "us_per_launch_by_shape": shapes, "best_shape": best,
-            "GBps": nbytes / shapes[best] / 1e3, "frac": nbytes / shapes[best] / 1e3 / PEAK_HBM_GBPS,
-            "fold_back_to_back_us": fold_us, "fold_time_over_ceiling_time": fold_us / shapes[best]}
+    out = {"reads_writes": f"{n_src}:{n_out}", "bytes": nbytes, "us_per_launch_by_shape": shapes,
+           "best_shape": best, "GBps": nbytes / shapes[best] / 1e3,
+           "frac": nbytes / shapes[best] / 1e3 / PEAK_HBM_GBPS}
+    for name, us in kernel_us.items():
+        out[f"{name}_back_to_back_us"] = us
+        out[f"{name}_time_over_ceiling_time"] = us / shapes[best] if us else None
+    return out
 
 
 def gather_ceiling(torch, dm, moe_us: float):
@@ -726,7 +731,7 @@ def main():
     if not args.no_secondary:
         sec = {}
         log("9:2 streaming ceiling (the fold's loads and stores without arithmetic)")
-        sec["stream_ceiling_9r2w_T2048_H4096"] = stream_ceiling(torch, d["T"], d["H"], fold_us)
+        sec["stream_ceiling_9r2w_T2048_H4096"] = stream_ceiling(torch, d["T"], d["H"], 9, 2, {"fold": fold_us})
         log("quantised read (T=2048 H=7168 P=8, fp8 out)")
         dq = workloads.quantised()
         n_q = max(2, -(-ROTATE_BYTES // ((dq["P"] + 2) * dq["T"] * dq["H"] * 2 + dq["T"] * dq["H"])))
@@ -761,6 +766,7 @@ def main():
         torch.cuda.empty_cache()
         log("complete_only, snapshot and add_to_output (prefill sizes), the unfused fallback, "
             "the largest RSv share of 2047 rows")
+        aux_us = {}
         for kind in ("complete_only", "snapshot", "add_to_output"):
             step, nb, keep = aux_case(torch, bnd, d, n_sets, kind)
             ta = timer.run(step, n_sets, 20, 256)
@@ -768,7 +774,14 @@ def main():
                                              "GBps": nb / ta["kernel_s"] / 1e9,
                                              "frac": nb / ta["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                                              "algorithmic_bytes": nb}
+            aux_us[kind] = back_to_back_us(torch, lambda i: step(i, None, None), n_sets)
             del keep, step
+        torch.cuda.empty_cache()
+        log("8:1 and 9:1 streaming ceilings (complete_only; snapshot and add_to_output)")
+        sec["stream_ceiling_8r1w_T2048_H4096"] = stream_ceiling(
+            torch, d["T"], d["H"], 8, 1, {"complete_only": aux_us["complete_only"]})
+        sec["stream_ceiling_9r1w_T2048_H4096"] = stream_ceiling(
+            torch, d["T"], d["H"], 9, 1, {"snapshot": aux_us["snapshot"], "add_to_output": aux_us["add_to_output"]})
         step, nb, keep = aux_case(torch, bnd, d, n_sets, "unfused")
         unfused_us = back_to_back_us(torch, lambda i: step(i, None, None), n_sets)
         sec["unfused_fallback_T2048_H4096_P8"] = {

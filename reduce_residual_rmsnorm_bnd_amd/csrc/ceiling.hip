@@ -1,12 +1,14 @@
 // ceiling.hip -- measurement support, not part of the boundary path.
 //
-// A kernel with the prefill fold's memory access mix and none of its arithmetic: for every
-// 16-byte vector of a row it reads nine rows (eight partials and the residual) and writes two
-// (the residual and the normalised output), one row per workgroup, through the same per-row
-// buffer resources and cache policy (non-temporal loads, sc1 stores) as the fold. The loaded
-// vectors are combined with XOR so that every load is consumed and every store depends on all
-// nine. Its rate on a device is what that memory system delivers for this 9:2 read:write stream
-// in this layout; the fold is compared with it as context. A gathering variant reads eight of
+// A kernel with a boundary call's memory access mix and none of its arithmetic: for every
+// 16-byte vector of a row it reads n rows and writes one or two, one row per workgroup, through
+// the same per-row buffer resources and cache policy (non-temporal loads, sc1 stores) as the
+// boundary kernels. The prefill fold's mix is nine reads (eight partials and the residual) and two
+// writes (the residual and the normalised output); complete_only's is eight and one, a snapshot's
+// or add_to_output's nine and one. The loaded vectors are combined with XOR so that every load is
+// consumed and every store depends on all of them. Its rate on a device is what that memory
+// system delivers for the stream in this layout; each call is compared with its own mix as
+// context. A gathering variant reads eight of
 // the nine rows through an int32 row index, as the MoE finalize reads its picks. An empty kernel
 // gives the cost of a launch with no work, the floor under the per-boundary time of small
 // batches. Built into its own library (libboundary_ceiling.so); the boundary library does not
@@ -15,14 +17,16 @@
 
 namespace {
 
-constexpr int kSources = 9;
+constexpr int kSources = 9;         // the gathering stream: eight gathered rows and one more
+constexpr int kMaxMixSources = 16;
 
 struct MixArgs {
-  const uint16_t* src[kSources];
+  const uint16_t* src[kMaxMixSources];
   uint16_t* out0;
-  uint16_t* out1;
+  uint16_t* out1;  // NULL: one output
   int64_t ld;      // elements between rows, same for every operand
   int row_bytes;   // bytes of a row that are read and written
+  int n_src;       // 1..16
 };
 
 template <int VPT>
@@ -38,8 +42,7 @@ __global__ __launch_bounds__(bnd::kMaxThreads) void mix_kernel(const MixArgs a) 
 #pragma unroll
     for (int v = 0; v < VPT; ++v) acc[v] = bnd::load16(r, off[v]);
   }
-#pragma unroll
-  for (int p = 1; p < kSources; ++p) {
+  for (int p = 1; p < a.n_src; ++p) {
     const bnd::Rsrc r = bnd::row_rsrc(a.src[p] + row * a.ld, a.row_bytes);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
@@ -48,11 +51,12 @@ __global__ __launch_bounds__(bnd::kMaxThreads) void mix_kernel(const MixArgs a) 
     }
   }
   const bnd::Rsrc o0 = bnd::row_rsrc(a.out0 + row * a.ld, a.row_bytes);
-  const bnd::Rsrc o1 = bnd::row_rsrc(a.out1 + row * a.ld, a.row_bytes);
 #pragma unroll
-  for (int v = 0; v < VPT; ++v) {
-    bnd::store16(o0, off[v], acc[v]);
-    bnd::store16(o1, off[v], acc[v]);
+  for (int v = 0; v < VPT; ++v) bnd::store16(o0, off[v], acc[v]);
+  if (a.out1) {
+    const bnd::Rsrc o1 = bnd::row_rsrc(a.out1 + row * a.ld, a.row_bytes);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) bnd::store16(o1, off[v], acc[v]);
   }
 }
 
@@ -113,40 +117,50 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 }  // namespace
 
-// Launches the 9:2 streaming kernel once on `stream`.
-//   src        nine device pointers to [rows, ld] bf16 row-major operands (read)
-//   out0/out1  two device pointers to [rows, ld] bf16 operands (written; may not alias src)
+// Launches the streaming kernel once on `stream`:
+//   src        n_src (1..16) device pointers to [rows, ld] bf16 row-major operands (read)
+//   out0/out1  device pointers to [rows, ld] bf16 operands (written; may not alias src); out1
+//              may be NULL for one output
 //   rows       grid size, one workgroup per row, 1 .. 2^31-1
 //   row_elems  bf16 elements per row that are streamed, a multiple of 8, row_elems <= ld
 //   threads    workgroup size, a multiple of 64 in [64, 1024]; vpt in {1, 2, 4, 8};
 //              threads * vpt * 8 must cover row_elems
 // Returns 0 on success, -1 on an invalid argument (nothing launched), or the hipError_t of the
 // launch.
-extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix_9r2w(
-    const void* const* src, void* out0, void* out1, int64_t rows, int64_t ld, int64_t row_elems,
+extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix(
+    const void* const* src, int n_src, void* out0, void* out1, int64_t rows, int64_t ld, int64_t row_elems,
     int threads, int vpt, hipStream_t stream) {
-  if (!src || !out0 || !out1 || rows < 1 || rows > 0x7fffffff || row_elems < 8 || row_elems % 8 ||
-      ld < row_elems || ld % 8 || row_elems * 2 > 0x7fffffff)
+  if (!src || n_src < 1 || n_src > kMaxMixSources || !out0 || rows < 1 || rows > 0x7fffffff || row_elems < 8 ||
+      row_elems % 8 || ld < row_elems || ld % 8 || row_elems * 2 > 0x7fffffff)
     return -1;
   if (threads < 64 || threads > bnd::kMaxThreads || threads % 64 || (vpt != 1 && vpt != 2 && vpt != 4 && vpt != 8) ||
       (int64_t)threads * vpt * 8 < row_elems)
     return -1;
-  MixArgs a;
-  for (int p = 0; p < kSources; ++p) {
+  MixArgs a = {};
+  for (int p = 0; p < n_src; ++p) {
     if (!src[p] || !aligned16(src[p])) return -1;
     a.src[p] = static_cast<const uint16_t*>(src[p]);
   }
-  if (!aligned16(out0) || !aligned16(out1)) return -1;
+  if (!aligned16(out0) || (out1 && !aligned16(out1))) return -1;
   a.out0 = static_cast<uint16_t*>(out0);
   a.out1 = static_cast<uint16_t*>(out1);
   a.ld = ld;
   a.row_bytes = (int)(row_elems * 2);
+  a.n_src = n_src;
   void* args[] = {&a};
   const void* fn = vpt == 1   ? reinterpret_cast<const void*>(&mix_kernel<1>)
                    : vpt == 2 ? reinterpret_cast<const void*>(&mix_kernel<2>)
                    : vpt == 4 ? reinterpret_cast<const void*>(&mix_kernel<4>)
                               : reinterpret_cast<const void*>(&mix_kernel<8>);
   return (int)hipLaunchKernel(fn, dim3((unsigned)rows), dim3((unsigned)threads), args, 0, stream);
+}
+
+// The prefill fold's mix: nine sources, two outputs (out1 must not be NULL).
+extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix_9r2w(
+    const void* const* src, void* out0, void* out1, int64_t rows, int64_t ld, int64_t row_elems, int threads,
+    int vpt, hipStream_t stream) {
+  if (!out1) return -1;
+  return bnd_ceiling_mix(src, 9, out0, out1, rows, ld, row_elems, threads, vpt, stream);
 }
 
 // Launches the empty kernel once on `stream`: `workgroups` (1 .. 2^31-1) workgroups of `threads`

@@ -19,6 +19,9 @@ def _lib():
     L.bnd_ceiling_mix_9r2w.argtypes = [ctypes.POINTER(VP), VP, VP, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, VP]
     L.bnd_ceiling_mix_9r2w.restype = ctypes.c_int
+    L.bnd_ceiling_mix.argtypes = [ctypes.POINTER(VP), ctypes.c_int, VP, VP, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int64, ctypes.c_int, ctypes.c_int, VP]
+    L.bnd_ceiling_mix.restype = ctypes.c_int
     L.bnd_ceiling_empty.argtypes = [ctypes.c_int64, ctypes.c_int, VP]
     L.bnd_ceiling_empty.restype = ctypes.c_int
     L.bnd_ceiling_gather_9r2w.argtypes = [VP, ctypes.c_int64, VP, VP, VP, VP, ctypes.c_int64, ctypes.c_int64,
@@ -52,6 +55,10 @@ def test_ceiling_refuses_bad_shapes():
         assert L.bnd_ceiling_mix_9r2w(*args, None) == -1, args
     src[4] = a + 2  # a misaligned source
     assert L.bnd_ceiling_mix_9r2w(src, o0, o1, 4, 4096, 4096, 512, 1, None) == -1
+    src16 = (VP * 16)(*[a + (i << 24) for i in range(16)])
+    for n in (0, 17):  # source counts outside 1..16
+        assert L.bnd_ceiling_mix(src16, n, o0, None, 4, 4096, 4096, 512, 1, None) == -1, n
+    assert L.bnd_ceiling_mix_9r2w(src, o0, None, 4, 4096, 4096, 512, 1, None) == -1  # 9:2 needs two outputs
     for wg, threads in ((0, 64), (1, 32), (1, 100), (1, 2048), (1 << 31, 64)):
         assert L.bnd_ceiling_empty(wg, threads, None) == -1, (wg, threads)
     E, idx, s8 = VP(a), VP(a + (30 << 24)), VP(a + (31 << 24))
@@ -128,3 +135,28 @@ def test_gather_streams_the_xor(rows, H, threads, vpt):
                 expect[t] ^= E[e]
     for o in out:
         assert torch.equal(o.cpu(), expect)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n_src,two_outputs", [(8, False), (9, False), (1, True), (16, False)])
+def test_mix_streams_the_xor(n_src, two_outputs):
+    L = _lib()
+    rows, H, threads, vpt = 13, 4096, 64, 8
+    g = torch.Generator().manual_seed(n_src)
+    host = [torch.randint(-32768, 32768, (rows, H), dtype=torch.int16, generator=g) for _ in range(n_src)]
+    srcs = [h.to("cuda:0") for h in host]
+    out = [torch.full((rows, H), 7, dtype=torch.int16, device="cuda:0") for _ in range(2)]
+    print(f"\n  mix {n_src}:{2 if two_outputs else 1} rows={rows} H={H}", flush=True)
+    rc = L.bnd_ceiling_mix((VP * n_src)(*[s.data_ptr() for s in srcs]), n_src, out[0].data_ptr(),
+                           out[1].data_ptr() if two_outputs else None, rows, H, H, threads, vpt,
+                           torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    expect = host[0].clone()
+    for h in host[1:]:
+        expect ^= h
+    assert torch.equal(out[0].cpu(), expect)
+    if two_outputs:
+        assert torch.equal(out[1].cpu(), expect)
+    else:
+        assert bool((out[1] == 7).all()), "one output: the second buffer is untouched"
