@@ -1108,3 +1108,56 @@ def test_random_cases(orc, i):
             a = _complete(d, kind, row_begin=rb, rows=rows, extra=extra)
             e, mag = _oracle_complete(orc, d, kind, row_begin=rb, rows=rows, extra=extra)
             tolerance.check_bf16(bits(a.view), e, mag, what)
+
+
+def test_graph_replay_of_every_hot_call():
+    """enter, a fold, an fp8 fold, a MoE finalize, complete_only and a one-partial fold, all at
+    2048 x 4096 (the one-wavefront kernels), captured once into a HIP graph and replayed several
+    times with eager library work in between; every replay must equal the eager run bitwise."""
+    T, H, P, k = 2048, 4096, 8, 8
+    d = workloads.fold_inputs(900, T, H, P)
+    m = workloads.moe_inputs(901, T, H, 64, k)
+    x_in = workloads.stack_input(902, T, H).to(DEV)
+    parts = [c.to(DEV) for c in d["partials"]]
+    w = d["weight"].to(DEV)
+    E, idx, gate = _moe_device(m)
+
+    def chain(res, y, q, sc, out):
+        s = bnd.bnd_stream_create(T, H, res)
+        bnd.bnd_enter_norm(s, x_in, w, 1e-6, y[0])
+        bnd.bnd_fold_norm(s, bnd.bnd_publish_partials(s, parts), w, 1e-6, y[1])
+        bnd.bnd_fold_norm_quant_fp8(s, bnd.bnd_publish_partials(s, parts), w, 1e-6, q, sc)
+        bnd.bnd_moe_finalize_fold_norm(s, bnd.bnd_publish_moe(s, E, idx, gate, k), w, 1e-6, y[2])
+        owed = bnd.bnd_complete_only(s, bnd.bnd_publish_partials(s, parts), out)
+        bnd.bnd_fold_norm(s, owed, w, 1e-6, y[3])
+        return s
+
+    def buffers():
+        z = lambda dt=torch.bfloat16: torch.zeros(T, H, dtype=dt, device=DEV)
+        return z(), [z() for _ in range(4)], z(torch.uint8), torch.zeros(T, device=DEV), z()
+
+    eager = buffers()
+    chain(*eager)
+    torch.cuda.synchronize()
+    assert bnd.last_launch_shape() == (T, 64, 8), "the chain runs the one-wavefront kernels"
+    graph = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain(*graph)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        keep = chain(*graph)
+    other = buffers()
+    flat = lambda b: [b[0], *b[1], b[2], b[3], b[4]]
+    for rep in range(3):
+        for t in flat(graph):
+            t.zero_()
+        g.replay()
+        chain(*other)  # eager library work between replays
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(flat(graph), flat(eager))):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager run"
+    del keep
