@@ -4,16 +4,21 @@
 // One workgroup per token row. The row is split into 16-byte vectors of 8
 // elements; thread t of a workgroup of `threads` lanes owns vectors
 // t, t + threads, ... (VPT of them), so each load instruction of a wavefront
-// reads 1 KiB of contiguous row. The row's work:
-//   1. complete: issue the loads of all sources (P partials, or the k
-//      gathered expert rows) and of the residual before any arithmetic, then
-//      sum in fp32 in source order (the deferred all-reduce of the study
-//      note's fusion point, on one GPU a sum over resident buffers);
+// reads 1 KiB of contiguous row. Two families of kernels, chosen per launch
+// by the host: read_kernel and complete_kernel give a row several wavefronts
+// and issue all of its loads before any arithmetic; wave_read_kernel and
+// wave_complete_kernel give a row one wavefront that streams the sources one
+// after another with two loads in flight. The row's work:
+//   1. complete: load the sources (P partials, or the k gathered expert rows)
+//      and the residual and sum them in fp32 in source order (the deferred
+//      all-reduce of the study note's fusion point, on one GPU a sum over
+//      resident buffers);
 //   2. fold: x = r + s in fp32 (guide, "Residual update and input read": the
 //      plain update is an add and the read keeps the fp32 sum);
-//   3. read: sum of squares over the row with a wave64 DPP reduction and one
-//      LDS step across wavefronts, inv = 1/sqrt(ss/H + eps) (correctly
-//      rounded divide and square root), y = x * inv * w;
+//   3. read: sum of squares over the row with a wave64 DPP reduction (and one
+//      LDS step across wavefronts when a row has several), inv =
+//      1/sqrt(ss/H + eps) (correctly rounded divide and square root),
+//      y = x * inv * w;
 //   4. store the residual as bf16 (round to nearest even, v_cvt_pk_bf16_f32)
 //      and y as bf16, or as OCP e4m3 codes (v_cvt_pk_fp8_f32) with a
 //      per-row fp32 scale.
