@@ -36,7 +36,7 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 1 << 30          # >= 4x the 256 MB Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["kernels.h", "launch.h", "k_partials.hip", "k_moe.hip", "k_read.hip",
-                  "k_complete.hip", "k_wave.hip", "host.cpp"]
+                  "k_complete.hip", "k_wave.hip", "k_wave_complete.hip", "host.cpp"]
 
 
 def log(msg: str) -> None:
@@ -168,8 +168,7 @@ class Timed:
 
 def launch_desc(bnd) -> dict:
     """The shape of this thread's last launch through the library, as the bench reports it."""
-    rows, threads, vpt = bnd.last_launch_shape()
-    one_wave = vpt in (8, 14)
+    rows, threads, vpt, one_wave = bnd.last_launch_shape()
     return {"workgroups": rows, "threads": threads, "vectors_per_thread": vpt,
             "rows_per_workgroup": 1, "one_wavefront_per_row": one_wave}
 

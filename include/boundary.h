@@ -281,23 +281,42 @@ typedef enum bnd_option {
   BND_OPT_FUSED_UNAVAILABLE = 1,
   /* Launch shape overrides for tuning; 0 = automatic. Threads per row: a
    * multiple of 64 in [64, 1024]. Vectors (of 8 elements) per thread: 1, 2
-   * or 4, or 8 or 14 for one wavefront per row (64 threads; H <= 4096 or
-   * H <= 7168; only calls that take owed partials or MoE picks: the folds,
-   * complete_only, add_to_output, and snapshot of a Pending stream). A shape
-   * that cannot cover H, or 8 or 14 for any other call, fails with NO_PATH. */
+   * or 4 for rows of several wavefronts, or an even count 6 .. 14 for one
+   * wavefront per row with that many vectors per lane (64 threads; H up to
+   * 64 * 8 times the count; only calls that take owed partials or MoE picks:
+   * the folds, complete_only, add_to_output, and snapshot of a Pending
+   * stream). A shape that cannot cover H, or a one-wavefront count for any
+   * other call, fails with NO_PATH. */
   BND_OPT_THREADS_PER_ROW = 2,
-  BND_OPT_VECTORS_PER_THREAD = 3
+  BND_OPT_VECTORS_PER_THREAD = 3,
+  /* When vectors per thread is automatic: BND_ONE_WAVEFRONT_AUTO (default)
+   * takes one wavefront per row where it is measured faster (a call that
+   * takes owed work, 1544 <= H <= 7168, at least 6 rows per CU, and either
+   * no more rows than the kernel holds on the chip at once or a last round of
+   * resident rows at least 3/4 full for the folds and MoE finalize, 1/3 full
+   * for complete_only, add_to_output and snapshot); ALWAYS requires it: every call runs its
+   * one-wavefront kernel of the narrowest width that covers H (4 .. 14
+   * vectors per lane), and a call that has none (enter, the read of a
+   * Written stream, its snapshot) or rows longer than 7168 elements fails
+   * with NO_PATH; NEVER never takes it. */
+  BND_OPT_ONE_WAVEFRONT = 4
 } bnd_option;
+
+#define BND_ONE_WAVEFRONT_AUTO 0
+#define BND_ONE_WAVEFRONT_ALWAYS 1
+#define BND_ONE_WAVEFRONT_NEVER 2
 
 BND_API bnd_status bnd_set_option(bnd_option opt, int64_t value);
 BND_API int64_t bnd_get_option(bnd_option opt);
 
 /* The launch shape of the calling thread's last kernel launch through this
- * library: workgroups (one per row), threads per workgroup and 16-byte vectors
- * per thread (8 or 14: one wavefront per row). All 0 before the thread's
- * first launch; a call that launches nothing (an error, zero rows) leaves the
- * previous values. Any pointer may be NULL. Always BND_OK. */
-BND_API bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_thread);
+ * library: workgroups (one per row), threads per workgroup, 16-byte vectors
+ * per thread, and 1 if the kernel was a one-wavefront-per-row kernel (0 if a
+ * row had several wavefronts). All 0 before the thread's first launch; a call
+ * that launches nothing (an error, zero rows) leaves the previous values. Any
+ * pointer may be NULL. Always BND_OK. */
+BND_API bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_thread,
+                                         int* one_wavefront);
 
 /* Timing: the calling thread's next kernel launch records `start_event` and
  * `stop_event` (hipEvent_t, created by the caller) from its own dispatch

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libboundary.so")
 CEILING_LIB_PATH = os.path.join(HERE, "libboundary_ceiling.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["host.cpp", "k_read.hip", "k_partials.hip", "k_moe.hip", "k_complete.hip", "k_wave.hip"]
+SOURCES = ["host.cpp", "k_read.hip", "k_partials.hip", "k_moe.hip", "k_complete.hip", "k_wave.hip",
+           "k_wave_complete.hip"]
 CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -41,6 +41,10 @@ BND_NORM_PLAIN, BND_NORM_GEMMA = 0, 1
 BND_OPT_FUSED_UNAVAILABLE = 1
 BND_OPT_THREADS_PER_ROW = 2
 BND_OPT_VECTORS_PER_THREAD = 3
+BND_OPT_ONE_WAVEFRONT = 4
+BND_ONE_WAVEFRONT_AUTO = 0
+BND_ONE_WAVEFRONT_ALWAYS = 1
+BND_ONE_WAVEFRONT_NEVER = 2
 
 # exported symbols, in header order
 SYMBOLS = [
@@ -91,7 +95,7 @@ def _declare(lib):
         "bnd_version": (c.c_char_p, []),
         "bnd_set_option": (st, [c.c_int, i64]),
         "bnd_get_option": (i64, [c.c_int]),
-        "bnd_last_launch_shape": (st, [c.POINTER(i64), c.POINTER(i32), c.POINTER(i32)]),
+        "bnd_last_launch_shape": (st, [c.POINTER(i64), c.POINTER(i32), c.POINTER(i32), c.POINTER(i32)]),
         "bnd_time_next_launch": (st, [vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -129,11 +133,13 @@ def get_option(opt: int) -> int:
     return lib().bnd_get_option(opt)
 
 
-def last_launch_shape() -> tuple[int, int, int]:
-    """(workgroups, threads per workgroup, vectors per thread) of this thread's last launch."""
-    rows, threads, vpt = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int()
-    _check(lib().bnd_last_launch_shape(ctypes.byref(rows), ctypes.byref(threads), ctypes.byref(vpt)))
-    return rows.value, threads.value, vpt.value
+def last_launch_shape() -> tuple[int, int, int, bool]:
+    """(workgroups, threads per workgroup, vectors per thread, one wavefront per row) of this
+    thread's last launch."""
+    rows, threads, vpt, one = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().bnd_last_launch_shape(ctypes.byref(rows), ctypes.byref(threads), ctypes.byref(vpt),
+                                       ctypes.byref(one)))
+    return rows.value, threads.value, vpt.value, bool(one.value)
 
 
 def _hip_stream(hip_stream):

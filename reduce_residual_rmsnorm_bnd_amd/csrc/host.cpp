@@ -62,6 +62,7 @@ std::atomic<uint64_t> g_serial{1};
 std::atomic<int> g_fused_unavailable{-1};  // -1: read BND_DISABLE_FUSED on first use
 std::atomic<int> g_threads_override{0};
 std::atomic<int> g_vpt_override{0};
+std::atomic<int> g_one_wave_mode{BND_ONE_WAVEFRONT_AUTO};
 thread_local hipEvent_t g_time_start = nullptr;  // consumed by the thread's next launch
 thread_local hipEvent_t g_time_stop = nullptr;
 thread_local Launch g_chosen;       // the shape of the launch being prepared
@@ -173,38 +174,56 @@ int compute_units() {
 //    workgroups measured 3-6% slower than 8- or 4-wave ones);
 //  - a call that takes owed partials or MoE picks (the folds with bf16 or
 //    fp8 output, complete_only, add_to_output, snapshot) runs one wavefront per
-//    row (64 threads) when its rows hold 449..512 vectors (H = 3592..4096, 8
-//    vectors per lane) or 833..896 (H = 6664..7168, 14 per lane), the launch
-//    has at least 6 rows per CU, and all its rows are resident at once: at
-//    most as many rows per CU as the kernel's occupancy allows (its VGPRs set
-//    it: 92..153 VGPRs hold 12 to 20 rows per CU, 146..255 hold 8 or 12).
-//    Against the shapes above: 5-12% faster at 2048 rows for every such call
-//    at H = 4096 and H = 7168, 1-7% faster at 1536 rows (6 per CU), 17-87%
-//    slower at 1024 rows and below (too few waves per CU), and once the rows
-//    need a second round slower (up to 15%) or equal; faster again wherever
-//    larger batches still fit in one round (up to 4096 rows at H = 4096 for the
-//    completes, 3072 at H = 7168).
+//    row (64 threads) when its rows hold 193..896 vectors (H = 1544..7168; the
+//    kernel of the narrowest even width of 4 to 14 vectors per lane that
+//    covers the row) and the launch has at least 6 rows per CU, unless its
+//    last round of resident rows would be mostly empty. A round is as many
+//    rows as the chip holds at once: the kernel's occupancy (its 52..255
+//    VGPRs hold 8 to 32 rows per CU) times the CUs. A launch of one round
+//    always qualifies, a longer one when its last round is at least 3/4 full
+//    for the reads and at least 1/3 full for the completes (both fractions
+//    measured, below). Against the shapes above,
+//    at 2048 rows: 5-12% faster for every such call at H = 4096 and 7168 and
+//    1-13% at H = 2048 .. 6144; between 10% slower and 5% faster at 1536
+//    rows (6 per CU); 17-87% slower at 1024 rows and below (too few waves per
+//    CU). Over whole rounds (3840 .. 8192 rows at H = 2560 .. 7168) 2-9%
+//    faster; with a last round a sixth to a half full 5-14% slower for the
+//    reads, while the completes were still 4-11% faster with their last round
+//    a third to a half full and 2-8% slower below that.
 int round_threads(int need) {
   const int unit = need >= 256 ? 4 * bnd::kWave : bnd::kWave;
   return ((need + unit - 1) / unit) * unit;
 }
 
-// The call's one-wavefront kernels: whether they exist, and the rows per CU
-// each width holds at once (0: never taken automatically).
+// The call's one-wavefront kernels: whether they exist, the rows per CU the
+// kernel of each width holds at once (0: never taken automatically), and how
+// full a launch's last round of resident rows must be, as a fraction
+// last_num / last_den of a round, for the automatic shape to take them.
 struct WaveFit {
   bool ok = false;
-  int rows_per_cu_8 = 0;
-  int rows_per_cu_14 = 0;
+  int rows_per_cu[bnd::kWaveWidths] = {};
+  int last_num = 1;
+  int last_den = 1;
 };
 
 WaveFit wave_fit_read(bnd::Source src, bool fp8) {
-  return {true, bnd::wave_read_rows_per_cu(src, fp8, bnd::kWaveVpt),
-          bnd::wave_read_rows_per_cu(src, fp8, bnd::kWaveVptWide)};
+  WaveFit f;
+  f.ok = true;
+  f.last_num = 3;
+  f.last_den = 4;
+  for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
+    f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_read_rows_per_cu(src, fp8, v);
+  return f;
 }
 
 WaveFit wave_fit_complete(bnd::Source src, bnd::Tail tail) {
-  return {true, bnd::wave_complete_rows_per_cu(src, tail, bnd::kWaveVpt),
-          bnd::wave_complete_rows_per_cu(src, tail, bnd::kWaveVptWide)};
+  WaveFit f;
+  f.ok = true;
+  f.last_num = 1;
+  f.last_den = 3;
+  for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
+    f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_complete_rows_per_cu(src, tail, v);
+  return f;
 }
 
 // The device queries the launch heuristic needs (CU count, the one-wavefront
@@ -215,7 +234,7 @@ void warm_launch_queries() {
   static std::once_flag once;
   std::call_once(once, [] {
     compute_units();
-    for (int w : {bnd::kWaveVpt, bnd::kWaveVptWide}) {
+    for (int w = bnd::kWaveVptMin; w <= bnd::kWaveVptMax; w += 2) {
       for (bool fp8 : {false, true}) {
         bnd::wave_read_rows_per_cu(Source::Partials, fp8, w);
         bnd::wave_read_rows_per_cu(Source::Moe, fp8, w);
@@ -228,19 +247,33 @@ void warm_launch_queries() {
   });
 }
 
+// Whether a launch of `rows` rows fills its rounds of `per_round` resident
+// rows well enough: one round always, more when the last one is at least
+// num / den full.
+bool rounds_fill(int64_t rows, int64_t per_round, int num, int den) {
+  if (per_round <= 0) return false;
+  if (rows <= per_round) return true;
+  const int64_t last = rows - (rows - 1) / per_round * per_round;  // rows of the last round, 1..per_round
+  return last * den >= per_round * num;
+}
+
 bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l) {
   const int nvec = (int)(H / 8);
   int vpt = g_vpt_override.load();
   int threads = g_threads_override.load();
+  const int one_wave_mode = g_one_wave_mode.load();
   const int64_t cus = compute_units();
-  if (vpt == 0) {
-    const bool many = rows >= 6 * cus;
-    if (many && nvec > (bnd::kWaveVpt - 1) * bnd::kWave && nvec <= bnd::kWaveVpt * bnd::kWave &&
-        rows <= wave.rows_per_cu_8 * cus) {
-      vpt = bnd::kWaveVpt;
-    } else if (many && nvec > (bnd::kWaveVptWide - 1) * bnd::kWave && nvec <= bnd::kWaveVptWide * bnd::kWave &&
-               rows <= wave.rows_per_cu_14 * cus) {
-      vpt = bnd::kWaveVptWide;
+  const int width = bnd::wave_width(nvec);  // the one-wavefront width that covers the row
+  bool one_wave = vpt > 4;                  // 6 .. 14 vectors per thread: one wavefront per row
+  if (vpt == 0 && one_wave_mode == BND_ONE_WAVEFRONT_ALWAYS) {
+    one_wave = true;
+    vpt = width;
+  } else if (vpt == 0) {
+    const int w = bnd::wave_slot(width);
+    if (one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && nvec > 3 * bnd::kWave &&
+        rows >= 6 * cus && rounds_fill(rows, wave.rows_per_cu[w] * cus, wave.last_num, wave.last_den)) {
+      one_wave = true;
+      vpt = width;
     } else if (nvec <= 256) {
       vpt = 1;
     } else if (nvec <= 1024 &&
@@ -250,21 +283,25 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
       vpt = nvec <= 2048 ? 2 : 4;
     }
   }
-  if (vpt == bnd::kWaveVpt || vpt == bnd::kWaveVptWide) {
+  if (one_wave) {
     if (!wave.ok)
       return fail(BND_ERR_NO_PATH,
-                  "%d vectors per thread (one wavefront per row) only takes the owed partials or MoE picks", vpt);
+                  "%d vectors per lane (one wavefront per row) only takes the owed partials or MoE picks", vpt);
+    if (bnd::wave_slot(vpt) < 0)
+      return fail(BND_ERR_NO_PATH, "one wavefront per row covers H <= %d, not H = %lld",
+                  bnd::kWaveVptMax * bnd::kWave * 8, (long long)H);
     if (nvec > vpt * bnd::kWave)
-      return fail(BND_ERR_NO_PATH, "%d vectors per thread (one wavefront per row) needs H <= %d", vpt,
+      return fail(BND_ERR_NO_PATH, "%d vectors per lane (one wavefront per row) needs H <= %d", vpt,
                   vpt * bnd::kWave * 8);
     if (threads != 0 && threads != bnd::kWave)
-      return fail(BND_ERR_NO_PATH, "%d vectors per thread (one wavefront per row) needs 64 threads, not %d", vpt,
+      return fail(BND_ERR_NO_PATH, "%d vectors per lane (one wavefront per row) needs 64 threads, not %d", vpt,
                   threads);
     threads = bnd::kWave;
   }
   if (threads == 0) threads = round_threads((nvec + vpt - 1) / vpt);
-  if (vpt != 1 && vpt != 2 && vpt != 4 && vpt != bnd::kWaveVpt && vpt != bnd::kWaveVptWide)
-    return fail(BND_ERR_NO_PATH, "vectors per thread %d: need 1, 2, 4, 8 or 14", vpt);
+  if (!one_wave && vpt != 1 && vpt != 2 && vpt != 4)
+    return fail(BND_ERR_NO_PATH, "vectors per thread %d: need 1, 2 or 4, or 6 .. 14 (even) for one wavefront "
+                "per row", vpt);
   if (threads < bnd::kWave || threads > bnd::kMaxThreads || threads % bnd::kWave != 0)
     return fail(BND_ERR_NO_PATH, "threads per row %d: need a multiple of 64 in [64, 1024]", threads);
   if ((int64_t)threads * vpt < nvec)
@@ -274,6 +311,7 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
   l->rows = (int)rows;
   l->threads = threads;
   l->vpt = vpt;
+  l->one_wave = one_wave;
   l->start = g_time_start;
   l->stop = g_time_stop;
   g_chosen = *l;
@@ -396,10 +434,11 @@ const char* bnd_last_error(void) { return g_last_error.c_str(); }
 
 const char* bnd_version(void) { return "libboundary 0.1 (gfx950)"; }
 
-bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_thread) {
+bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_thread, int* one_wavefront) {
   if (rows) *rows = g_last_launch.rows;
   if (threads) *threads = g_last_launch.threads;
   if (vectors_per_thread) *vectors_per_thread = g_last_launch.vpt;
+  if (one_wavefront) *one_wavefront = g_last_launch.one_wave ? 1 : 0;
   return ok();
 }
 
@@ -421,9 +460,14 @@ bnd_status bnd_set_option(bnd_option opt, int64_t value) {
       g_threads_override.store((int)value);
       return ok();
     case BND_OPT_VECTORS_PER_THREAD:
-      if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8 && value != 14)
-        return fail(BND_ERR_INVALID_ARG, "vectors per thread: 0, 1, 2, 4, 8 or 14");
+      if (value != 0 && value != 1 && value != 2 && value != 4 && (value < 6 || value > 14 || value % 2 != 0))
+        return fail(BND_ERR_INVALID_ARG, "vectors per thread: 0, 1, 2, 4, or 6 .. 14 (even)");
       g_vpt_override.store((int)value);
+      return ok();
+    case BND_OPT_ONE_WAVEFRONT:
+      if (value != BND_ONE_WAVEFRONT_AUTO && value != BND_ONE_WAVEFRONT_ALWAYS && value != BND_ONE_WAVEFRONT_NEVER)
+        return fail(BND_ERR_INVALID_ARG, "one-wavefront mode: 0 (automatic), 1 (always) or 2 (never)");
+      g_one_wave_mode.store((int)value);
       return ok();
   }
   return fail(BND_ERR_INVALID_ARG, "unknown option %d", (int)opt);
@@ -434,6 +478,7 @@ int64_t bnd_get_option(bnd_option opt) {
     case BND_OPT_FUSED_UNAVAILABLE: return fused_unavailable() ? 1 : 0;
     case BND_OPT_THREADS_PER_ROW: return g_threads_override.load();
     case BND_OPT_VECTORS_PER_THREAD: return g_vpt_override.load();
+    case BND_OPT_ONE_WAVEFRONT: return g_one_wave_mode.load();
   }
   return -1;
 }

@@ -1,7 +1,8 @@
 // complete_only and add_to_output (the owed sum of P partials or k MoE picks,
 // plus an optional extra row, stored bf16) and snapshot (residual plus the sum
-// of P partials, or a copy of the residual, stored bf16 into a separate output),
-// with the multi-wave row shapes or one wavefront per row.
+// of P partials, or a copy of the residual, stored bf16 into a separate output)
+// with several wavefronts per row; the one-wavefront forms are in
+// k_wave_complete.hip.
 #include "kernels.h"
 
 namespace bnd {
@@ -20,48 +21,10 @@ constexpr std::array<std::array<KernelFn, kMaxSources>, 3> kMoe = {
 constexpr KernelFn kCopy[3] = {&complete_kernel<Source::Residual, 0, 1, true>,
                                &complete_kernel<Source::Residual, 0, 2, true>,
                                &complete_kernel<Source::Residual, 0, 4, true>};
-template <int VPT>
-constexpr std::array<KernelFn, 5> wave_complete_table() {
-  return {{&wave_complete_kernel<Source::Partials, VPT, Tail::None>,
-           &wave_complete_kernel<Source::Partials, VPT, Tail::Extra>,
-           &wave_complete_kernel<Source::Partials, VPT, Tail::Residual>,
-           &wave_complete_kernel<Source::Moe, VPT, Tail::None>, &wave_complete_kernel<Source::Moe, VPT, Tail::Extra>}};
-}
-// [vectors per lane: 8, 14][partials: none, extra, residual; MoE picks: none, extra]
-constexpr std::array<KernelFn, 5> kWaveComplete[2] = {wave_complete_table<kWaveVpt>(),
-                                                      wave_complete_table<kWaveVptWide>()};
-
-// the table slot of a call, or -1 when it has no one-wavefront kernel
-int wave_kind(Source src, Tail tail) {
-  if (src == Source::Partials) return (int)tail;
-  if (src == Source::Moe && tail != Tail::Residual) return 3 + (int)tail;
-  return -1;
-}
-
-hipError_t launch_complete_wave(Source src, int n, Tail tail, const RowArgs& a, const Launch& l,
-                                hipStream_t stream) {
-  const bool wide = l.vpt == kWaveVptWide;
-  if ((l.vpt != kWaveVpt && !wide) || l.threads != kWave || a.nvec > kWave * l.vpt || n < 1 || n > kMaxSources)
-    return hipErrorInvalidValue;
-  const int kind = wave_kind(src, tail);
-  if (kind < 0) return hipErrorInvalidValue;
-  RowArgs b = a;
-  b.nsrc = n;
-  return launch_kernel(kWaveComplete[wide ? 1 : 0][kind], b, l, stream);
-}
-
-std::atomic<int> g_rows_per_cu[2][5];  // 0: not read yet, -1: unknown
 }  // namespace
 
-int wave_complete_rows_per_cu(Source src, Tail tail, int vpt) {
-  const int kind = wave_kind(src, tail);
-  if (kind < 0 || (vpt != kWaveVpt && vpt != kWaveVptWide)) return 0;
-  const int w = vpt == kWaveVptWide ? 1 : 0;
-  return occupancy_rows(kWaveComplete[w][kind], g_rows_per_cu[w][kind]);
-}
-
 hipError_t launch_complete(Source src, int n, bool fold, const RowArgs& a, const Launch& l, hipStream_t stream) {
-  if (l.vpt == kWaveVpt || l.vpt == kWaveVptWide)
+  if (l.one_wave)
     return launch_complete_wave(src, n, fold ? Tail::Residual : a.extra ? Tail::Extra : Tail::None, a, l, stream);
   const int slot = vpt_slot(l.vpt);
   if (slot < 0) return hipErrorInvalidValue;

@@ -6,7 +6,6 @@ namespace bnd {
 
 hipError_t launch_read_partials(int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream);
 hipError_t launch_read_moe(int n, const RowArgs& a, const Launch& l, hipStream_t stream);
-hipError_t launch_read_wave(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream);
 
 namespace {
 // [source: input, residual][vpt slot][bf16, fp8]
@@ -20,7 +19,7 @@ constexpr KernelFn kPlain[2][3][2] = {
 }  // namespace
 
 hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
-  if (l.vpt == kWaveVpt || l.vpt == kWaveVptWide) return launch_read_wave(src, n, fp8, a, l, stream);
+  if (l.one_wave) return launch_read_wave(src, n, fp8, a, l, stream);
   switch (src) {
     case Source::Partials:
       return launch_read_partials(n, fp8, a, l, stream);

@@ -435,8 +435,9 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
 
 // ---------------------------------------------------------------------------
 // The boundary read with one wavefront per row, for folds of partials or MoE
-// picks: 64 lanes x VPT vectors (VPT = 8: rows of up to 4096 elements, 121..153
-// VGPRs; VPT = 14: up to 7168, 209..255 VGPRs, two waves per SIMD).
+// picks: 64 lanes x VPT vectors, VPT an even count from 4 (rows of up to 2048
+// elements) to 14 (up to 7168; 209..255 VGPRs, two waves per SIMD); VPT = 8,
+// rows of up to 4096, takes 121..153 VGPRs.
 //
 // Used when a launch's rows just fit on the chip in one round (on 256 CUs:
 // the 2048-row prefill, quantised and MoE boundaries). What makes it faster

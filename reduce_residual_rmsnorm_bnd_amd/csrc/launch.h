@@ -10,10 +10,21 @@ namespace bnd {
 constexpr int kMaxSources = 16;
 constexpr int kMaxThreads = 1024;
 constexpr int kWave = 64;
-// vectors per lane of the one-wavefront-per-row read: 8 for rows of up to 4096
-// elements, 14 for rows of up to 7168
-constexpr int kWaveVpt = 8;
-constexpr int kWaveVptWide = 14;
+// Vectors per lane of the one-wavefront-per-row kernels: an even count from 4
+// to 14 (rows of up to 2048 .. 7168 elements), one kernel per width.
+constexpr int kWaveVptMin = 4;
+constexpr int kWaveVptMax = 14;
+constexpr int kWaveWidths = (kWaveVptMax - kWaveVptMin) / 2 + 1;
+// the table slot of a one-wavefront width, or -1 for a width without kernels
+constexpr int wave_slot(int vpt) {
+  return vpt >= kWaveVptMin && vpt <= kWaveVptMax && vpt % 2 == 0 ? (vpt - kWaveVptMin) / 2 : -1;
+}
+// the narrowest one-wavefront width whose 64 lanes cover a row of nvec vectors
+// (may exceed kWaveVptMax: no kernel then)
+constexpr int wave_width(int nvec) {
+  const int w = 2 * ((nvec + 2 * 64 - 1) / (2 * 64));
+  return w < kWaveVptMin ? kWaveVptMin : w;
+}
 
 // Arguments of one boundary launch. Every row pointer is already offset to
 // the first row the launch processes, so a kernel addresses row i of each
@@ -50,7 +61,8 @@ struct RowArgs {
 struct Launch {
   int rows = 0;     // grid size
   int threads = 0;  // workgroup size, multiple of 64
-  int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; 8 or 14 = one wavefront per row (threads = 64)
+  int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; for one wavefront per row 4 .. 14, even
+  bool one_wave = false;  // one wavefront per row (wave_read_kernel, wave_complete_kernel; threads = 64)
   hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
   hipEvent_t stop = nullptr;
 };
@@ -71,10 +83,16 @@ hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Laun
 hipError_t launch_complete(Source src, int n, bool fold, const RowArgs& a, const Launch& l,
                            hipStream_t stream);
 
+// One wavefront per row (l.one_wave): the read of a fold, or a complete.
+hipError_t launch_read_wave(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream);
+hipError_t launch_complete_wave(Source src, int n, Tail tail, const RowArgs& a, const Launch& l,
+                                hipStream_t stream);
+
 // Rows of one launch that a compute unit of the current device holds at once
-// with the one-wavefront read or complete kernel of vpt (8 or 14) vectors per
-// lane (its occupancy in 64-thread workgroups, from the HIP runtime, read once
-// per kernel); 0 when no such kernel exists or the runtime cannot tell.
+// with the one-wavefront read or complete kernel of vpt (4 .. 14, even)
+// vectors per lane (its occupancy in 64-thread workgroups, from the HIP
+// runtime, read once per kernel); 0 when no such kernel exists or the runtime
+// cannot tell.
 int wave_read_rows_per_cu(Source src, bool fp8, int vpt);
 int wave_complete_rows_per_cu(Source src, Tail tail, int vpt);
 

@@ -43,7 +43,8 @@ def fake(off=0):
 @pytest.fixture(autouse=True)
 def _reset_options():
     yield
-    for opt in (B.BND_OPT_FUSED_UNAVAILABLE, B.BND_OPT_THREADS_PER_ROW, B.BND_OPT_VECTORS_PER_THREAD):
+    for opt in (B.BND_OPT_FUSED_UNAVAILABLE, B.BND_OPT_THREADS_PER_ROW, B.BND_OPT_VECTORS_PER_THREAD,
+                B.BND_OPT_ONE_WAVEFRONT):
         L.bnd_set_option(opt, 0)
 
 
@@ -334,7 +335,8 @@ def test_rsv_share():
 def test_options_validation():
     for opt, bad in ((B.BND_OPT_FUSED_UNAVAILABLE, 2), (B.BND_OPT_THREADS_PER_ROW, 100),
                      (B.BND_OPT_THREADS_PER_ROW, 2048), (B.BND_OPT_VECTORS_PER_THREAD, 3),
-                     (B.BND_OPT_VECTORS_PER_THREAD, 16)):
+                     (B.BND_OPT_VECTORS_PER_THREAD, 5), (B.BND_OPT_VECTORS_PER_THREAD, 16),
+                     (B.BND_OPT_ONE_WAVEFRONT, 3), (B.BND_OPT_ONE_WAVEFRONT, -1)):
         assert L.bnd_set_option(opt, bad) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(99, 0) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(B.BND_OPT_THREADS_PER_ROW, 256) == 0
@@ -425,15 +427,16 @@ def test_last_launch_shape_before_any_launch():
     got = {}
 
     def probe():
-        rows, threads, vpt = ctypes.c_int64(-1), ctypes.c_int(-1), ctypes.c_int(-1)
-        got["st"] = L.bnd_last_launch_shape(ctypes.byref(rows), ctypes.byref(threads), ctypes.byref(vpt))
-        got["shape"] = (rows.value, threads.value, vpt.value)
-        got["null"] = L.bnd_last_launch_shape(None, None, None)
+        rows, threads, vpt, one = ctypes.c_int64(-1), ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_int(-1)
+        got["st"] = L.bnd_last_launch_shape(ctypes.byref(rows), ctypes.byref(threads), ctypes.byref(vpt),
+                                            ctypes.byref(one))
+        got["shape"] = (rows.value, threads.value, vpt.value, one.value)
+        got["null"] = L.bnd_last_launch_shape(None, None, None, None)
 
     t = threading.Thread(target=probe)
     t.start()
     t.join()
-    assert got == {"st": 0, "shape": (0, 0, 0), "null": 0}
+    assert got == {"st": 0, "shape": (0, 0, 0, 0), "null": 0}
 
 
 def test_size_limits_without_overflow():
@@ -459,3 +462,27 @@ def test_size_limits_without_overflow():
                              ctypes.byref(o)) == B.BND_ERR_INVALID_ARG
     assert L.bnd_stream_state(h) == B.BND_WRITTEN
     L.bnd_stream_destroy(h)
+
+
+def test_one_wavefront_modes():
+    assert L.bnd_get_option(B.BND_OPT_ONE_WAVEFRONT) == B.BND_ONE_WAVEFRONT_AUTO
+    for v in (B.BND_ONE_WAVEFRONT_ALWAYS, B.BND_ONE_WAVEFRONT_NEVER, B.BND_ONE_WAVEFRONT_AUTO):
+        assert L.bnd_set_option(B.BND_OPT_ONE_WAVEFRONT, v) == 0 and L.bnd_get_option(B.BND_OPT_ONE_WAVEFRONT) == v
+    for v in (6, 10, 12):  # the other one-wavefront widths are accepted as vectors per thread
+        assert L.bnd_set_option(B.BND_OPT_VECTORS_PER_THREAD, v) == 0
+    assert L.bnd_set_option(B.BND_OPT_VECTORS_PER_THREAD, 0) == 0
+    assert L.bnd_set_option(B.BND_OPT_ONE_WAVEFRONT, B.BND_ONE_WAVEFRONT_ALWAYS) == 0
+    # ALWAYS: a call without a one-wavefront kernel, or rows longer than 7168, is refused
+    h = create(T=8, rows=8)
+    st = L.bnd_enter_norm(h, fake(1 << 28), H, fake(1 << 31), 1e-6, fake(1 << 30), H, None)
+    assert st == B.BND_ERR_NO_PATH and b"wavefront" in L.bnd_last_error()
+    assert L.bnd_stream_state(h) == B.BND_INITIAL
+    wide = 7176
+    h = create(T=8, rows=4, ld=wide, Hh=wide)
+    assert L.bnd_written(h, fake(), wide) == 0
+    o = owed_out()
+    arr = (VP * 2)(*[fake((p + 1) << 24) for p in range(2)])
+    assert L.bnd_publish_partials(h, arr, 2, wide, ctypes.byref(o)) == 0
+    st = L.bnd_fold_norm(h, o.value, fake(1 << 31), 1e-6, fake(1 << 30), wide, None)
+    assert st == B.BND_ERR_NO_PATH and b"H <= 7168" in L.bnd_last_error()
+    _unchanged(h)

@@ -43,6 +43,24 @@ static int fails = 0;
 #define EXPECT(c) do { if (!(c)) { printf("line %d: %s: %s\n", __LINE__, #c, bnd_last_error()); ++fails; } } while (0)
 static void* fake(uint64_t k) { return (void*)(uintptr_t)(0x7F0000000000ull + (k << 36)); }
 
+// The automatic launch shape of a two-partial fold (or complete_only) over `rows` rows of H:
+// the one-wavefront width, 0 for a multi-wave shape, -1 on an error. With the stubs above a
+// round is 12 rows per CU at 8 vectors per lane and 8 elsewhere for the reads, 16 and 8 for
+// the completes, on the 256 CUs assumed without a device.
+static int auto_width(int64_t H, int64_t rows, bool complete) {
+  bnd_stream* s = nullptr;
+  bnd_owed o = BND_OWED_NONE, o2 = BND_OWED_NONE;
+  const void* parts[2] = {fake(4), fake(5)};
+  if (bnd_stream_create(&s, rows, H, 0, rows, fake(0), H) != BND_OK) return -1;
+  int rc = bnd_written(s, fake(0), H) | bnd_publish_partials(s, parts, 2, H, &o);
+  rc |= complete ? bnd_complete_only(s, o, fake(25), H, &o2, nullptr)
+                 : bnd_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr);
+  bnd_stream_destroy(s);
+  int64_t r = 0; int th = 0, v = 0, one = 0;
+  if (rc != BND_OK || bnd_last_launch_shape(&r, &th, &v, &one) != BND_OK || r != rows) return -1;
+  return one ? v : 0;
+}
+
 int main() {
   const int64_t H = 4096;
   bnd_owed o = BND_OWED_NONE, o2 = BND_OWED_NONE;
@@ -82,8 +100,27 @@ int main() {
   }
   int64_t counts[4] = {3, 0, 5, 2}, b = 0, n = 0, t = 0;
   EXPECT(bnd_rsv_share(counts, 4, 2, &b, &n, &t) == BND_OK && b == 3 && n == 5 && t == 10);
-  int64_t r = 0; int th = 0, v = 0;
-  EXPECT(bnd_last_launch_shape(&r, &th, &v) == BND_OK && r == 2048);
+  int64_t r = 0; int th = 0, v = 0, one = 0;
+  EXPECT(bnd_last_launch_shape(&r, &th, &v, &one) == BND_OK && r == 2048);
+  // one wavefront per row from 6 rows per CU, over one round or a last round full enough
+  EXPECT(auto_width(4096, 1535, false) == 0);
+  EXPECT(auto_width(4096, 1536, false) == 8);
+  EXPECT(auto_width(4096, 3072, false) == 8);     // one round of 3072
+  EXPECT(auto_width(4096, 4096, false) == 0);     // last round 1/3 full
+  EXPECT(auto_width(4096, 5375, false) == 0);     // just under 3/4
+  EXPECT(auto_width(4096, 5376, false) == 8);     // 3/4
+  EXPECT(auto_width(4096, 6144, false) == 8);     // two whole rounds
+  EXPECT(auto_width(7168, 3072, false) == 0);     // rounds of 2048: half full
+  EXPECT(auto_width(7168, 4096, false) == 14);
+  EXPECT(auto_width(2048, 2048, false) == 4);     // the narrowest width that covers the row
+  EXPECT(auto_width(5120, 2048, false) == 10);
+  EXPECT(auto_width(1536, 2048, false) == 0);     // 192 vectors: three per lane, too short
+  EXPECT(auto_width(8192, 2048, false) == 0);     // longer than 14 vectors per lane
+  EXPECT(auto_width(4096, 5461, true) == 0);      // complete rounds of 4096: just under 1/3
+  EXPECT(auto_width(4096, 5462, true) == 8);      // 1/3
+  EXPECT(auto_width(7168, 2560, true) == 0);      // rounds of 2048, 1/4 full
+  EXPECT(auto_width(7168, 2048 + 682, true) == 0);
+  EXPECT(auto_width(7168, 2048 + 683, true) == 14);
   printf("host walk: %d failures\n", fails);
   return fails ? 1 : 0;
 }

@@ -33,7 +33,7 @@ def orc():
 def _reset_options():
     yield
     for opt in (bnd.BND_OPT_FUSED_UNAVAILABLE, bnd.BND_OPT_THREADS_PER_ROW,
-                bnd.BND_OPT_VECTORS_PER_THREAD):
+                bnd.BND_OPT_VECTORS_PER_THREAD, bnd.BND_OPT_ONE_WAVEFRONT):
         bnd.set_option(opt, 0)
 
 
@@ -42,22 +42,34 @@ def bits(t):
 
 
 class forced_shape:
-    """Pin the launch shape (threads per row, vectors per thread) for a block of calls.
+    """Pin the launch shape (threads per row, vectors per thread) for a block of calls; with
+    one_wave, the one-wavefront mode instead (ALWAYS: the narrowest one-wavefront kernel that
+    covers H, which is how the 4-vector kernel is reached).
 
     The residual is elementwise and does not depend on the launch shape; the read's sum of
     squares is reduced in an order fixed by the shape, so comparisons of y between calls with
     different row counts are bit-exact only under one shape."""
 
-    def __init__(self, threads, vpt):
-        self.threads, self.vpt = threads, vpt
+    def __init__(self, threads, vpt, one_wave=bnd.BND_ONE_WAVEFRONT_AUTO):
+        self.threads, self.vpt, self.one_wave = threads, vpt, one_wave
 
     def __enter__(self):
         bnd.set_option(bnd.BND_OPT_THREADS_PER_ROW, self.threads)
         bnd.set_option(bnd.BND_OPT_VECTORS_PER_THREAD, self.vpt)
+        bnd.set_option(bnd.BND_OPT_ONE_WAVEFRONT, self.one_wave)
 
     def __exit__(self, *exc):
         bnd.set_option(bnd.BND_OPT_THREADS_PER_ROW, 0)
         bnd.set_option(bnd.BND_OPT_VECTORS_PER_THREAD, 0)
+        bnd.set_option(bnd.BND_OPT_ONE_WAVEFRONT, bnd.BND_ONE_WAVEFRONT_AUTO)
+
+
+def forced_wave(vpt):
+    """The one-wavefront kernel of `vpt` vectors per lane (4: through the ALWAYS mode, for rows
+    of up to 2048 elements)."""
+    if vpt == 4:
+        return forced_shape(0, 0, bnd.BND_ONE_WAVEFRONT_ALWAYS)
+    return forced_shape(64, vpt)
 
 
 class Guarded:
@@ -752,6 +764,15 @@ WAVE_SHAPES = [  # vectors per lane, T, H, P, pad, row_begin, rows
     (14, 9, 4104, 16, 0, 0, None),    # just above the narrow kernel's rows, sixteen sources
     (14, 3, 8, 1, 0, 0, None),
     (14, 40, 7168, 2, 16, 11, 25),
+    (4, 33, 2048, 8, 0, 0, None),
+    (4, 9, 1544, 3, 8, 2, 5),       # 193 vectors: one vector of the last lane column busy
+    (4, 5, 8, 16, 0, 0, None),
+    (6, 21, 3072, 5, 0, 0, None),
+    (6, 7, 2056, 16, 8, 1, 4),      # 257 vectors
+    (10, 15, 5120, 8, 0, 0, None),
+    (10, 9, 4104, 4, 16, 2, 6),
+    (12, 13, 6144, 8, 0, 0, None),
+    (12, 5, 5128, 2, 0, 0, None),
 ]
 
 
@@ -759,15 +780,19 @@ WAVE_SHAPES = [  # vectors per lane, T, H, P, pad, row_begin, rows
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
 def test_wave_rows(orc, vpt, T, H, P, pad, rb, rows, fp8):
     d = workloads.fold_inputs(300 + T + H + P, T, H, P)
-    with forced_shape(64, vpt):
+    with forced_wave(vpt):
         assert_fold_matches(orc, d, f"one wave per row x{vpt} T={T} H={H} P={P} slice={rb}+{rows}",
                             fp8=fp8, pad=pad, row_begin=rb, rows=rows)
+    assert bnd.last_launch_shape()[1:] == (64, vpt, True)
 
 
-@pytest.mark.parametrize("shape,H", [(WAVE, 4096), (WAVE_WIDE, 7168)], ids=["x8", "x14"])
-def test_wave_rows_edge_cases(orc, shape, H):
+WAVE_WIDTHS = [(8, 4096), (14, 7168), (4, 2048), (6, 3072), (10, 5120), (12, 6144)]
+
+
+@pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
+def test_wave_rows_edge_cases(orc, vpt, H):
     d = workloads.fold_inputs(31, 12, H, 3)
-    with forced_shape(*shape):
+    with forced_wave(vpt):
         assert_fold_matches(orc, d, "one wave per row, no residual", with_residual=False)
         assert_fold_matches(orc, d, "one wave per row, no residual fp8", with_residual=False, fp8=True)
         assert_fold_matches(orc, d, "one wave per row, Gemma weight", gemma=True)
@@ -779,17 +804,17 @@ def test_wave_rows_edge_cases(orc, shape, H):
         c[2].zero_()
         c[5, 17] = 3.0e4
     d["residual"][2].zero_()
-    with forced_shape(*shape):
+    with forced_wave(vpt):
         assert_fold_matches(orc, d, "one wave per row, zero and outlier rows")
         assert_fold_matches(orc, d, "one wave per row, zero and outlier rows fp8", fp8=True)
 
 
-@pytest.mark.parametrize("shape,H", [(WAVE, 4096), (WAVE_WIDE, 7168)], ids=["x8", "x14"])
-def test_wave_rows_residual_matches_other_shapes(orc, shape, H):
+@pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
+def test_wave_rows_residual_matches_other_shapes(orc, vpt, H):
     """The residual is elementwise: bitwise the same for every launch shape; y agrees with the
     oracle under each."""
     d = workloads.fold_inputs(32, 64, H, 8)
-    with forced_shape(*shape):
+    with forced_wave(vpt):
         a = run_fold(d)
     with forced_shape(512, 2):
         b = run_fold(d)
@@ -820,6 +845,11 @@ def test_wave_rows_moe(orc):
     dr = workloads.moe_inputs(38, 6, 5000, 8, 3)
     with forced_shape(*WAVE_WIDE):
         run_moe(orc, dr, 0, 6, "one wave per row x14, MoE k=3 H=5000")
+    for vpt, H in ((4, 2048), (6, 2600), (10, 5120), (12, 6104)):
+        dv = workloads.moe_inputs(40 + vpt, 20, H, 16, 8)
+        with forced_wave(vpt):
+            run_moe(orc, dv, 3, 15, f"one wave per row x{vpt}, MoE k=8 H={H}")
+        assert bnd.last_launch_shape()[1:] == (64, vpt, True)
 
 
 def test_wave_rows_moe_over_stacked_partials_is_fold(orc):
@@ -842,8 +872,9 @@ def test_wave_rows_moe_over_stacked_partials_is_fold(orc):
 
 
 def test_wave_rows_refused_where_no_kernel(orc):
-    """One wavefront per row exists only for folds with H <= 4096 (8 vectors per lane) or
-    H <= 7168 (14): other calls refuse it before launching anything."""
+    """One wavefront per row of a given width exists only for calls with owed work and rows it
+    covers (8 vectors per lane: H <= 4096, 14: H <= 7168); other calls refuse it before
+    launching anything, and so does the ALWAYS mode for rows longer than 7168."""
     d = workloads.fold_inputs(36, 4, 4104, 2)
     with forced_shape(*WAVE):
         with pytest.raises(bnd.BoundaryError) as e:
@@ -864,6 +895,16 @@ def test_wave_rows_refused_where_no_kernel(orc):
     torch.cuda.synchronize()
     res.check_guards("refused enter residual")
     y.check_guards("refused enter y")
+    d = workloads.fold_inputs(41, 4, 7176, 2)
+    with forced_shape(0, 0, bnd.BND_ONE_WAVEFRONT_ALWAYS):
+        with pytest.raises(bnd.BoundaryError) as e:
+            run_fold(d)
+        assert e.value.status == bnd.BND_ERR_NO_PATH
+    # NEVER keeps the multi-wave shapes even where the automatic choice takes one wavefront
+    d = workloads.fold_inputs(42, 2048, 4096, 2)
+    with forced_shape(0, 0, bnd.BND_ONE_WAVEFRONT_NEVER):
+        run_fold(d)
+    assert bnd.last_launch_shape()[3] is False
 
 
 # ------------------------------------------------------------------ one wavefront per row: complete
@@ -916,34 +957,40 @@ def _oracle_complete(orc, d, kind, *, row_begin=0, rows=None, extra=None, moe=Fa
     return c["s_exact"], c["mag"]
 
 
-WAVE_COMPLETE_SHAPES = [  # shape, T, H, P, row_begin, rows
-    (WAVE, 50, 4096, 8, 0, None),
-    (WAVE, 21, 3600, 1, 3, 15),      # one source: the stored pass is the only pass; ragged rows
-    (WAVE_WIDE, 30, 7168, 8, 0, None),
-    (WAVE_WIDE, 17, 6680, 3, 5, 9),
+WAVE_COMPLETE_SHAPES = [  # vectors per lane, T, H, P, row_begin, rows
+    (8, 50, 4096, 8, 0, None),
+    (8, 21, 3600, 1, 3, 15),      # one source: the stored pass is the only pass; ragged rows
+    (14, 30, 7168, 8, 0, None),
+    (14, 17, 6680, 3, 5, 9),
+    (4, 25, 2048, 8, 2, 20),
+    (4, 9, 1000, 1, 0, None),
+    (6, 11, 2600, 5, 0, None),
+    (10, 13, 5120, 8, 1, 10),
+    (12, 7, 6144, 2, 0, None),
 ]
 
 
-@pytest.mark.parametrize("shape,T,H,P,rb,rows", WAVE_COMPLETE_SHAPES)
+@pytest.mark.parametrize("vpt,T,H,P,rb,rows", WAVE_COMPLETE_SHAPES)
 @pytest.mark.parametrize("kind", ["complete_only", "add_to_output", "snapshot"])
-def test_wave_complete(orc, kind, shape, T, H, P, rb, rows):
+def test_wave_complete(orc, kind, vpt, T, H, P, rb, rows):
     """The one-wavefront complete against the oracle, and bitwise against the multi-wave shape
     (the sums run in the same order)."""
     d = workloads.fold_inputs(400 + T + P, T, H, P)
     extra = (workloads.to_bf16(workloads.normal_f32(400 + T, 12345, (T, H), 0.0, 0.25))
              if kind == "add_to_output" else None)
-    what = f"one wave per row x{shape[1]} {kind} T={T} H={H} P={P} slice={rb}+{rows}"
+    what = f"one wave per row x{vpt} {kind} T={T} H={H} P={P} slice={rb}+{rows}"
     print(f"\n  {what}", flush=True)
-    with forced_shape(*shape):
+    with forced_wave(vpt):
         a = _complete(d, kind, row_begin=rb, rows=rows, extra=extra)
+    assert bnd.last_launch_shape()[1:] == (64, vpt, True)
     b = _complete(d, kind, row_begin=rb, rows=rows, extra=extra)  # the automatic shape
     ex, mag = _oracle_complete(orc, d, kind, row_begin=rb, rows=rows, extra=extra)
     tolerance.check_bf16(bits(a.view), ex, mag, what)
     assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16)), f"{what}: differs from the other shape"
 
 
-@pytest.mark.parametrize("shape,H", [(WAVE, 4096), (WAVE_WIDE, 7168)], ids=["x8", "x14"])
-def test_wave_complete_moe(orc, shape, H):
+@pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
+def test_wave_complete_moe(orc, vpt, H):
     d = workloads.moe_inputs(410, 40, H, 16, 8)
     idx = d["idx"].clone()
     idx[5] = -1
@@ -951,34 +998,34 @@ def test_wave_complete_moe(orc, shape, H):
     d["idx"] = idx
     extra = workloads.to_bf16(workloads.normal_f32(410, 12345, (40, H), 0.0, 0.25))
     for kind, ex in (("complete_only", None), ("add_to_output", extra)):
-        what = f"one wave per row x{shape[1]} MoE {kind} H={H}"
-        with forced_shape(*shape):
+        what = f"one wave per row x{vpt} MoE {kind} H={H}"
+        with forced_wave(vpt):
             a = _complete(d, kind, row_begin=4, rows=30, extra=ex, moe=True)
         b = _complete(d, kind, row_begin=4, rows=30, extra=ex, moe=True)
         e, mag = _oracle_complete(orc, d, kind, row_begin=4, rows=30, extra=ex, moe=True)
         tolerance.check_bf16(bits(a.view), e, mag, what)
         assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16)), what
     d1 = workloads.moe_inputs(411, 6, H, 4, 1)  # one pick: the stored pass is the only pass
-    with forced_shape(*shape):
+    with forced_wave(vpt):
         a = _complete(d1, "complete_only", moe=True)
     e, mag = _oracle_complete(orc, d1, "complete_only", moe=True)
     tolerance.check_bf16(bits(a.view), e, mag, "one wave per row MoE k=1 complete_only")
 
 
-@pytest.mark.parametrize("shape,H", [(WAVE, 4096), (WAVE_WIDE, 7168)], ids=["x8", "x14"])
-def test_wave_complete_edge_cases(orc, shape, H):
+@pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
+def test_wave_complete_edge_cases(orc, vpt, H):
     d = workloads.fold_inputs(412, 12, H, 4)
     # signed zeros: sums of -0 store +0 under both shapes
     d["partials"] = [c.clone() for c in d["partials"]]
     for c in d["partials"]:
         c[3].fill_(-0.0)
-    with forced_shape(*shape):
+    with forced_wave(vpt):
         a = _complete(d, "complete_only")
     b = _complete(d, "complete_only")
     assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16))
     assert int((a.view[3].view(torch.int16) != 0).sum()) == 0, "a sum of -0 stores +0"
     # a snapshot of a Pending stream without a residual is bf16(s)
-    with forced_shape(*shape):
+    with forced_wave(vpt):
         a = _complete(d, "snapshot", with_residual=False)
     e, mag = _oracle_complete(orc, d, "snapshot", with_residual=False)
     tolerance.check_bf16(bits(a.view), e, mag, "snapshot without a residual")
@@ -987,7 +1034,7 @@ def test_wave_complete_edge_cases(orc, shape, H):
     out = Guarded(12, H)
     s = bnd.bnd_stream_create(12, H, res.view)
     bnd.bnd_written(s, res.view)
-    with forced_shape(*shape):
+    with forced_wave(vpt):
         with pytest.raises(bnd.BoundaryError) as e:
             bnd.bnd_snapshot(s, bnd.BND_OWED_NONE, out.view)
     assert e.value.status == bnd.BND_ERR_NO_PATH
@@ -997,11 +1044,12 @@ def test_wave_complete_edge_cases(orc, shape, H):
 
 
 def test_automatic_launch_shapes():
-    """The launch shapes the library picks for the benchmarked workloads on a 256-CU MI355X:
-    one wavefront per row where a launch's rows fit on the chip in one round."""
+    """The launch shapes the library picks on a 256-CU MI355X: one wavefront per row from 6 rows
+    per CU where a launch's rows fit on the chip in one round, or where its last round of
+    resident rows is full enough (3/4 for the reads, 1/3 for the completes)."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("shape expectations are for 256 compute units")
-    w = torch.ones(7168, device=DEV)
+    w = torch.ones(8192, device=DEV)
 
     def fold(T, H, P, fp8=False, kind="fold"):
         res = torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
@@ -1021,16 +1069,27 @@ def test_automatic_launch_shapes():
         torch.cuda.synchronize()
         return bnd.last_launch_shape()
 
-    assert fold(2048, 4096, 8) == (2048, 64, 8)                   # prefill boundary
-    assert fold(2048, 7168, 8, fp8=True) == (2048, 64, 14)        # quantised boundary
-    assert fold(2048, 4096, 8, kind="complete_only") == (2048, 64, 8)
-    assert fold(2048, 7168, 8, kind="snapshot") == (2048, 64, 14)
-    assert fold(1536, 4096, 8) == (1536, 64, 8)                   # 6 rows per CU
-    assert fold(1024, 4096, 8)[2] == 1                            # too few rows per CU
-    assert fold(128, 4096, 4)[2] == 1                             # a decode boundary
+    assert fold(2048, 4096, 8) == (2048, 64, 8, True)                   # prefill boundary
+    assert fold(2048, 7168, 8, fp8=True) == (2048, 64, 14, True)        # quantised boundary
+    assert fold(2048, 4096, 8, kind="complete_only") == (2048, 64, 8, True)
+    assert fold(2048, 7168, 8, kind="snapshot") == (2048, 64, 14, True)
+    assert fold(1536, 4096, 8) == (1536, 64, 8, True)                   # 6 rows per CU
+    assert fold(2048, 2048, 8) == (2048, 64, 4, True)                   # other hidden sizes
+    assert fold(2048, 5120, 8) == (2048, 64, 10, True)
+    assert fold(2048, 6144, 8) == (2048, 64, 12, True)
+    assert fold(4096, 7168, 8) == (4096, 64, 14, True)                  # two whole rounds of 2048
+    assert fold(6144, 4096, 8) == (6144, 64, 8, True)                   # two whole rounds of 3072
+    assert fold(3072, 7168, 8)[3] is False                              # last round half full
+    assert fold(4096, 4096, 8)[3] is False                              # last round a third full
+    assert fold(6144, 4096, 8, kind="complete_only") == (6144, 64, 8, True)  # rounds of 4096, 1/2
+    assert fold(3584, 7168, 8, kind="complete_only")[3] is False        # rounds of 3072, 1/6
+    assert fold(2048, 1024, 8)[3] is False                              # rows too short
+    assert fold(2048, 8192, 8)[3] is False                              # rows too long
+    assert fold(1024, 4096, 8)[3] is False                              # too few rows per CU
+    assert fold(128, 4096, 4)[3] is False                               # a decode boundary
     d = workloads.moe_inputs(5, 2048, 4096, 16, 8)
     E, idx, gate = _moe_device(d)
-    for rb, rows, shape in ((0, 2048, (2048, 64, 8)), (768, 256, (256, 512, 1))):
+    for rb, rows, shape in ((0, 2048, (2048, 64, 8, True)), (768, 256, (256, 512, 1, False))):
         res = torch.zeros(rows, 4096, dtype=torch.bfloat16, device=DEV)
         s = bnd.bnd_stream_create(2048, 4096, res, rb, rows)
         bnd.bnd_written(s, res)
@@ -1081,10 +1140,11 @@ def _random_case(i):
     for th, v in ((64, 8), (128, 4), (256, 2), (256, 4), (512, 1), (512, 2), (1024, 1), (1024, 2)):
         if th * v >= nvec:
             shapes.append((th, v))
-    if nvec <= 512:
-        shapes.append((64, 8))
+    for w in (6, 8, 10, 12, 14):  # one wavefront per row, every width that covers the row
+        if nvec <= 64 * w:
+            shapes.append((64, w))
     if nvec <= 896:
-        shapes.append((64, 14))
+        shapes.append((0, 0, bnd.BND_ONE_WAVEFRONT_ALWAYS))  # the narrowest width, 4 included
     shape = shapes[int(rng.integers(0, len(shapes)))]
     return kind, T, H, P, rb, rows, gemma, shape
 
@@ -1092,7 +1152,9 @@ def _random_case(i):
 @pytest.mark.parametrize("i", range(36))
 def test_random_cases(orc, i):
     kind, T, H, P, rb, rows, gemma, shape = _random_case(i)
-    what = f"case {i}: {kind} T={T} H={H} P/k={P} slice={rb}+{rows} gemma={gemma} shape={shape[0]}x{shape[1]}"
+    mode = " one-wavefront always" if len(shape) == 3 else ""
+    what = (f"case {i}: {kind} T={T} H={H} P/k={P} slice={rb}+{rows} gemma={gemma} "
+            f"shape={shape[0]}x{shape[1]}{mode}")
     print(f"\n  {what}", flush=True)
     with forced_shape(*shape):
         if kind in ("fold", "fp8"):
@@ -1139,7 +1201,7 @@ def test_graph_replay_of_every_hot_call():
     eager = buffers()
     chain(*eager)
     torch.cuda.synchronize()
-    assert bnd.last_launch_shape() == (T, 64, 8), "the chain runs the one-wavefront kernels"
+    assert bnd.last_launch_shape() == (T, 64, 8, True), "the chain runs the one-wavefront kernels"
     graph = buffers()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

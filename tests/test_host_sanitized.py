@@ -42,7 +42,7 @@ import test_abi_host as T
 L = B._lib
 
 def reset():
-    for opt in (1, 2, 3):
+    for opt in (1, 2, 3, 4):
         L.bnd_set_option(opt, 0)
 
 n = 0

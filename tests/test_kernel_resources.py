@@ -6,10 +6,9 @@ occupancy, so the fold and read kernels with one or two vectors per thread and u
 partial sources must stay within 64 VGPRs and never use scratch. A data-dependent branch around
 the Gemma weight offset once pushed the P = 8 fold to 100 VGPRs (half the resident rows, about
 a microsecond on the prefill boundary); this test fails on such a change before it reaches a
-benchmark. The one-wavefront-per-row read and complete kernels (8 or 14 vectors per lane, the
-source count a runtime argument) are chosen only while a launch's rows fit on the chip in one
-round, counted from their occupancy; they must keep at least two waves per SIMD (at most 256
-VGPRs), also without scratch.
+benchmark. The one-wavefront-per-row read and complete kernels (4 to 14 vectors per lane, even,
+the source count a runtime argument) are chosen from their occupancy (rows resident at once);
+they must keep at least two waves per SIMD (at most 256 VGPRs), also without scratch.
 """
 import os
 import re
@@ -73,23 +72,24 @@ def _resources(tmp_path, files):
 def resources(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not installed")
-    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip", "k_wave.hip", "k_complete.hip"])
+    return _resources(tmp_path_factory.mktemp("res"), ["k_partials.hip", "k_read.hip", "k_wave.hip",
+                                                       "k_wave_complete.hip"])
 
 
 def test_every_instance_reported(resources):
     # 16 source counts x 3 vector counts x bf16/fp8 for partials; 3 x 2 each for input and residual
     assert sum(1 for k in resources if k[0] == "Partials") == 96
     assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
-    # one wavefront per row: partials bf16 and fp8, MoE bf16, at 8 and 14 vectors per lane
+    # one wavefront per row: partials bf16 and fp8, MoE bf16, at 4, 6, ..., 14 vectors per lane
     waves = sorted((k[0], k[2], k[3]) for k in resources if k[0] in ("WavePartials", "WaveMoe"))
-    assert waves == sorted((kind, vpt, fp8) for vpt in (8, 14)
+    assert waves == sorted((kind, vpt, fp8) for vpt in range(4, 15, 2)
                            for kind, fp8 in (("WavePartials", False), ("WavePartials", True), ("WaveMoe", False))), waves
 
 
 def test_one_wave_completes_reported(resources):
     # partials with no tail, the extra row or the residual; MoE picks with no tail or the extra row
     got = sorted((k[0], k[1], k[2]) for k in resources if k[0].startswith("WaveComplete"))
-    assert got == sorted((kind, tail, vpt) for vpt in (8, 14) for kind, tail in (
+    assert got == sorted((kind, tail, vpt) for vpt in range(4, 15, 2) for kind, tail in (
         ("WaveCompletePartials", "None"), ("WaveCompletePartials", "Extra"), ("WaveCompletePartials", "Residual"),
         ("WaveCompleteMoe", "None"), ("WaveCompleteMoe", "Extra"))), got
 
