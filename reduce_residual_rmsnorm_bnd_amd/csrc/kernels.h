@@ -436,12 +436,12 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
 // ---------------------------------------------------------------------------
 // The boundary read with one wavefront per row, for folds of partials or MoE
 // picks: 64 lanes x VPT vectors, VPT an even count from 4 (rows of up to 2048
-// elements) to 14 (up to 7168; 209..255 VGPRs, two waves per SIMD); VPT = 8,
-// rows of up to 4096, takes 121..153 VGPRs.
+// elements) to 14 (up to 7168); 87..255 VGPRs, two to five waves per SIMD.
 //
-// Used when a launch's rows just fit on the chip in one round (on 256 CUs:
-// the 2048-row prefill, quantised and MoE boundaries). What makes it faster
-// there than the multi-wave rows of read_kernel, all measured on MI355X:
+// Used from 6 rows per CU when a launch's rows fill their rounds of resident
+// rows well (on 256 CUs: the 2048-row prefill, quantised and MoE boundaries).
+// What makes it faster there than the multi-wave rows of read_kernel, all
+// measured on MI355X:
 //  - loads go source by source (every vector of source 0, then of source 1,
 //    ..., the residual last), so a wave streams one contiguous row of one
 //    operand at a time; vector-major order is up to 25% slower;
