@@ -121,8 +121,9 @@ typedef uint64_t bnd_owed;
  * dimension ld_res); it holds no value until a read enters or folds.
  * The first call in a process also reads, once, the current device's CU count
  * and the occupancy of the one-wavefront kernels, which the launch shapes are
- * chosen from; no later call queries the device, so every hot call may run
- * under HIP graph capture.
+ * chosen from on every device the process uses (the devices are taken to be
+ * alike); no later call queries the device, so every hot call may run under
+ * HIP graph capture.
  * Errors: INVALID_ARG (out == NULL, T < 0, bad slice, residual NULL with
  * rows > 0, misaligned, ld_res), NO_PATH (H, T > BND_MAX_ROWS). */
 BND_API bnd_status bnd_stream_create(bnd_stream** out, int64_t T, int64_t H, int64_t row_begin,

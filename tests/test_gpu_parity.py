@@ -911,7 +911,7 @@ def test_wave_rows_refused_where_no_kernel(orc):
 
 def _complete(d, kind, *, row_begin=0, rows=None, extra=None, moe=False, with_residual=True):
     """complete_only / add_to_output / snapshot through the library under the current launch
-    shape; returns the guarded output and residual buffers."""
+    shape; checks that the residual is untouched and returns the guarded output buffer."""
     T, H = d["T"], d["H"]
     rows = T - row_begin if rows is None else rows
     res = Guarded(rows, H)
@@ -1041,6 +1041,29 @@ def test_wave_complete_edge_cases(orc, vpt, H):
     torch.cuda.synchronize()
     out.check_guards("refused snapshot")
     assert int((out.view.view(torch.int16) != CANARY16).sum()) == 0, "a refused call wrote its output"
+
+
+def test_wave_rows_over_several_rounds(orc):
+    """Launches for which the automatic shape takes one wavefront per row over more than one round
+    of resident rows, against the oracle on every row: a fold, an fp8 fold and a MoE finalize over
+    two whole rounds (4096 rows at H = 7168) and a complete_only whose last round is half full
+    (6144 rows at H = 4096)."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("round sizes are for 256 compute units")
+    d = workloads.fold_inputs(420, 4096, 7168, 3)
+    assert_fold_matches(orc, d, "fold T=4096 H=7168 P=3, two rounds")
+    assert bnd.last_launch_shape() == (4096, 64, 14, True)
+    assert_fold_matches(orc, d, "fp8 fold T=4096 H=7168 P=3, two rounds", fp8=True)
+    assert bnd.last_launch_shape() == (4096, 64, 14, True)
+    dm = workloads.moe_inputs(422, 4096, 7168, 16, 4)
+    run_moe(orc, dm, 0, 4096, "MoE finalize T=4096 H=7168 k=4, two rounds")
+    assert bnd.last_launch_shape() == (4096, 64, 14, True)
+    del dm
+    d = workloads.fold_inputs(421, 6144, 4096, 3)
+    out = _complete(d, "complete_only")
+    assert bnd.last_launch_shape() == (6144, 64, 8, True)
+    ex, mag = _oracle_complete(orc, d, "complete_only")
+    tolerance.check_bf16(bits(out.view), ex, mag, "complete_only T=6144 H=4096 P=3, 1.5 rounds")
 
 
 def test_automatic_launch_shapes():
