@@ -23,6 +23,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -108,6 +109,12 @@ class HipEvents:
         self.ev = []
 
 
+def nearest_rank(sorted_values, q: float) -> float:
+    """The q-quantile of an ascending list by the nearest-rank rule."""
+    n = len(sorted_values)
+    return sorted_values[min(n - 1, max(0, math.ceil(q * n) - 1))]
+
+
 class Timed:
     """Runs step(i, start, stop) K times. Every `sample_every`-th launch of the
     timed region records start/stop events from its own dispatch
@@ -150,7 +157,7 @@ class Timed:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         durs = sorted(ev.elapsed_s(2 * n, 2 * n + 1) for n in range(len(sampled)))
-        gaps = [ev.elapsed_s(2 * n, 2 * n + 2) / self.sample_every for n in range(len(sampled) - 1)]
+        gaps = sorted(ev.elapsed_s(2 * n, 2 * n + 2) / self.sample_every for n in range(len(sampled) - 1))
         ev.close()
         dispatch = sum(durs) / len(durs)
         interval = sum(gaps) / len(gaps)
@@ -159,6 +166,11 @@ class Timed:
             "kernel_s": min(dispatch, interval),
             "dispatch_event_mean_s": dispatch,
             "dispatch_event_median_s": durs[len(durs) // 2],
+            "dispatch_event_p10_s": nearest_rank(durs, 0.10),
+            "dispatch_event_p90_s": nearest_rank(durs, 0.90),
+            "interval_median_s": gaps[len(gaps) // 2],
+            "interval_p10_s": nearest_rank(gaps, 0.10),
+            "interval_p90_s": nearest_rank(gaps, 0.90),
             "dispatch_events": len(durs),
             "interval_mean_s": interval,
             "intervals": len(gaps),
@@ -177,7 +189,15 @@ def kernel_fields(t, bnd) -> dict:
     """Per-launch figures of a timed run, with the launch shape it used."""
     return {"launch": launch_desc(bnd), "kernel_us": t["kernel_s"] * 1e6,
             "dispatch_event_mean_us": t["dispatch_event_mean_s"] * 1e6,
-            "interval_us_per_launch": t["interval_mean_s"] * 1e6}
+            "interval_us_per_launch": t["interval_mean_s"] * 1e6,
+            **spread_fields(t)}
+
+
+def spread_fields(t) -> dict:
+    """Median, p10 and p90 of a timed run's sampled launches (start to stop) and of its per-launch
+    intervals, in microseconds."""
+    return {f"{k}_{q}_us": t[f"{k}_{q}_s"] * 1e6
+            for k in ("dispatch_event", "interval") for q in ("median", "p10", "p90")}
 
 
 def fold_case(torch, bnd, d, n_sets, fp8=False, row_begin=0, rows=None):
@@ -716,7 +736,7 @@ def main():
                                       "sampled launches' own start-to-stop, and start-to-start "
                                       "intervals between sampled launches / launches spanned",
                      "dispatch_event_mean_us": t["dispatch_event_mean_s"] * 1e6,
-                     "dispatch_event_median_us": t["dispatch_event_median_s"] * 1e6,
+                     **spread_fields(t),
                      "dispatch_events": t["dispatch_events"],
                      "interval_us_per_launch": t["interval_mean_s"] * 1e6,
                      "intervals": t["intervals"],
