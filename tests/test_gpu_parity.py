@@ -342,6 +342,23 @@ def test_launch_shapes(orc, threads, vpt):
     assert_fold_matches(orc, d, f"launch {threads}x{vpt} fp8", fp8=True)
 
 
+@pytest.mark.parametrize("mode", [bnd.BND_ONE_WAVEFRONT_NEVER, bnd.BND_ONE_WAVEFRONT_ALWAYS],
+                         ids=["multi_wave", "one_wave"])
+def test_many_rows(orc, mode):
+    """More rows than a 16-bit grid dimension holds (70001 rows of H = 64), under both launch
+    forms, against the oracle on every row: folds with bf16 and fp8 output and a MoE finalize."""
+    one = mode == bnd.BND_ONE_WAVEFRONT_ALWAYS
+    bnd.set_option(bnd.BND_OPT_ONE_WAVEFRONT, mode)
+    d = workloads.fold_inputs(430, 70001, 64, 2)
+    for fp8 in (False, True):
+        assert_fold_matches(orc, d, f"T=70001 H=64 P=2 {'fp8' if fp8 else 'bf16'} one_wave={one}", fp8=fp8)
+        rows, _, _, got_one = bnd.last_launch_shape()
+        assert rows == 70001 and got_one == one
+    dm = workloads.moe_inputs(431, 70001, 64, 8, 2)
+    run_moe(orc, dm, 0, 70001, f"MoE T=70001 H=64 k=2 one_wave={one}")
+    assert bnd.last_launch_shape()[3] == one
+
+
 def test_pending_without_residual(orc):
     d = workloads.fold_inputs(8, 12, 1024, 3)
     assert_fold_matches(orc, d, "no residual", with_residual=False)
