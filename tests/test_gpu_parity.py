@@ -1083,6 +1083,21 @@ def test_wave_rows_over_several_rounds(orc):
     tolerance.check_bf16(bits(out.view), ex, mag, "complete_only T=6144 H=4096 P=3, 1.5 rounds")
 
 
+def test_automatic_one_wave_at_its_shortest_rows(orc):
+    """The shortest rows the automatic shape gives one wavefront (H = 1544: 193 vectors, so only
+    lane 0 holds a fourth) and the longest it does not (H = 1536), at 6 rows per CU, against the
+    oracle."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the row count is 6 per CU on 256 compute units")
+    for H, one in ((1544, True), (1536, False)):
+        d = workloads.fold_inputs(424 + H, 1536, H, 3)
+        for fp8 in (False, True):
+            assert_fold_matches(orc, d, f"fold T=1536 H={H} P=3 fp8={fp8}", fp8=fp8)
+            assert bnd.last_launch_shape()[3] is one
+            if one:
+                assert bnd.last_launch_shape()[2] == 4
+
+
 def test_automatic_launch_shapes():
     """The launch shapes the library picks on a 256-CU MI355X: one wavefront per row from 6 rows
     per CU where a launch's rows fit on the chip in one round, or where its last round of
