@@ -42,12 +42,16 @@
  * taken here is the Gemma convention of a weight stored as an offset from
  * one: y_h = x_h * (1 + w_h) / sqrt(mean_h(x_h^2) + eps). `gemma` selects it.
  *
- * Quantised read (fp8): per row, scale = fp32(max_h |y_h| / 448) and
+ * Quantised read (fp8): per row, scale = max_h |y_h| / 448 and
  * q_h = e4m3(y_h / scale), OCP E4M3FN ("OFP8 Formats for Deep Learning",
  * OCP 8-bit floating point specification, 2023): bias 7, three mantissa
  * bits, largest finite 448, no infinities. A row with max |y| = 0 has scale 0
  * and all codes +0. The pages say only that the consumer input may be
- * quantised; this per-token reading is stated in the design notes.
+ * quantised; this per-token reading is stated in the design notes. They fix
+ * no precision for it, so the steps that decide a code run in the device's
+ * precision, fp32: y is rounded to fp32, the scale is one fp32 division of
+ * the largest |y| by 448, and each code is the e4m3 rounding of the fp32
+ * quotient y / scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -214,21 +218,24 @@ static void store_bf16_row(int64_t H, const double* v, uint16_t* out) {
   for (int64_t h = 0; h < H; ++h) out[h] = orc_bf16_round(v[h]);
 }
 
-/* Per-token fp8: scale = fp32(amax / 448), q = e4m3(clamp(y / scale)). */
+/* Per-token fp8, decided in fp32: y32 = fp32(y), scale = fp32(max |y32| / 448),
+ * q = e4m3(clamp(fp32(y32 / scale))). */
 static float store_fp8_row(int64_t H, const double* y, uint8_t* q) {
-  double amax = 0.0;
-  for (int64_t h = 0; h < H; ++h)
-    if (fabs(y[h]) > amax) amax = fabs(y[h]);
-  float scale = (float)(amax / 448.0);
+  float amax = 0.0f;
+  for (int64_t h = 0; h < H; ++h) {
+    const float a = fabsf((float)y[h]);
+    if (a > amax) amax = a;
+  }
+  const float scale = amax / 448.0f;
   for (int64_t h = 0; h < H; ++h) {
     if (scale == 0.0f) {
       q[h] = 0x00;
       continue;
     }
-    double v = y[h] / (double)scale;
-    if (v > 448.0) v = 448.0;
-    if (v < -448.0) v = -448.0;
-    q[h] = orc_e4m3_round(v);
+    float v = (float)y[h] / scale;
+    if (v > 448.0f) v = 448.0f;
+    if (v < -448.0f) v = -448.0f;
+    q[h] = orc_e4m3_round((double)v);
   }
   return scale;
 }

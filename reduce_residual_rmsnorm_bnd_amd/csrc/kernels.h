@@ -110,16 +110,30 @@ __device__ __forceinline__ uint2 f32_to_e4m3x8(const float f[8]) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
-// The e4m3 inputs of eight y values of a row: y / scale, clamped to +-448.
-// `rcp` is 1 / scale, and multiplying by it stands in for the division (one
-// reciprocal per row); a zero scale (a zero row) has rcp = 0 and gives +0
-// codes. A scale below 2^-128, which only a row of tiny (subnormal) weights
-// reaches, has no finite reciprocal: such a row takes kDivide, since y * inf
-// would give +-448 for small y and NaN for y = 0.
+// The e4m3 inputs of eight y values of a row: the fp32 quotient y / scale,
+// correctly rounded, clamped to +-448. `rcp` is the correctly rounded 1 /
+// scale (one division per row); q = y * rcp is then within one ulp of
+// y / scale, r = y - q * scale is exact as one fma, and q + r * rcp as one
+// fma is the correctly rounded quotient (P. Markstein, "Computation of
+// elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990), so a code is decided on the same fp32 value a division
+// gives, midpoints included. A zero scale (a zero row) has rcp = 0 and gives
+// +0 codes. A scale below 2^-128, which only a row of tiny (subnormal)
+// weights reaches, has no finite reciprocal: such a row takes kDivide, since
+// y * inf would give +-448 for small y and NaN for y = 0.
 template <bool kDivide>
 __device__ __forceinline__ void fp8_inputs(const float (&y)[8], float scale, float rcp, float (&t)[8]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = fminf(fmaxf(kDivide ? y[e] / scale : y[e] * rcp, -448.0f), 448.0f);
+  for (int e = 0; e < 8; ++e) {
+    float q;
+    if constexpr (kDivide) {
+      q = y[e] / scale;
+    } else {
+      q = y[e] * rcp;
+      q = fmaf(fmaf(-q, scale, y[e]), rcp, q);
+    }
+    t[e] = fminf(fmaxf(q, -448.0f), 448.0f);
+  }
 }
 
 __device__ __forceinline__ bool fp8_divide(float rcp) { return !(rcp <= 3.40282347e38f); }

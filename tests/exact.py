@@ -120,25 +120,37 @@ def boundary_row(r_bits, contrib: list[Fraction], w: list[float], eps: float):
     return x, inv, y
 
 
+def f32_round(v: Fraction) -> tuple[Fraction, Fraction]:
+    """Round to the nearest fp32 (ties to even, normal and subnormal range), decided exactly;
+    returns (value, distance from the nearest rounding tie in units of the fp32 step)."""
+    a = abs(v)
+    if a == 0:
+        return Fraction(0), Fraction(1)
+    e = max(_binade(a), -126)
+    step = Fraction(2) ** (e - 23)
+    r, tie_dist = _round_grid(a, step)
+    return (r if v > 0 else -r), tie_dist / step
+
+
 def fp8_row(y: list[Fraction]):
-    """scale = fp32(amax/448), q = e4m3(clamp(y/scale)); returns (scale, codes, min tie distance)."""
+    """The per-token fp8 read decided in fp32: y32 = fp32(y), scale = fp32(max|y32| / 448),
+    q = e4m3(clamp(fp32(y32 / scale))). The two fp32 divisions are IEEE single-precision
+    divisions (numpy float32); every rounding to fp32 or e4m3 is decided exactly. Returns
+    (scale, codes, the smallest distance of a y from an fp32 rounding tie, in fp32 steps)."""
     import numpy as np
 
-    amax = max(abs(v) for v in y)
-    q_amax = amax / 448
-    # single rounding of the exact quotient to fp32, decided exactly
-    scale_f = float(np.float32(float(q_amax)))
-    cands = [np.float32(scale_f), np.nextafter(np.float32(scale_f), np.float32(np.inf)),
-             np.nextafter(np.float32(scale_f), np.float32(0))]
-    scale = min(cands, key=lambda c: abs(Fraction(float(c)) - q_amax))
-    scale = float(scale)
-    if scale == 0.0:
-        return 0.0, [0] * len(y), Fraction(1)
-    codes, dmin = [], Fraction(10**9)
+    y32, tie = [], Fraction(10**9)
     for v in y:
-        t = v / Fraction(scale)
+        r, d = f32_round(v)
+        y32.append(r)
+        tie = min(tie, d)
+    amax = max(abs(v) for v in y32)
+    scale = float(np.float32(float(amax)) / np.float32(448.0))
+    if scale == 0.0:
+        return 0.0, [0] * len(y), tie
+    codes = []
+    for v in y32:
+        t = Fraction(float(np.float32(float(v)) / np.float32(scale)))
         t = min(max(t, Fraction(-448)), Fraction(448))
-        c, d = e4m3_round(t)
-        codes.append(c)
-        dmin = min(dmin, d)
-    return scale, codes, dmin
+        codes.append(e4m3_round(t)[0])
+    return scale, codes, tie

@@ -90,6 +90,17 @@ def pin_e5_fp8(o):
     assert list(out["q"][0]) == c["expect_codes"], [hex(v) for v in out["q"][0]]
 
 
+def pin_e8_fp8_decided_in_fp32(o):
+    """Codes of fp32 quotients that fall exactly on e4m3 midpoints, whose exact quotients lie
+    just off them: the decision is taken in fp32, as on the device."""
+    c = CASES["E8_fp8_decided_in_fp32"]
+    H = len(c["weight"])
+    out = o.fold_norm([bits([[0.0] * H])], bits([[1.0] * H]), f32(c["weight"]), c["eps"], fp8=True)
+    assert float(out["scale"][0]) == c["expect_scale"], out["scale"]
+    assert list(out["q"][0]) == c["expect_codes"], [hex(v) for v in out["q"][0]]
+    assert c["expect_codes"] != c["exact_quotient_codes"]
+
+
 def pin_e6_zero_row(o):
     c = CASES["E6_zero_row"]
     H = c["H"]
@@ -180,6 +191,7 @@ def pin_bruteforce_fold(o):
 
 def pin_bruteforce_fp8(o):
     eps = 1e-6
+    checked = 0
     for seed, T, H, P in [(21, 3, 16, 2), (22, 2, 8, 3), (23, 4, 16, 1), (24, 3, 16, 2)]:
         parts, res, w = _tiny_fold_case(seed, T, H, P, wide=(seed == 22))
         if seed == 24:  # subnormal weights: the scale is subnormal too (below 2^-128)
@@ -191,9 +203,14 @@ def pin_bruteforce_fp8(o):
             s = _exact_contrib_partials(parts, i, H)
             _, _, y = exact.boundary_row(res[i], s, list(w), eps)
             scale, codes, tie = exact.fp8_row(y)
-            assert float(out["scale"][i]) == scale, (seed, i, out["scale"][i], scale)
-            if tie > Fraction(1, 10**9):
+            # the oracle's fp64 y sits within ~1e-13 of the exact y: away from an fp32 rounding
+            # tie both round y to the same fp32 value, and from there every step is the same
+            # fp32 arithmetic, so scale and codes agree exactly
+            if tie > Fraction(1, 10**4):
+                assert float(out["scale"][i]) == scale, (seed, i, out["scale"][i], scale)
                 assert list(out["q"][i]) == codes, (seed, i)
+                checked += 1
+    assert checked >= 10, checked
 
 
 def _tiny_moe_case(seed, T, H, n_experts, k):
@@ -397,5 +414,6 @@ def pin_invariants(o):
 
 
 PINS = [pin_e1_closed_form, pin_e2_fold, pin_e3_eps_inside_root, pin_e4_one_hot, pin_e5_fp8,
+        pin_e8_fp8_decided_in_fp32,
         pin_e6_zero_row, pin_e7_gemma, pin_bruteforce_fold, pin_bruteforce_fp8, pin_bruteforce_moe,
         pin_bruteforce_complete, pin_add_to_output, pin_snapshot, pin_bf16_codec, pin_e4m3_codec, pin_invariants]

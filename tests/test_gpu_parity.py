@@ -1155,6 +1155,32 @@ def test_automatic_launch_shapes():
         assert bnd.last_launch_shape() == shape, (rb, rows)
 
 
+@pytest.mark.parametrize("mode", [bnd.BND_ONE_WAVEFRONT_NEVER, bnd.BND_ONE_WAVEFRONT_ALWAYS],
+                         ids=["multi_wave", "one_wave"])
+def test_fp8_codes_at_e4m3_midpoints(orc, mode):
+    """Rows whose fp32 quotients y / scale fall exactly on e4m3 midpoints while the exact quotients
+    lie just off them (the weights of the oracle's pinned case E8), on 64 rows x = 2^-32 .. 2^31
+    that each normalise to y = w exactly: the device takes every code from the correctly rounded
+    fp32 quotient, as the oracle does, so codes and scales match exactly, under both launch
+    forms."""
+    w = np.array([3.0, 0.007114955689758062, 0.01130022294819355, 0.012974330224096775,
+                  -0.010463169775903225, 1.0, -3.0, 0.0], np.float32)
+    T, H = 64, 8
+    res = torch.tensor([[2.0 ** (r - 32)] * H for r in range(T)], dtype=torch.float32).to(torch.bfloat16)
+    d = {"T": T, "H": H, "P": 1, "partials": [torch.zeros(T, H, dtype=torch.bfloat16)], "residual": res,
+         "weight": torch.from_numpy(w), "eps": 0.0}
+    bnd.set_option(bnd.BND_OPT_ONE_WAVEFRONT, mode)
+    got = run_fold(d, fp8=True)
+    assert bnd.last_launch_shape()[3] == (mode == bnd.BND_ONE_WAVEFRONT_ALWAYS)
+    ref = oracle_fold(orc, d, fp8=True)
+    got["q"].check_guards("midpoint q")
+    q = got["q"].view.cpu().numpy()
+    sc = got["scale_buf"].cpu().numpy()
+    assert sc[0] == -1.0 and sc[-1] == -1.0, "scale written outside its rows"
+    assert np.array_equal(sc[1:-1], ref["scale"]), (sc[1:-1], ref["scale"])
+    assert np.array_equal(q, ref["q"]), [[hex(int(v)) for v in row] for row in q[:2]]
+
+
 @pytest.mark.parametrize("shape", [(512, 2), (576, 1), (64, 14)], ids=["512x2", "576x1", "wave"])
 def test_fp8_subnormal_scale(orc, shape):
     """A row whose scale is subnormal has no finite reciprocal; the kernels divide by such a

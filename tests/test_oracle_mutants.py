@@ -46,8 +46,12 @@ MUTANTS = {
                       "r = n_r * step;\n  }\n  float f"),
     "e4m3_subnormal_step": ("if (e < -6) e = -6;", "if (e < -7) e = -7;"),
     "e4m3_bias": ("v = ldexp(1.0 + m / 8.0, e - 7);", "v = ldexp(1.0 + m / 8.0, e - 8);"),
-    "fnuz_max": ("float scale = (float)(amax / 448.0);", "float scale = (float)(amax / 240.0);"),
-    "scale_inverted": ("double v = y[h] / (double)scale;", "double v = y[h] * (double)scale;"),
+    "fnuz_max": ("const float scale = amax / 448.0f;", "const float scale = amax / 240.0f;"),
+    "scale_inverted": ("float v = (float)y[h] / scale;", "float v = (float)y[h] * scale;"),
+    "fp8_decided_in_fp64": ("float v = (float)y[h] / scale;\n    if (v > 448.0f) v = 448.0f;\n"
+                            "    if (v < -448.0f) v = -448.0f;",
+                            "double v = y[h] / (double)scale;\n    if (v > 448.0) v = 448.0;\n"
+                            "    if (v < -448.0) v = -448.0;"),
     "moe_index_ignored": ("int64_t e = idx[t * k + j];", "int64_t e = t * k + j;"),
     "extra_dropped": ("if (extra) add_extra_row(H, extra + (row_begin + i) * ld_x, b.s, b.mag);",
                       "(void)extra;"),
