@@ -889,9 +889,10 @@ def test_wave_rows_moe_over_stacked_partials_is_fold(orc):
 
 
 def test_wave_rows_refused_where_no_kernel(orc):
-    """One wavefront per row of a given width exists only for calls with owed work and rows it
-    covers (8 vectors per lane: H <= 4096, 14: H <= 7168); other calls refuse it before
-    launching anything, and so does the ALWAYS mode for rows longer than 7168."""
+    """One wavefront per row of a given width (4 to 14 vectors per lane, rows of up to 512 times
+    the width) exists only for calls with owed work and rows it covers: a forced width that does
+    not cover the row (8 for H = 4104, 14 for H = 7176) and a call without owed work are refused
+    before anything is launched, and so is the ALWAYS mode for rows longer than 7168."""
     d = workloads.fold_inputs(36, 4, 4104, 2)
     with forced_shape(*WAVE):
         with pytest.raises(bnd.BoundaryError) as e:
