@@ -1254,6 +1254,42 @@ def test_random_cases(orc, i):
             tolerance.check_bf16(bits(a.view), e, mag, what)
 
 
+def _auto_case(i):
+    """Case i of the seeded sweep at batch sizes where the automatic launch shape chooses between
+    one wavefront per row and several (1536 .. 4608 rows): kind, sizes and slice."""
+    rng = np.random.default_rng(7500 + i)
+    kind = ["fold", "fp8", "moe", "complete_only", "add_to_output", "snapshot"][i % 6]
+    H = int(rng.choice([1536, 1544, 2048, 2600, 3072, 4096, 5000, 6144, 7168]))
+    T = int(rng.integers(1536, 4609))
+    full = bool(rng.integers(0, 2))
+    rb = 0 if full else int(rng.integers(0, T // 4))
+    rows = T - rb if full else int(rng.integers(T // 2, T - rb + 1))
+    P = int(rng.integers(1, 9))
+    return kind, T, H, P, rb, rows
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_cases_automatic_shape(orc, i):
+    kind, T, H, P, rb, rows = _auto_case(i)
+    what = f"auto case {i}: {kind} T={T} H={H} P/k={P} slice={rb}+{rows}"
+    if kind in ("fold", "fp8"):
+        d = workloads.fold_inputs(8500 + i, T, H, P)
+        assert_fold_matches(orc, d, what, fp8=kind == "fp8", row_begin=rb, rows=rows)
+    elif kind == "moe":
+        d = workloads.moe_inputs(8500 + i, T, H, max(P, 2), P)
+        run_moe(orc, d, rb, rows, what)
+    else:
+        d = workloads.fold_inputs(8500 + i, T, H, P)
+        extra = (workloads.to_bf16(workloads.normal_f32(8500 + i, 12345, (T, H), 0.0, 0.25))
+                 if kind == "add_to_output" else None)
+        a = _complete(d, kind, row_begin=rb, rows=rows, extra=extra)
+        e, mag = _oracle_complete(orc, d, kind, row_begin=rb, rows=rows, extra=extra)
+        tolerance.check_bf16(bits(a.view), e, mag, what)
+    r, th, v, one = bnd.last_launch_shape()
+    assert r == rows
+    print(f"\n  {what}: launch {th}x{v}{' one wavefront' if one else ''}", flush=True)
+
+
 def test_graph_replay_of_every_hot_call():
     """enter, a fold, an fp8 fold, a MoE finalize, complete_only and a one-partial fold, all at
     2048 x 4096 (the one-wavefront kernels), captured once into a HIP graph and replayed several
