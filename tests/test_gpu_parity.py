@@ -1290,6 +1290,46 @@ def test_random_cases_automatic_shape(orc, i):
     print(f"\n  {what}: launch {th}x{v}{' one wavefront' if one else ''}", flush=True)
 
 
+def test_concurrent_threads_on_separate_streams(orc):
+    """Four host threads fold their own batches concurrently, each on its own HIP stream (default
+    priority), five times each: every result equals the same call made alone, bitwise, and the
+    lone calls match the oracle. The launch-shape state is per thread and the device queries are
+    made once, so the threads share nothing but the read-only kernel tables."""
+    import threading
+
+    ds = [workloads.fold_inputs(950 + i, 512 + 256 * i, 4096 - 1024 * (i % 2), 4) for i in range(4)]
+    alone = []
+    for i, d in enumerate(ds):
+        got, _ = assert_fold_matches(orc, d, f"thread batch {i} alone")
+        alone.append((bits(got["res"].view), bits(got["y"].view), bnd.last_launch_shape()))
+    torch.cuda.synchronize()
+    barrier = threading.Barrier(4)
+    errors = []
+
+    def worker(i):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                barrier.wait()
+                for rep in range(5):
+                    got = run_fold(ds[i])
+                    res, y = bits(got["res"].view), bits(got["y"].view)
+                    if not (np.array_equal(res, alone[i][0]) and np.array_equal(y, alone[i][1])):
+                        errors.append(f"thread {i} rep {rep}: differs from the call made alone")
+                    if bnd.last_launch_shape() != alone[i][2]:
+                        errors.append(f"thread {i} rep {rep}: launch shape {bnd.last_launch_shape()}")
+        except Exception as e:  # reported below, after every thread has ended
+            errors.append(f"thread {i}: {e!r}")
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in ts), "a worker thread did not finish"
+    assert not errors, errors
+
+
 def test_graph_replay_of_every_hot_call():
     """enter, a fold, an fp8 fold, a MoE finalize, complete_only and a one-partial fold, all at
     2048 x 4096 (the one-wavefront kernels), captured once into a HIP graph and replayed several
