@@ -177,9 +177,11 @@ int compute_units() {
 //    row (64 threads) when its rows hold 193..896 vectors (H = 1544..7168; the
 //    kernel of the narrowest even width of 4 to 14 vectors per lane that
 //    covers the row) and the launch has at least 6 rows per CU, unless its
-//    last round of resident rows would be mostly empty. A round is as many
-//    rows as the chip holds at once: the kernel's occupancy (its 52..255
-//    VGPRs hold 8 to 32 rows per CU) times the CUs. A launch of one round
+//    last round of resident rows would be mostly empty; so does a call on
+//    owed partials whose rows hold 97..128 vectors (H = 776..1024, the width
+//    of 2) from 12 rows per CU. A round is as many rows as the chip holds at
+//    once: the kernel's occupancy (its 34..255 VGPRs hold 8 to 32 rows per
+//    CU) times the CUs. A launch of one round
 //    always qualifies, a longer one when its last round is at least 3/4 full
 //    for the reads and at least 1/3 full for the completes (both fractions
 //    measured, below). Against the shapes above,
@@ -189,7 +191,12 @@ int compute_units() {
 //    CU). Over whole rounds (3840 .. 8192 rows at H = 2560 .. 7168) 2-9%
 //    faster; with a last round a sixth to a half full 5-14% slower for the
 //    reads, while the completes were still 4-11% faster with their last round
-//    a third to a half full and 2-8% slower below that.
+//    a third to a half full and 2-8% slower below that. The width of 2 at
+//    H = 896 .. 1024: 2-18% slower at 1536 rows, from 6% faster to 14% slower
+//    at 2048, from 7% faster to 2% slower at 3072 and 2-11% faster at 4096 and
+//    8192 for the folds and completes; the MoE finalize was 0-19% slower at
+//    every row count measured, and rows that fill half or three quarters of
+//    its lanes (H = 512, 768) were from 4% faster to 41% slower.
 int round_threads(int need) {
   const int unit = need >= 256 ? 4 * bnd::kWave : bnd::kWave;
   return ((need + unit - 1) / unit) * unit;
@@ -204,6 +211,7 @@ struct WaveFit {
   int rows_per_cu[bnd::kWaveWidths] = {};
   int last_num = 1;
   int last_den = 1;
+  bool narrow = false;  // whether the automatic shape may take the narrowest width, 2
 };
 
 WaveFit wave_fit_read(bnd::Source src, bool fp8) {
@@ -211,6 +219,7 @@ WaveFit wave_fit_read(bnd::Source src, bool fp8) {
   f.ok = true;
   f.last_num = 3;
   f.last_den = 4;
+  f.narrow = src == Source::Partials;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_read_rows_per_cu(src, fp8, v);
   return f;
@@ -221,6 +230,7 @@ WaveFit wave_fit_complete(bnd::Source src, bnd::Tail tail) {
   f.ok = true;
   f.last_num = 1;
   f.last_den = 3;
+  f.narrow = src == Source::Partials;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_complete_rows_per_cu(src, tail, v);
   return f;
@@ -264,14 +274,24 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
   const int one_wave_mode = g_one_wave_mode.load();
   const int64_t cus = compute_units();
   const int width = bnd::wave_width(nvec);  // the one-wavefront width that covers the row
-  bool one_wave = vpt > 4;                  // 6 .. 14 vectors per thread: one wavefront per row
-  if (vpt == 0 && one_wave_mode == BND_ONE_WAVEFRONT_ALWAYS) {
+  const bool forced = vpt != 0;
+  // A forced count of 6 .. 14 is one wavefront per row; under ALWAYS every
+  // forced count is (2 and 4 included); under NEVER none may be.
+  bool one_wave = forced && (vpt > 4 || one_wave_mode == BND_ONE_WAVEFRONT_ALWAYS);
+  if (one_wave && one_wave_mode == BND_ONE_WAVEFRONT_NEVER)
+    return fail(BND_ERR_NO_PATH, "%d vectors per thread is one wavefront per row, which is switched off", vpt);
+  if (!forced && one_wave_mode == BND_ONE_WAVEFRONT_ALWAYS) {
     one_wave = true;
     vpt = width;
-  } else if (vpt == 0) {
+  } else if (!forced) {
     const int w = bnd::wave_slot(width);
-    if (one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && nvec > 3 * bnd::kWave &&
-        rows >= 6 * cus && rounds_fill(rows, wave.rows_per_cu[w] * cus, wave.last_num, wave.last_den)) {
+    // The row must fill more than 3/4 of the width's lanes: 193 vectors or more for the widths of
+    // 4 and above, 97 .. 128 for width 2, which only the calls on owed partials take, from 12
+    // rows per CU (6 for the others).
+    const bool two = width == 2;
+    const bool fills = two ? wave.narrow && 4 * nvec > 3 * 2 * bnd::kWave : nvec > 3 * bnd::kWave;
+    if (one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && fills && rows >= (two ? 12 : 6) * cus &&
+        rounds_fill(rows, wave.rows_per_cu[w] * cus, wave.last_num, wave.last_den)) {
       one_wave = true;
       vpt = width;
     } else if (nvec <= 256) {
@@ -288,8 +308,10 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
       return fail(BND_ERR_NO_PATH,
                   "%d vectors per lane (one wavefront per row) only takes the owed partials or MoE picks", vpt);
     if (bnd::wave_slot(vpt) < 0)
-      return fail(BND_ERR_NO_PATH, "one wavefront per row covers H <= %d, not H = %lld",
-                  bnd::kWaveVptMax * bnd::kWave * 8, (long long)H);
+      return forced ? fail(BND_ERR_NO_PATH, "one wavefront per row takes %d .. %d (even) vectors per lane, not %d",
+                           bnd::kWaveVptMin, bnd::kWaveVptMax, vpt)
+                    : fail(BND_ERR_NO_PATH, "one wavefront per row covers H <= %d, not H = %lld",
+                           bnd::kWaveVptMax * bnd::kWave * 8, (long long)H);
     if (nvec > vpt * bnd::kWave)
       return fail(BND_ERR_NO_PATH, "%d vectors per lane (one wavefront per row) needs H <= %d", vpt,
                   vpt * bnd::kWave * 8);

@@ -1,4 +1,4 @@
-// Boundary reads with one wavefront per row (64 lanes x 4 .. 14 vectors):
+// Boundary reads with one wavefront per row (64 lanes x 2 .. 14 vectors):
 // folds of P plain partials with bf16 or fp8 output, and MoE finalize folds
 // of k gathered picks with bf16 output; P and k (1..16) are runtime values.
 #include "kernels.h"
@@ -11,11 +11,12 @@ constexpr std::array<KernelFn, 3> wave_read_row() {
   return {{&wave_read_kernel<Source::Partials, VPT, false>, &wave_read_kernel<Source::Partials, VPT, true>,
            &wave_read_kernel<Source::Moe, VPT, false>}};
 }
-// [width slot: 4, 6, ..., 14 vectors per lane][partials bf16, partials fp8, MoE bf16]
-constexpr std::array<KernelFn, 3> kWaveKernels[kWaveWidths] = {wave_read_row<4>(),  wave_read_row<6>(),
-                                                               wave_read_row<8>(),  wave_read_row<10>(),
-                                                               wave_read_row<12>(), wave_read_row<14>()};
-static_assert(kWaveWidths == 6 && wave_slot(14) == 5, "one table row per width");
+// [width slot: 2, 4, ..., 14 vectors per lane][partials bf16, partials fp8, MoE bf16]
+constexpr std::array<KernelFn, 3> kWaveKernels[kWaveWidths] = {wave_read_row<2>(),  wave_read_row<4>(),
+                                                               wave_read_row<6>(),  wave_read_row<8>(),
+                                                               wave_read_row<10>(), wave_read_row<12>(),
+                                                               wave_read_row<14>()};
+static_assert(kWaveWidths == 7 && wave_slot(2) == 0 && wave_slot(14) == 6, "one table row per width");
 
 // the table column of a call, or -1 when it has no one-wavefront kernel
 int wave_kind(Source src, bool fp8) {

@@ -449,11 +449,12 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
 
 // ---------------------------------------------------------------------------
 // The boundary read with one wavefront per row, for folds of partials or MoE
-// picks: 64 lanes x VPT vectors, VPT an even count from 4 (rows of up to 2048
-// elements) to 14 (up to 7168); 87..255 VGPRs, two to five waves per SIMD.
+// picks: 64 lanes x VPT vectors, VPT an even count from 2 (rows of up to 1024
+// elements) to 14 (up to 7168); 51..255 VGPRs, two to eight waves per SIMD.
 //
-// Used from 6 rows per CU when a launch's rows fill their rounds of resident
-// rows well (on 256 CUs: the 2048-row prefill, quantised and MoE boundaries).
+// Used from 6 rows per CU (12 at the width of 2) when a launch's rows fill
+// their rounds of resident rows well (on 256 CUs: the 2048-row prefill,
+// quantised and MoE boundaries).
 // What makes it faster there than the multi-wave rows of read_kernel, all
 // measured on MI355X:
 //  - loads go source by source (every vector of source 0, then of source 1,

@@ -10,9 +10,9 @@ namespace bnd {
 constexpr int kMaxSources = 16;
 constexpr int kMaxThreads = 1024;
 constexpr int kWave = 64;
-// Vectors per lane of the one-wavefront-per-row kernels: an even count from 4
-// to 14 (rows of up to 2048 .. 7168 elements), one kernel per width.
-constexpr int kWaveVptMin = 4;
+// Vectors per lane of the one-wavefront-per-row kernels: an even count from 2
+// to 14 (rows of up to 1024 .. 7168 elements), one kernel per width.
+constexpr int kWaveVptMin = 2;
 constexpr int kWaveVptMax = 14;
 constexpr int kWaveWidths = (kWaveVptMax - kWaveVptMin) / 2 + 1;
 // the table slot of a one-wavefront width, or -1 for a width without kernels
@@ -61,7 +61,7 @@ struct RowArgs {
 struct Launch {
   int rows = 0;     // grid size
   int threads = 0;  // workgroup size, multiple of 64
-  int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; for one wavefront per row 4 .. 14, even
+  int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; for one wavefront per row 2 .. 14, even
   bool one_wave = false;  // one wavefront per row (wave_read_kernel, wave_complete_kernel; threads = 64)
   hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
   hipEvent_t stop = nullptr;
@@ -89,7 +89,7 @@ hipError_t launch_complete_wave(Source src, int n, Tail tail, const RowArgs& a, 
                                 hipStream_t stream);
 
 // Rows of one launch that a compute unit of the current device holds at once
-// with the one-wavefront read or complete kernel of vpt (4 .. 14, even)
+// with the one-wavefront read or complete kernel of vpt (2 .. 14, even)
 // vectors per lane (its occupancy in 64-thread workgroups, from the HIP
 // runtime, read once per kernel); 0 when no such kernel exists or the runtime
 // cannot tell.

@@ -486,3 +486,17 @@ def test_one_wavefront_modes():
     st = L.bnd_fold_norm(h, o.value, fake(1 << 31), 1e-6, fake(1 << 30), wide, None)
     assert st == B.BND_ERR_NO_PATH and b"H <= 7168" in L.bnd_last_error()
     _unchanged(h)
+    # under ALWAYS a forced count names the width: an odd one is refused
+    h = create(T=8, rows=4)
+    assert L.bnd_written(h, fake(), H) == 0
+    arr = (VP * 2)(*[fake((p + 1) << 24) for p in range(2)])
+    assert L.bnd_publish_partials(h, arr, 2, H, ctypes.byref(o)) == 0
+    assert L.bnd_set_option(B.BND_OPT_VECTORS_PER_THREAD, 1) == 0
+    st = L.bnd_fold_norm(h, o.value, fake(1 << 31), 1e-6, fake(1 << 30), H, None)
+    assert st == B.BND_ERR_NO_PATH and b"2 .. 14 (even)" in L.bnd_last_error()
+    # under NEVER a one-wavefront count is refused
+    assert L.bnd_set_option(B.BND_OPT_ONE_WAVEFRONT, B.BND_ONE_WAVEFRONT_NEVER) == 0
+    assert L.bnd_set_option(B.BND_OPT_VECTORS_PER_THREAD, 8) == 0
+    st = L.bnd_fold_norm(h, o.value, fake(1 << 31), 1e-6, fake(1 << 30), H, None)
+    assert st == B.BND_ERR_NO_PATH and b"switched off" in L.bnd_last_error()
+    assert L.bnd_stream_state(h) == B.BND_PENDING

@@ -61,6 +61,20 @@ static int auto_width(int64_t H, int64_t rows, bool complete) {
   return one ? v : 0;
 }
 
+// The same for a MoE finalize (k = 2 picks per row).
+static int auto_width_moe(int64_t H, int64_t rows) {
+  bnd_stream* s = nullptr;
+  bnd_owed o = BND_OWED_NONE;
+  if (bnd_stream_create(&s, rows, H, 0, rows, fake(0), H) != BND_OK) return -1;
+  int rc = bnd_written(s, fake(0), H);
+  rc |= bnd_publish_moe(s, fake(26), 2 * rows, H, (const int32_t*)fake(27), (const float*)fake(28), 2, &o);
+  rc |= bnd_moe_finalize_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr);
+  bnd_stream_destroy(s);
+  int64_t r = 0; int th = 0, v = 0, one = 0;
+  if (rc != BND_OK || bnd_last_launch_shape(&r, &th, &v, &one) != BND_OK || r != rows) return -1;
+  return one ? v : 0;
+}
+
 int main() {
   const int64_t H = 4096;
   bnd_owed o = BND_OWED_NONE, o2 = BND_OWED_NONE;
@@ -121,6 +135,16 @@ int main() {
   EXPECT(auto_width(7168, 2560, true) == 0);      // rounds of 2048, 1/4 full
   EXPECT(auto_width(7168, 2048 + 682, true) == 0);
   EXPECT(auto_width(7168, 2048 + 683, true) == 14);
+  // width 2 (rounds of 2048 with the stubs): rows of 97..128 vectors, from 12 rows per CU
+  EXPECT(auto_width(1024, 3071, false) == 0);     // under 12 rows per CU
+  EXPECT(auto_width(1024, 4096, false) == 2);     // two whole rounds
+  EXPECT(auto_width(1024, 3072, false) == 0);     // last round half full
+  EXPECT(auto_width(776, 4096, false) == 2);      // 97 vectors
+  EXPECT(auto_width(768, 4096, false) == 0);      // 96 vectors: three quarters of the lanes
+  EXPECT(auto_width(1024, 4096, true) == 2);
+  EXPECT(auto_width(1032, 4096, false) == 0);     // 129 vectors: width 4, too few to fill it
+  EXPECT(auto_width_moe(1024, 4096) == 0);        // width 2 is not taken for MoE picks
+  EXPECT(auto_width_moe(4096, 2048) == 8);
   printf("host walk: %d failures\n", fails);
   return fails ? 1 : 0;
 }

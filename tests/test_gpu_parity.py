@@ -65,11 +65,9 @@ class forced_shape:
 
 
 def forced_wave(vpt):
-    """The one-wavefront kernel of `vpt` vectors per lane (4: through the ALWAYS mode, for rows
-    of up to 2048 elements)."""
-    if vpt == 4:
-        return forced_shape(0, 0, bnd.BND_ONE_WAVEFRONT_ALWAYS)
-    return forced_shape(64, vpt)
+    """The one-wavefront kernel of `vpt` vectors per lane (2 .. 14, even): under the ALWAYS mode a
+    forced count names the one-wavefront width."""
+    return forced_shape(64, vpt, bnd.BND_ONE_WAVEFRONT_ALWAYS)
 
 
 class Guarded:
@@ -790,6 +788,9 @@ WAVE_SHAPES = [  # vectors per lane, T, H, P, pad, row_begin, rows
     (10, 9, 4104, 4, 16, 2, 6),
     (12, 13, 6144, 8, 0, 0, None),
     (12, 5, 5128, 2, 0, 0, None),
+    (2, 33, 1024, 8, 0, 0, None),
+    (2, 9, 776, 3, 8, 2, 5),        # 97 vectors: one vector of the last lane column busy
+    (2, 5, 8, 16, 0, 0, None),
 ]
 
 
@@ -803,7 +804,7 @@ def test_wave_rows(orc, vpt, T, H, P, pad, rb, rows, fp8):
     assert bnd.last_launch_shape()[1:] == (64, vpt, True)
 
 
-WAVE_WIDTHS = [(8, 4096), (14, 7168), (4, 2048), (6, 3072), (10, 5120), (12, 6144)]
+WAVE_WIDTHS = [(8, 4096), (14, 7168), (4, 2048), (6, 3072), (10, 5120), (12, 6144), (2, 1024)]
 
 
 @pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
@@ -862,7 +863,7 @@ def test_wave_rows_moe(orc):
     dr = workloads.moe_inputs(38, 6, 5000, 8, 3)
     with forced_shape(*WAVE_WIDE):
         run_moe(orc, dr, 0, 6, "one wave per row x14, MoE k=3 H=5000")
-    for vpt, H in ((4, 2048), (6, 2600), (10, 5120), (12, 6104)):
+    for vpt, H in ((4, 2048), (6, 2600), (10, 5120), (12, 6104), (2, 1016)):
         dv = workloads.moe_inputs(40 + vpt, 20, H, 16, 8)
         with forced_wave(vpt):
             run_moe(orc, dv, 3, 15, f"one wave per row x{vpt}, MoE k=8 H={H}")
@@ -889,7 +890,7 @@ def test_wave_rows_moe_over_stacked_partials_is_fold(orc):
 
 
 def test_wave_rows_refused_where_no_kernel(orc):
-    """One wavefront per row of a given width (4 to 14 vectors per lane, rows of up to 512 times
+    """One wavefront per row of a given width (2 to 14 vectors per lane, rows of up to 512 times
     the width) exists only for calls with owed work and rows it covers: a forced width that does
     not cover the row (8 for H = 4104, 14 for H = 7176) and a call without owed work are refused
     before anything is launched, and so is the ALWAYS mode for rows longer than 7168."""
@@ -985,6 +986,8 @@ WAVE_COMPLETE_SHAPES = [  # vectors per lane, T, H, P, row_begin, rows
     (6, 11, 2600, 5, 0, None),
     (10, 13, 5120, 8, 1, 10),
     (12, 7, 6144, 2, 0, None),
+    (2, 19, 1024, 8, 1, 16),
+    (2, 6, 520, 1, 0, None),
 ]
 
 
@@ -1139,7 +1142,10 @@ def test_automatic_launch_shapes():
     assert fold(4096, 4096, 8)[3] is False                              # last round a third full
     assert fold(6144, 4096, 8, kind="complete_only") == (6144, 64, 8, True)  # rounds of 4096, 1/2
     assert fold(3584, 7168, 8, kind="complete_only")[3] is False        # rounds of 3072, 1/6
-    assert fold(2048, 1024, 8)[3] is False                              # rows too short
+    assert fold(4096, 1024, 8) == (4096, 64, 2, True)                   # width 2 from 12 rows per CU
+    assert fold(4096, 1024, 8, kind="complete_only") == (4096, 64, 2, True)
+    assert fold(2048, 1024, 8)[3] is False                              # width 2: too few rows
+    assert fold(4096, 768, 8)[3] is False                               # rows too short
     assert fold(2048, 8192, 8)[3] is False                              # rows too long
     assert fold(1024, 4096, 8)[3] is False                              # too few rows per CU
     assert fold(128, 4096, 4)[3] is False                               # a decode boundary
@@ -1154,6 +1160,16 @@ def test_automatic_launch_shapes():
                                                                              device=DEV))
         torch.cuda.synchronize()
         assert bnd.last_launch_shape() == shape, (rb, rows)
+    # the width of 2 is never taken for MoE picks
+    d = workloads.moe_inputs(6, 4096, 1024, 16, 8)
+    E, idx, gate = _moe_device(d)
+    res = torch.zeros(4096, 1024, dtype=torch.bfloat16, device=DEV)
+    s = bnd.bnd_stream_create(4096, 1024, res)
+    bnd.bnd_written(s, res)
+    bnd.bnd_moe_finalize_fold_norm(s, bnd.bnd_publish_moe(s, E, idx, gate, 8), w[:1024], 1e-6,
+                                   torch.empty(4096, 1024, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert bnd.last_launch_shape()[3] is False
 
 
 @pytest.mark.parametrize("mode", [bnd.BND_ONE_WAVEFRONT_NEVER, bnd.BND_ONE_WAVEFRONT_ALWAYS],

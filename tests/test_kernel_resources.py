@@ -82,14 +82,14 @@ def test_every_instance_reported(resources):
     assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
     # one wavefront per row: partials bf16 and fp8, MoE bf16, at 4, 6, ..., 14 vectors per lane
     waves = sorted((k[0], k[2], k[3]) for k in resources if k[0] in ("WavePartials", "WaveMoe"))
-    assert waves == sorted((kind, vpt, fp8) for vpt in range(4, 15, 2)
+    assert waves == sorted((kind, vpt, fp8) for vpt in range(2, 15, 2)
                            for kind, fp8 in (("WavePartials", False), ("WavePartials", True), ("WaveMoe", False))), waves
 
 
 def test_one_wave_completes_reported(resources):
     # partials with no tail, the extra row or the residual; MoE picks with no tail or the extra row
     got = sorted((k[0], k[1], k[2]) for k in resources if k[0].startswith("WaveComplete"))
-    assert got == sorted((kind, tail, vpt) for vpt in range(4, 15, 2) for kind, tail in (
+    assert got == sorted((kind, tail, vpt) for vpt in range(2, 15, 2) for kind, tail in (
         ("WaveCompletePartials", "None"), ("WaveCompletePartials", "Extra"), ("WaveCompletePartials", "Residual"),
         ("WaveCompleteMoe", "None"), ("WaveCompleteMoe", "Extra"))), got
 
