@@ -282,11 +282,11 @@ typedef enum bnd_option {
   BND_OPT_FUSED_UNAVAILABLE = 1,
   /* Launch shape overrides for tuning; 0 = automatic. Threads per row: a
    * multiple of 64 in [64, 1024]. Vectors (of 8 elements) per thread: 1, 2
-   * or 4 for rows of several wavefronts, or an even count 6 .. 14 for one
+   * or 4 for rows of several wavefronts, or an even count 6 .. 16 for one
    * wavefront per row with that many vectors per lane (64 threads; H up to
    * 64 * 8 times the count; only calls that take owed partials or MoE picks:
    * the folds, complete_only, add_to_output, and snapshot of a Pending
-   * stream). Under BND_ONE_WAVEFRONT_ALWAYS every forced count names the
+   * stream; 16 only for complete_only, add_to_output and snapshot). Under BND_ONE_WAVEFRONT_ALWAYS every forced count names the
    * one-wavefront width (2 and 4 included; an odd count fails); under
    * BND_ONE_WAVEFRONT_NEVER a count of 6 .. 14 fails. A shape that cannot
    * cover H, or a one-wavefront count for any other call, fails with
@@ -295,15 +295,17 @@ typedef enum bnd_option {
   BND_OPT_VECTORS_PER_THREAD = 3,
   /* When vectors per thread is automatic: BND_ONE_WAVEFRONT_AUTO (default)
    * takes one wavefront per row where it is measured faster: a call that
-   * takes owed work with rows of 1544 <= H <= 7168 and at least 6 rows per
-   * CU, or a call on owed partials with rows of 776 <= H <= 1024 and at
+   * takes owed work with rows of 1544 <= H <= 7168 (8192 for complete_only,
+   * add_to_output and snapshot) and at least 6 rows per CU, or a call on owed
+   * partials with rows of 776 <= H <= 1024 and at
    * least 12 rows per CU, and either no more rows than the kernel holds on
    * the chip at once or a last round of resident rows at least 3/4 full for
    * the folds and MoE finalize, 1/3 full for complete_only, add_to_output and
    * snapshot. ALWAYS requires it: every call runs its one-wavefront kernel of
-   * the narrowest width that covers H (2 .. 14 vectors per lane), and a call
-   * that has none (enter, the read of a Written stream, its snapshot) or rows
-   * longer than 7168 elements fails with NO_PATH; NEVER never takes it. */
+   * the narrowest width that covers H (2 .. 14 vectors per lane, 16 for the
+   * completes), and a call that has none (enter, the read of a Written
+   * stream, its snapshot) or rows longer than 7168 elements (8192 for the
+   * completes) fails with NO_PATH; NEVER never takes it. */
   BND_OPT_ONE_WAVEFRONT = 4
 } bnd_option;
 

@@ -174,9 +174,10 @@ int compute_units() {
 //    workgroups measured 3-6% slower than 8- or 4-wave ones);
 //  - a call that takes owed partials or MoE picks (the folds with bf16 or
 //    fp8 output, complete_only, add_to_output, snapshot) runs one wavefront per
-//    row (64 threads) when its rows hold 193..896 vectors (H = 1544..7168; the
-//    kernel of the narrowest even width of 4 to 14 vectors per lane that
-//    covers the row) and the launch has at least 6 rows per CU, unless its
+//    row (64 threads) when its rows hold 193..896 vectors (H = 1544..7168;
+//    1024 vectors, H = 8192, for the completes; the kernel of the narrowest
+//    even width of 4 to 14 (16) vectors per lane that covers the row) and the
+//    launch has at least 6 rows per CU, unless its
 //    last round of resident rows would be mostly empty; so does a call on
 //    owed partials whose rows hold 97..128 vectors (H = 776..1024, the width
 //    of 2) from 12 rows per CU. A round is as many rows as the chip holds at
@@ -212,6 +213,7 @@ struct WaveFit {
   int last_num = 1;
   int last_den = 1;
   bool narrow = false;  // whether the automatic shape may take the narrowest width, 2
+  int max_vpt = 0;      // the widest one-wavefront kernel of the call
 };
 
 WaveFit wave_fit_read(bnd::Source src, bool fp8) {
@@ -220,6 +222,7 @@ WaveFit wave_fit_read(bnd::Source src, bool fp8) {
   f.last_num = 3;
   f.last_den = 4;
   f.narrow = src == Source::Partials;
+  f.max_vpt = bnd::kWaveReadVptMax;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_read_rows_per_cu(src, fp8, v);
   return f;
@@ -231,6 +234,7 @@ WaveFit wave_fit_complete(bnd::Source src, bnd::Tail tail) {
   f.last_num = 1;
   f.last_den = 3;
   f.narrow = src == Source::Partials;
+  f.max_vpt = bnd::kWaveVptMax;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_complete_rows_per_cu(src, tail, v);
   return f;
@@ -290,7 +294,8 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
     // rows per CU (6 for the others).
     const bool two = width == 2;
     const bool fills = two ? wave.narrow && 4 * nvec > 3 * 2 * bnd::kWave : nvec > 3 * bnd::kWave;
-    if (one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && fills && rows >= (two ? 12 : 6) * cus &&
+    if (one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && width <= wave.max_vpt && fills &&
+        rows >= (two ? 12 : 6) * cus &&
         rounds_fill(rows, wave.rows_per_cu[w] * cus, wave.last_num, wave.last_den)) {
       one_wave = true;
       vpt = width;
@@ -307,11 +312,11 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
     if (!wave.ok)
       return fail(BND_ERR_NO_PATH,
                   "%d vectors per lane (one wavefront per row) only takes the owed partials or MoE picks", vpt);
-    if (bnd::wave_slot(vpt) < 0)
+    if (bnd::wave_slot(vpt) < 0 || vpt > wave.max_vpt)
       return forced ? fail(BND_ERR_NO_PATH, "one wavefront per row takes %d .. %d (even) vectors per lane, not %d",
-                           bnd::kWaveVptMin, bnd::kWaveVptMax, vpt)
+                           bnd::kWaveVptMin, wave.max_vpt, vpt)
                     : fail(BND_ERR_NO_PATH, "one wavefront per row covers H <= %d, not H = %lld",
-                           bnd::kWaveVptMax * bnd::kWave * 8, (long long)H);
+                           wave.max_vpt * bnd::kWave * 8, (long long)H);
     if (nvec > vpt * bnd::kWave)
       return fail(BND_ERR_NO_PATH, "%d vectors per lane (one wavefront per row) needs H <= %d", vpt,
                   vpt * bnd::kWave * 8);
@@ -322,7 +327,7 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
   }
   if (threads == 0) threads = round_threads((nvec + vpt - 1) / vpt);
   if (!one_wave && vpt != 1 && vpt != 2 && vpt != 4)
-    return fail(BND_ERR_NO_PATH, "vectors per thread %d: need 1, 2 or 4, or 6 .. 14 (even) for one wavefront "
+    return fail(BND_ERR_NO_PATH, "vectors per thread %d: need 1, 2 or 4, or 6 .. 16 (even) for one wavefront "
                 "per row", vpt);
   if (threads < bnd::kWave || threads > bnd::kMaxThreads || threads % bnd::kWave != 0)
     return fail(BND_ERR_NO_PATH, "threads per row %d: need a multiple of 64 in [64, 1024]", threads);
@@ -482,8 +487,8 @@ bnd_status bnd_set_option(bnd_option opt, int64_t value) {
       g_threads_override.store((int)value);
       return ok();
     case BND_OPT_VECTORS_PER_THREAD:
-      if (value != 0 && value != 1 && value != 2 && value != 4 && (value < 6 || value > 14 || value % 2 != 0))
-        return fail(BND_ERR_INVALID_ARG, "vectors per thread: 0, 1, 2, 4, or 6 .. 14 (even)");
+      if (value != 0 && value != 1 && value != 2 && value != 4 && (value < 6 || value > 16 || value % 2 != 0))
+        return fail(BND_ERR_INVALID_ARG, "vectors per thread: 0, 1, 2, 4, or 6 .. 16 (even)");
       g_vpt_override.store((int)value);
       return ok();
     case BND_OPT_ONE_WAVEFRONT:

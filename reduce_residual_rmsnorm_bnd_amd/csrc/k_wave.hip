@@ -12,11 +12,11 @@ constexpr std::array<KernelFn, 3> wave_read_row() {
            &wave_read_kernel<Source::Moe, VPT, false>}};
 }
 // [width slot: 2, 4, ..., 14 vectors per lane][partials bf16, partials fp8, MoE bf16]
-constexpr std::array<KernelFn, 3> kWaveKernels[kWaveWidths] = {wave_read_row<2>(),  wave_read_row<4>(),
-                                                               wave_read_row<6>(),  wave_read_row<8>(),
-                                                               wave_read_row<10>(), wave_read_row<12>(),
-                                                               wave_read_row<14>()};
-static_assert(kWaveWidths == 7 && wave_slot(2) == 0 && wave_slot(14) == 6, "one table row per width");
+constexpr std::array<KernelFn, 3> kWaveKernels[kWaveWidths] = {
+    wave_read_row<2>(),  wave_read_row<4>(),  wave_read_row<6>(),  wave_read_row<8>(),
+    wave_read_row<10>(), wave_read_row<12>(), wave_read_row<14>(), {{nullptr, nullptr, nullptr}}};
+static_assert(kWaveWidths == 8 && wave_slot(2) == 0 && wave_slot(kWaveReadVptMax) == 6,
+              "one table row per width, the last one empty");
 
 // the table column of a call, or -1 when it has no one-wavefront kernel
 int wave_kind(Source src, bool fp8) {
@@ -30,14 +30,14 @@ std::atomic<int> g_rows_per_cu[kWaveWidths][3];  // 0: not read yet, -1: unknown
 
 int wave_read_rows_per_cu(Source src, bool fp8, int vpt) {
   const int kind = wave_kind(src, fp8), w = wave_slot(vpt);
-  if (kind < 0 || w < 0) return 0;
+  if (kind < 0 || w < 0 || vpt > kWaveReadVptMax) return 0;
   return occupancy_rows(kWaveKernels[w][kind], g_rows_per_cu[w][kind]);
 }
 
 hipError_t launch_read_wave(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
   const int kind = wave_kind(src, fp8), w = wave_slot(l.vpt);
-  if (!l.one_wave || w < 0 || kind < 0 || l.threads != kWave || a.nvec > kWave * l.vpt || n < 1 ||
-      n > kMaxSources)
+  if (!l.one_wave || w < 0 || l.vpt > kWaveReadVptMax || kind < 0 || l.threads != kWave || a.nvec > kWave * l.vpt ||
+      n < 1 || n > kMaxSources)
     return hipErrorInvalidValue;
   RowArgs b = a;
   b.nsrc = n;

@@ -1,5 +1,5 @@
 // complete_only, add_to_output and snapshot with one wavefront per row
-// (64 lanes x 2 .. 14 vectors): the owed P partials or k MoE picks, then
+// (64 lanes x 2 .. 16 vectors): the owed P partials or k MoE picks, then
 // nothing, the extra row or the residual; P and k (1..16) are runtime values.
 #include "kernels.h"
 
@@ -13,11 +13,11 @@ constexpr std::array<KernelFn, 5> wave_complete_row() {
            &wave_complete_kernel<Source::Partials, VPT, Tail::Residual>,
            &wave_complete_kernel<Source::Moe, VPT, Tail::None>, &wave_complete_kernel<Source::Moe, VPT, Tail::Extra>}};
 }
-// [width slot: 2, 4, ..., 14 vectors per lane][partials: none, extra, residual; MoE picks: none, extra]
+// [width slot: 2, 4, ..., 16 vectors per lane][partials: none, extra, residual; MoE picks: none, extra]
 constexpr std::array<KernelFn, 5> kWaveComplete[kWaveWidths] = {
-    wave_complete_row<2>(),  wave_complete_row<4>(),  wave_complete_row<6>(), wave_complete_row<8>(),
-    wave_complete_row<10>(), wave_complete_row<12>(), wave_complete_row<14>()};
-static_assert(kWaveWidths == 7, "one table row per width");
+    wave_complete_row<2>(),  wave_complete_row<4>(),  wave_complete_row<6>(),  wave_complete_row<8>(),
+    wave_complete_row<10>(), wave_complete_row<12>(), wave_complete_row<14>(), wave_complete_row<16>()};
+static_assert(kWaveWidths == 8 && wave_slot(kWaveVptMax) == 7, "one table row per width");
 
 // the table column of a call, or -1 when it has no one-wavefront kernel
 int wave_kind(Source src, Tail tail) {

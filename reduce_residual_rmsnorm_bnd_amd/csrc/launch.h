@@ -11,9 +11,12 @@ constexpr int kMaxSources = 16;
 constexpr int kMaxThreads = 1024;
 constexpr int kWave = 64;
 // Vectors per lane of the one-wavefront-per-row kernels: an even count from 2
-// to 14 (rows of up to 1024 .. 7168 elements), one kernel per width.
+// to 14 for the reads (rows of up to 1024 .. 7168 elements) and to 16 for the
+// completes (up to 8192), one kernel per width. The tables have a slot for
+// every width up to kWaveVptMax; the reads leave the widest one empty.
 constexpr int kWaveVptMin = 2;
-constexpr int kWaveVptMax = 14;
+constexpr int kWaveReadVptMax = 14;
+constexpr int kWaveVptMax = 16;
 constexpr int kWaveWidths = (kWaveVptMax - kWaveVptMin) / 2 + 1;
 // the table slot of a one-wavefront width, or -1 for a width without kernels
 constexpr int wave_slot(int vpt) {

@@ -335,7 +335,7 @@ def test_rsv_share():
 def test_options_validation():
     for opt, bad in ((B.BND_OPT_FUSED_UNAVAILABLE, 2), (B.BND_OPT_THREADS_PER_ROW, 100),
                      (B.BND_OPT_THREADS_PER_ROW, 2048), (B.BND_OPT_VECTORS_PER_THREAD, 3),
-                     (B.BND_OPT_VECTORS_PER_THREAD, 5), (B.BND_OPT_VECTORS_PER_THREAD, 16),
+                     (B.BND_OPT_VECTORS_PER_THREAD, 5), (B.BND_OPT_VECTORS_PER_THREAD, 18),
                      (B.BND_OPT_ONE_WAVEFRONT, 3), (B.BND_OPT_ONE_WAVEFRONT, -1)):
         assert L.bnd_set_option(opt, bad) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(99, 0) == B.BND_ERR_INVALID_ARG

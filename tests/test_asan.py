@@ -143,6 +143,8 @@ int main() {
   EXPECT(auto_width(768, 4096, false) == 0);      // 96 vectors: three quarters of the lanes
   EXPECT(auto_width(1024, 4096, true) == 2);
   EXPECT(auto_width(1032, 4096, false) == 0);     // 129 vectors: width 4, too few to fill it
+  EXPECT(auto_width(8192, 2048, true) == 16);     // the completes go to 16 vectors per lane
+  EXPECT(auto_width(8200, 2048, true) == 0);
   EXPECT(auto_width_moe(1024, 4096) == 0);        // width 2 is not taken for MoE picks
   EXPECT(auto_width_moe(4096, 2048) == 8);
   printf("host walk: %d failures\n", fails);

@@ -805,6 +805,7 @@ def test_wave_rows(orc, vpt, T, H, P, pad, rb, rows, fp8):
 
 
 WAVE_WIDTHS = [(8, 4096), (14, 7168), (4, 2048), (6, 3072), (10, 5120), (12, 6144), (2, 1024)]
+WAVE_COMPLETE_WIDTHS = WAVE_WIDTHS + [(16, 8192)]  # the completes go one width further
 
 
 @pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
@@ -919,6 +920,12 @@ def test_wave_rows_refused_where_no_kernel(orc):
         with pytest.raises(bnd.BoundaryError) as e:
             run_fold(d)
         assert e.value.status == bnd.BND_ERR_NO_PATH
+    # the completes go to 8192 (16 vectors per lane) and no further
+    d = workloads.fold_inputs(43, 4, 8200, 2)
+    with forced_shape(0, 0, bnd.BND_ONE_WAVEFRONT_ALWAYS):
+        with pytest.raises(bnd.BoundaryError) as e:
+            _complete(d, "complete_only")
+        assert e.value.status == bnd.BND_ERR_NO_PATH and "8192" in str(e.value)
     # NEVER keeps the multi-wave shapes even where the automatic choice takes one wavefront
     d = workloads.fold_inputs(42, 2048, 4096, 2)
     with forced_shape(0, 0, bnd.BND_ONE_WAVEFRONT_NEVER):
@@ -988,6 +995,8 @@ WAVE_COMPLETE_SHAPES = [  # vectors per lane, T, H, P, row_begin, rows
     (12, 7, 6144, 2, 0, None),
     (2, 19, 1024, 8, 1, 16),
     (2, 6, 520, 1, 0, None),
+    (16, 12, 8192, 8, 0, None),
+    (16, 7, 7176, 3, 1, 5),       # 897 vectors: just past the reads' widest kernel
 ]
 
 
@@ -1010,7 +1019,7 @@ def test_wave_complete(orc, kind, vpt, T, H, P, rb, rows):
     assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16)), f"{what}: differs from the other shape"
 
 
-@pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
+@pytest.mark.parametrize("vpt,H", WAVE_COMPLETE_WIDTHS, ids=lambda v: str(v))
 def test_wave_complete_moe(orc, vpt, H):
     d = workloads.moe_inputs(410, 40, H, 16, 8)
     idx = d["idx"].clone()
@@ -1033,7 +1042,7 @@ def test_wave_complete_moe(orc, vpt, H):
     tolerance.check_bf16(bits(a.view), e, mag, "one wave per row MoE k=1 complete_only")
 
 
-@pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
+@pytest.mark.parametrize("vpt,H", WAVE_COMPLETE_WIDTHS, ids=lambda v: str(v))
 def test_wave_complete_edge_cases(orc, vpt, H):
     d = workloads.fold_inputs(412, 12, H, 4)
     # signed zeros: sums of -0 store +0 under both shapes
@@ -1146,7 +1155,9 @@ def test_automatic_launch_shapes():
     assert fold(4096, 1024, 8, kind="complete_only") == (4096, 64, 2, True)
     assert fold(2048, 1024, 8)[3] is False                              # width 2: too few rows
     assert fold(4096, 768, 8)[3] is False                               # rows too short
-    assert fold(2048, 8192, 8)[3] is False                              # rows too long
+    assert fold(2048, 8192, 8)[3] is False                              # rows too long for a read
+    assert fold(2048, 8192, 8, kind="complete_only") == (2048, 64, 16, True)
+    assert fold(2048, 8192, 8, kind="snapshot") == (2048, 64, 16, True)
     assert fold(1024, 4096, 8)[3] is False                              # too few rows per CU
     assert fold(128, 4096, 4)[3] is False                               # a decode boundary
     d = workloads.moe_inputs(5, 2048, 4096, 16, 8)

@@ -6,7 +6,7 @@ occupancy, so the fold and read kernels with one or two vectors per thread and u
 partial sources must stay within 64 VGPRs and never use scratch. A data-dependent branch around
 the Gemma weight offset once pushed the P = 8 fold to 100 VGPRs (half the resident rows, about
 a microsecond on the prefill boundary); this test fails on such a change before it reaches a
-benchmark. The one-wavefront-per-row read and complete kernels (4 to 14 vectors per lane, even,
+benchmark. The one-wavefront-per-row read and complete kernels (2 to 14 and 2 to 16 vectors per lane, even,
 the source count a runtime argument) are chosen from their occupancy (rows resident at once);
 they must keep at least two waves per SIMD (at most 256 VGPRs), also without scratch.
 """
@@ -89,7 +89,7 @@ def test_every_instance_reported(resources):
 def test_one_wave_completes_reported(resources):
     # partials with no tail, the extra row or the residual; MoE picks with no tail or the extra row
     got = sorted((k[0], k[1], k[2]) for k in resources if k[0].startswith("WaveComplete"))
-    assert got == sorted((kind, tail, vpt) for vpt in range(2, 15, 2) for kind, tail in (
+    assert got == sorted((kind, tail, vpt) for vpt in range(2, 17, 2) for kind, tail in (
         ("WaveCompletePartials", "None"), ("WaveCompletePartials", "Extra"), ("WaveCompletePartials", "Residual"),
         ("WaveCompleteMoe", "None"), ("WaveCompleteMoe", "Extra"))), got
 
