@@ -500,3 +500,20 @@ def test_one_wavefront_modes():
     st = L.bnd_fold_norm(h, o.value, fake(1 << 31), 1e-6, fake(1 << 30), H, None)
     assert st == B.BND_ERR_NO_PATH and b"switched off" in L.bnd_last_error()
     assert L.bnd_stream_state(h) == B.BND_PENDING
+
+
+def test_missing_library_raises():
+    """Without the built library the binding raises on first use; nothing falls back to the CPU."""
+    import subprocess
+    import sys
+    code = ("import reduce_residual_rmsnorm_bnd_amd.boundary as B\n"
+            "B.LIB_PATH = '/nonexistent/libboundary.so'\n"
+            "B._lib = None\n"
+            "try:\n"
+            "    B.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.startswith("raised:") and "is not built" in out.stdout
