@@ -279,7 +279,7 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
   const int64_t cus = compute_units();
   const int width = bnd::wave_width(nvec);  // the one-wavefront width that covers the row
   const bool forced = vpt != 0;
-  // A forced count of 6 .. 14 is one wavefront per row; under ALWAYS every
+  // A forced count of 6 .. 16 is one wavefront per row; under ALWAYS every
   // forced count is (2 and 4 included); under NEVER none may be.
   bool one_wave = forced && (vpt > 4 || one_wave_mode == BND_ONE_WAVEFRONT_ALWAYS);
   if (one_wave && one_wave_mode == BND_ONE_WAVEFRONT_NEVER)
