@@ -182,7 +182,8 @@ def launch_desc(bnd) -> dict:
     """The shape of this thread's last launch through the library, as the bench reports it."""
     rows, threads, vpt, one_wave = bnd.last_launch_shape()
     return {"workgroups": rows, "threads": threads, "vectors_per_thread": vpt,
-            "rows_per_workgroup": 1, "one_wavefront_per_row": one_wave}
+            "rows_per_workgroup": 1, "one_wavefront_per_row": one_wave,
+            "ring_depth": bnd.last_launch_ring_depth()}
 
 
 def kernel_fields(t, bnd) -> dict:

@@ -296,8 +296,9 @@ typedef enum bnd_option {
   /* When vectors per thread is automatic: BND_ONE_WAVEFRONT_AUTO (default)
    * takes one wavefront per row where it is measured faster: a call that
    * takes owed work with rows of 1544 <= H <= 7168 (8192 for complete_only,
-   * add_to_output and snapshot) and at least 6 rows per CU, or a call on owed
-   * partials with rows of 776 <= H <= 1024 and at
+   * add_to_output and snapshot) and at least 6 rows per CU (4 for rows of
+   * 3080 <= H <= 4096, which take the deep ring below 8 rows per CU; see
+   * BND_OPT_RING_DEPTH), or a call on owed partials with rows of 776 <= H <= 1024 and at
    * least 12 rows per CU, and either no more rows than the kernel holds on
    * the chip at once or a last round of resident rows at least 3/4 full for
    * the folds and MoE finalize, 1/3 full for complete_only, add_to_output and
@@ -306,7 +307,12 @@ typedef enum bnd_option {
    * completes), and a call that has none (enter, the read of a Written
    * stream, its snapshot) or rows longer than 7168 elements (8192 for the
    * completes) fails with NO_PATH; NEVER never takes it. */
-  BND_OPT_ONE_WAVEFRONT = 4
+  BND_OPT_ONE_WAVEFRONT = 4,
+  /* Loads each one-wavefront row keeps in flight: 0 = automatic (the deep
+   * ring of 8 for the 8-vector kernels, H = 3080 .. 4096, when a launch has 4
+   * to 7 rows per CU; 2 otherwise), 2, or 8 (only for a launch with one
+   * wavefront per row of 8 vectors per lane; NO_PATH for any other). */
+  BND_OPT_RING_DEPTH = 5
 } bnd_option;
 
 #define BND_ONE_WAVEFRONT_AUTO 0
@@ -324,6 +330,10 @@ BND_API int64_t bnd_get_option(bnd_option opt);
  * pointer may be NULL. Always BND_OK. */
 BND_API bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_thread,
                                          int* one_wavefront);
+/* The load ring depth of the calling thread's last launch through this
+ * library: 2 or 8 for one wavefront per row, 0 for several wavefronts (and
+ * before the thread's first launch). `depth` may be NULL. Always BND_OK. */
+BND_API bnd_status bnd_last_launch_ring_depth(int* depth);
 
 /* Timing: the calling thread's next kernel launch records `start_event` and
  * `stop_event` (hipEvent_t, created by the caller) from its own dispatch

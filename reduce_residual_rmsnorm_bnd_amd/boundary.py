@@ -45,6 +45,7 @@ BND_OPT_ONE_WAVEFRONT = 4
 BND_ONE_WAVEFRONT_AUTO = 0
 BND_ONE_WAVEFRONT_ALWAYS = 1
 BND_ONE_WAVEFRONT_NEVER = 2
+BND_OPT_RING_DEPTH = 5
 
 # exported symbols, in header order
 SYMBOLS = [
@@ -52,7 +53,8 @@ SYMBOLS = [
     "bnd_stream_has_residual", "bnd_stream_set_norm_form", "bnd_publish_partials", "bnd_publish_moe", "bnd_enter_norm",
     "bnd_fold_norm", "bnd_fold_norm_quant_fp8", "bnd_moe_finalize_fold_norm", "bnd_complete_only",
     "bnd_add_to_output", "bnd_snapshot", "bnd_rsv_share", "bnd_written", "bnd_take_output", "bnd_status_str", "bnd_last_error", "bnd_version",
-    "bnd_set_option", "bnd_get_option", "bnd_last_launch_shape", "bnd_time_next_launch",
+    "bnd_set_option", "bnd_get_option", "bnd_last_launch_shape", "bnd_last_launch_ring_depth",
+    "bnd_time_next_launch",
 ]
 
 _lib = None
@@ -96,6 +98,7 @@ def _declare(lib):
         "bnd_set_option": (st, [c.c_int, i64]),
         "bnd_get_option": (i64, [c.c_int]),
         "bnd_last_launch_shape": (st, [c.POINTER(i64), c.POINTER(i32), c.POINTER(i32), c.POINTER(i32)]),
+        "bnd_last_launch_ring_depth": (st, [c.POINTER(i32)]),
         "bnd_time_next_launch": (st, [vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -140,6 +143,14 @@ def last_launch_shape() -> tuple[int, int, int, bool]:
     _check(lib().bnd_last_launch_shape(ctypes.byref(rows), ctypes.byref(threads), ctypes.byref(vpt),
                                        ctypes.byref(one)))
     return rows.value, threads.value, vpt.value, bool(one.value)
+
+
+def last_launch_ring_depth() -> int:
+    """Loads in flight per one-wavefront row in this thread's last launch (2 or 8; 0 for a launch
+    with several wavefronts per row)."""
+    depth = ctypes.c_int()
+    _check(lib().bnd_last_launch_ring_depth(ctypes.byref(depth)))
+    return depth.value
 
 
 def _hip_stream(hip_stream):

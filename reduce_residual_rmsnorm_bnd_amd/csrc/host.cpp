@@ -63,6 +63,7 @@ std::atomic<int> g_fused_unavailable{-1};  // -1: read BND_DISABLE_FUSED on firs
 std::atomic<int> g_threads_override{0};
 std::atomic<int> g_vpt_override{0};
 std::atomic<int> g_one_wave_mode{BND_ONE_WAVEFRONT_AUTO};
+std::atomic<int> g_depth_override{0};
 thread_local hipEvent_t g_time_start = nullptr;  // consumed by the thread's next launch
 thread_local hipEvent_t g_time_stop = nullptr;
 thread_local Launch g_chosen;       // the shape of the launch being prepared
@@ -214,6 +215,7 @@ struct WaveFit {
   int last_den = 1;
   bool narrow = false;  // whether the automatic shape may take the narrowest width, 2
   int max_vpt = 0;      // the widest one-wavefront kernel of the call
+  int deep_rows_per_cu = 0;  // the same as rows_per_cu for the 8-wide kernel with the deep ring
 };
 
 WaveFit wave_fit_read(bnd::Source src, bool fp8) {
@@ -225,6 +227,7 @@ WaveFit wave_fit_read(bnd::Source src, bool fp8) {
   f.max_vpt = bnd::kWaveReadVptMax;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_read_rows_per_cu(src, fp8, v);
+  f.deep_rows_per_cu = bnd::wave_read_rows_per_cu(src, fp8, bnd::kWaveDeepVpt, true);
   return f;
 }
 
@@ -237,6 +240,7 @@ WaveFit wave_fit_complete(bnd::Source src, bnd::Tail tail) {
   f.max_vpt = bnd::kWaveVptMax;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_complete_rows_per_cu(src, tail, v);
+  f.deep_rows_per_cu = bnd::wave_complete_rows_per_cu(src, tail, bnd::kWaveDeepVpt, true);
   return f;
 }
 
@@ -258,6 +262,14 @@ void warm_launch_queries() {
         bnd::wave_complete_rows_per_cu(Source::Moe, t, w);
       }
     }
+    for (bool fp8 : {false, true}) {
+      bnd::wave_read_rows_per_cu(Source::Partials, fp8, bnd::kWaveDeepVpt, true);
+      bnd::wave_read_rows_per_cu(Source::Moe, fp8, bnd::kWaveDeepVpt, true);
+    }
+    for (bnd::Tail t : {bnd::Tail::None, bnd::Tail::Extra, bnd::Tail::Residual}) {
+      bnd::wave_complete_rows_per_cu(Source::Partials, t, bnd::kWaveDeepVpt, true);
+      bnd::wave_complete_rows_per_cu(Source::Moe, t, bnd::kWaveDeepVpt, true);
+    }
   });
 }
 
@@ -276,12 +288,14 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
   int vpt = g_vpt_override.load();
   int threads = g_threads_override.load();
   const int one_wave_mode = g_one_wave_mode.load();
+  const int depth = g_depth_override.load();
   const int64_t cus = compute_units();
   const int width = bnd::wave_width(nvec);  // the one-wavefront width that covers the row
   const bool forced = vpt != 0;
   // A forced count of 6 .. 16 is one wavefront per row; under ALWAYS every
   // forced count is (2 and 4 included); under NEVER none may be.
   bool one_wave = forced && (vpt > 4 || one_wave_mode == BND_ONE_WAVEFRONT_ALWAYS);
+  bool deep = false;
   if (one_wave && one_wave_mode == BND_ONE_WAVEFRONT_NEVER)
     return fail(BND_ERR_NO_PATH, "%d vectors per thread is one wavefront per row, which is switched off", vpt);
   if (!forced && one_wave_mode == BND_ONE_WAVEFRONT_ALWAYS) {
@@ -294,9 +308,17 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
     // rows per CU (6 for the others).
     const bool two = width == 2;
     const bool fills = two ? wave.narrow && 4 * nvec > 3 * 2 * bnd::kWave : nvec > 3 * bnd::kWave;
-    if (one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && width <= wave.max_vpt && fills &&
-        rows >= (two ? 12 : 6) * cus &&
-        rounds_fill(rows, wave.rows_per_cu[w] * cus, wave.last_num, wave.last_den)) {
+    // The 8-wide kernels with the deep ring take launches of 4 to 7 rows per CU (one round).
+    const bool deep_fits = width == bnd::kWaveDeepVpt && depth != 2 && rows >= 4 * cus && rows < 8 * cus &&
+                           rows <= (int64_t)wave.deep_rows_per_cu * cus;
+    const bool auto_wave = one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && width <= wave.max_vpt &&
+                           fills;
+    if (auto_wave && deep_fits) {
+      one_wave = true;
+      deep = true;
+      vpt = width;
+    } else if (auto_wave && rows >= (two ? 12 : 6) * cus &&
+               rounds_fill(rows, wave.rows_per_cu[w] * cus, wave.last_num, wave.last_den)) {
       one_wave = true;
       vpt = width;
     } else if (nvec <= 256) {
@@ -324,6 +346,14 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
       return fail(BND_ERR_NO_PATH, "%d vectors per lane (one wavefront per row) needs 64 threads, not %d", vpt,
                   threads);
     threads = bnd::kWave;
+    if (depth == bnd::kWaveDeepDepth) {
+      if (vpt != bnd::kWaveDeepVpt)
+        return fail(BND_ERR_NO_PATH, "the deep ring is built for %d vectors per lane, not %d", bnd::kWaveDeepVpt, vpt);
+      deep = true;
+    }
+  } else if (depth == bnd::kWaveDeepDepth) {
+    return fail(BND_ERR_NO_PATH, "the deep ring is for one wavefront per row; this launch has %d threads per row",
+                threads != 0 ? threads : round_threads((nvec + vpt - 1) / vpt));
   }
   if (threads == 0) threads = round_threads((nvec + vpt - 1) / vpt);
   if (!one_wave && vpt != 1 && vpt != 2 && vpt != 4)
@@ -339,6 +369,7 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
   l->threads = threads;
   l->vpt = vpt;
   l->one_wave = one_wave;
+  l->deep = deep;
   l->start = g_time_start;
   l->stop = g_time_stop;
   g_chosen = *l;
@@ -469,6 +500,11 @@ bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_t
   return ok();
 }
 
+bnd_status bnd_last_launch_ring_depth(int* depth) {
+  if (depth) *depth = g_last_launch.one_wave ? (g_last_launch.deep ? bnd::kWaveDeepDepth : 2) : 0;
+  return ok();
+}
+
 bnd_status bnd_time_next_launch(void* start_event, void* stop_event) {
   g_time_start = static_cast<hipEvent_t>(start_event);
   g_time_stop = static_cast<hipEvent_t>(stop_event);
@@ -496,6 +532,11 @@ bnd_status bnd_set_option(bnd_option opt, int64_t value) {
         return fail(BND_ERR_INVALID_ARG, "one-wavefront mode: 0 (automatic), 1 (always) or 2 (never)");
       g_one_wave_mode.store((int)value);
       return ok();
+    case BND_OPT_RING_DEPTH:
+      if (value != 0 && value != 2 && value != bnd::kWaveDeepDepth)
+        return fail(BND_ERR_INVALID_ARG, "ring depth: 0 (automatic), 2 or %d", bnd::kWaveDeepDepth);
+      g_depth_override.store((int)value);
+      return ok();
   }
   return fail(BND_ERR_INVALID_ARG, "unknown option %d", (int)opt);
 }
@@ -506,6 +547,7 @@ int64_t bnd_get_option(bnd_option opt) {
     case BND_OPT_THREADS_PER_ROW: return g_threads_override.load();
     case BND_OPT_VECTORS_PER_THREAD: return g_vpt_override.load();
     case BND_OPT_ONE_WAVEFRONT: return g_one_wave_mode.load();
+    case BND_OPT_RING_DEPTH: return g_depth_override.load();
   }
   return -1;
 }

@@ -18,6 +18,11 @@ constexpr std::array<KernelFn, 3> kWaveKernels[kWaveWidths] = {
 static_assert(kWaveWidths == 8 && wave_slot(2) == 0 && wave_slot(kWaveReadVptMax) == 6,
               "one table row per width, the last one empty");
 
+// the 8-wide kernels with the deep ring, by the same columns
+constexpr std::array<KernelFn, 3> kWaveDeep = {{&wave_read_kernel<Source::Partials, kWaveDeepVpt, false, kWaveDeepDepth>,
+                                                &wave_read_kernel<Source::Partials, kWaveDeepVpt, true, kWaveDeepDepth>,
+                                                &wave_read_kernel<Source::Moe, kWaveDeepVpt, false, kWaveDeepDepth>}};
+
 // the table column of a call, or -1 when it has no one-wavefront kernel
 int wave_kind(Source src, bool fp8) {
   if (src == Source::Partials) return fp8 ? 1 : 0;
@@ -26,22 +31,24 @@ int wave_kind(Source src, bool fp8) {
 }
 
 std::atomic<int> g_rows_per_cu[kWaveWidths][3];  // 0: not read yet, -1: unknown
+std::atomic<int> g_deep_rows_per_cu[3];
 }  // namespace
 
-int wave_read_rows_per_cu(Source src, bool fp8, int vpt) {
+int wave_read_rows_per_cu(Source src, bool fp8, int vpt, bool deep) {
   const int kind = wave_kind(src, fp8), w = wave_slot(vpt);
-  if (kind < 0 || w < 0 || vpt > kWaveReadVptMax) return 0;
+  if (kind < 0 || w < 0 || vpt > kWaveReadVptMax || (deep && vpt != kWaveDeepVpt)) return 0;
+  if (deep) return occupancy_rows(kWaveDeep[kind], g_deep_rows_per_cu[kind]);
   return occupancy_rows(kWaveKernels[w][kind], g_rows_per_cu[w][kind]);
 }
 
 hipError_t launch_read_wave(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
   const int kind = wave_kind(src, fp8), w = wave_slot(l.vpt);
   if (!l.one_wave || w < 0 || l.vpt > kWaveReadVptMax || kind < 0 || l.threads != kWave || a.nvec > kWave * l.vpt ||
-      n < 1 || n > kMaxSources)
+      n < 1 || n > kMaxSources || (l.deep && l.vpt != kWaveDeepVpt))
     return hipErrorInvalidValue;
   RowArgs b = a;
   b.nsrc = n;
-  return launch_kernel(kWaveKernels[w][kind], b, l, stream);
+  return launch_kernel(l.deep ? kWaveDeep[kind] : kWaveKernels[w][kind], b, l, stream);
 }
 
 }  // namespace bnd

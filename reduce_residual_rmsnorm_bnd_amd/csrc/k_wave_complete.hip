@@ -19,6 +19,14 @@ constexpr std::array<KernelFn, 5> kWaveComplete[kWaveWidths] = {
     wave_complete_row<10>(), wave_complete_row<12>(), wave_complete_row<14>(), wave_complete_row<16>()};
 static_assert(kWaveWidths == 8 && wave_slot(kWaveVptMax) == 7, "one table row per width");
 
+// the 8-wide kernels with the deep ring, by the same columns
+constexpr std::array<KernelFn, 5> kWaveCompleteDeep = {
+    {&wave_complete_kernel<Source::Partials, kWaveDeepVpt, Tail::None, kWaveDeepDepth>,
+     &wave_complete_kernel<Source::Partials, kWaveDeepVpt, Tail::Extra, kWaveDeepDepth>,
+     &wave_complete_kernel<Source::Partials, kWaveDeepVpt, Tail::Residual, kWaveDeepDepth>,
+     &wave_complete_kernel<Source::Moe, kWaveDeepVpt, Tail::None, kWaveDeepDepth>,
+     &wave_complete_kernel<Source::Moe, kWaveDeepVpt, Tail::Extra, kWaveDeepDepth>}};
+
 // the table column of a call, or -1 when it has no one-wavefront kernel
 int wave_kind(Source src, Tail tail) {
   if (src == Source::Partials) return (int)tail;
@@ -27,11 +35,13 @@ int wave_kind(Source src, Tail tail) {
 }
 
 std::atomic<int> g_rows_per_cu[kWaveWidths][5];  // 0: not read yet, -1: unknown
+std::atomic<int> g_deep_rows_per_cu[5];
 }  // namespace
 
-int wave_complete_rows_per_cu(Source src, Tail tail, int vpt) {
+int wave_complete_rows_per_cu(Source src, Tail tail, int vpt, bool deep) {
   const int kind = wave_kind(src, tail), w = wave_slot(vpt);
-  if (kind < 0 || w < 0) return 0;
+  if (kind < 0 || w < 0 || (deep && vpt != kWaveDeepVpt)) return 0;
+  if (deep) return occupancy_rows(kWaveCompleteDeep[kind], g_deep_rows_per_cu[kind]);
   return occupancy_rows(kWaveComplete[w][kind], g_rows_per_cu[w][kind]);
 }
 
@@ -39,11 +49,11 @@ hipError_t launch_complete_wave(Source src, int n, Tail tail, const RowArgs& a, 
                                 hipStream_t stream) {
   const int kind = wave_kind(src, tail), w = wave_slot(l.vpt);
   if (!l.one_wave || w < 0 || kind < 0 || l.threads != kWave || a.nvec > kWave * l.vpt || n < 1 ||
-      n > kMaxSources)
+      n > kMaxSources || (l.deep && l.vpt != kWaveDeepVpt))
     return hipErrorInvalidValue;
   RowArgs b = a;
   b.nsrc = n;
-  return launch_kernel(kWaveComplete[w][kind], b, l, stream);
+  return launch_kernel(l.deep ? kWaveCompleteDeep[kind] : kWaveComplete[w][kind], b, l, stream);
 }
 
 }  // namespace bnd

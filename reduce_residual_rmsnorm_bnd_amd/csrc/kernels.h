@@ -474,11 +474,14 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
 // residual is bitwise the same as with read_kernel; y = (x w) inv, and the
 // fp8 codes are those of (x w) inv times the reciprocal of the row's scale.
 // ---------------------------------------------------------------------------
-// Loads each wave keeps in flight through its ring, per width: a divisor of
-// the width, so that the ring slot of a load is its vector index modulo the
-// depth whatever the source. Two at every width: deeper rings measured 3-5%
-// faster at 4096 rows for the 4- and 6-wide reads but 1-2% slower at 2048,
-// and up to 10% slower for the 12-wide read.
+// Loads each wave keeps in flight through its ring by default, per width: a
+// divisor of the width, so that the ring slot of a load is its vector index
+// modulo the depth whatever the source. Two at every width: deeper rings
+// measured 3-5% faster at 4096 rows for the 4- and 6-wide reads but 1-2%
+// slower at 2048, and up to 10% slower for the 12-wide read. The kernels take
+// the depth as a template argument; the 8-wide ones are also built with every
+// vector of a source in flight (depth 8), which the host takes for launches
+// of 4 to 7 rows per CU, where two loads per wave leave the memory idle.
 constexpr int wave_depth(int) { return 2; }
 
 // One source row of the fold: its resource (empty for an invalid MoE pick or a
@@ -556,10 +559,9 @@ __device__ __forceinline__ void add_source(float g, const float (&t)[8], float (
   }
 }
 
-template <Source S, int VPT, bool kFirst>
-__device__ __forceinline__ void fold_source(const RowSource& cur, const RowSource& next, int lane,
-                                            uint4 (&ring)[wave_depth(VPT)], float (&x)[VPT][8]) {
-  constexpr int D = wave_depth(VPT);
+template <Source S, int VPT, bool kFirst, int D>
+__device__ __forceinline__ void fold_source(const RowSource& cur, const RowSource& next, int lane, uint4 (&ring)[D],
+                                            float (&x)[VPT][8]) {
   static_assert(VPT % D == 0, "ring slots follow the vector index");
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
@@ -573,7 +575,7 @@ __device__ __forceinline__ void fold_source(const RowSource& cur, const RowSourc
   }
 }
 
-template <Source S, int VPT, bool FP8>
+template <Source S, int VPT, bool FP8, int D = wave_depth(VPT)>
 __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
   static_assert(S == Source::Partials || S == Source::Moe, "one-wave rows fold partials or MoE picks");
   const int64_t row = blockIdx.x;
@@ -583,7 +585,6 @@ __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
   const Rsrc res = row_rsrc(a.res + row * a.ld_res, a.H * 2);
   const float offset = a.gemma ? 1.0f : 0.0f;
 
-  constexpr int D = wave_depth(VPT);
   uint4 ring[D];
   u32x4 wlo[D], whi[D];
   const RowPicks picks = row_picks<S>(a, row, lane);
@@ -693,13 +694,12 @@ __device__ __forceinline__ RowSource complete_source(const RowArgs& a, const Row
 }
 
 // The last source's pass: add it and store every vector as soon as it is final.
-template <Source S, int VPT, bool kFirst, Tail kTail>
-__device__ __forceinline__ void store_source(const RowSource& cur, int lane, uint4 (&ring)[wave_depth(VPT)],
-                                             float (&x)[VPT][8], const Rsrc& out) {
+template <Source S, int VPT, bool kFirst, Tail kTail, int D>
+__device__ __forceinline__ void store_source(const RowSource& cur, int lane, uint4 (&ring)[D], float (&x)[VPT][8],
+                                             const Rsrc& out) {
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     float t[8];
-    constexpr int D = wave_depth(VPT);
     bf16x8_to_f32(ring[v % D], t);
     if (v + D < VPT) ring[v % D] = load16(cur.r, (lane + (v + D) * kWave) * 16);
     if constexpr (kTail == Tail::Extra) {
@@ -719,7 +719,7 @@ __device__ __forceinline__ void store_source(const RowSource& cur, int lane, uin
   }
 }
 
-template <Source S, int VPT, Tail kTail>
+template <Source S, int VPT, Tail kTail, int D = wave_depth(VPT)>
 __global__ __launch_bounds__(kWave) void wave_complete_kernel(const RowArgs a) {
   static_assert(S == Source::Partials || S == Source::Moe, "one-wave rows complete partials or MoE picks");
   static_assert(kTail != Tail::Residual || S == Source::Partials, "a snapshot folds partials");
@@ -730,7 +730,6 @@ __global__ __launch_bounds__(kWave) void wave_complete_kernel(const RowArgs a) {
   const Rsrc out = row_rsrc(a.y + row * a.ld_y, a.H * 2);
   const RowPicks picks = row_picks<S>(a, row, lane);
 
-  constexpr int D = wave_depth(VPT);
   uint4 ring[D];
   RowSource cur = complete_source<S, kTail>(a, picks, row, 0);
   RowSource next = complete_source<S, kTail>(a, picks, row, 1);

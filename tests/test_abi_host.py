@@ -44,7 +44,7 @@ def fake(off=0):
 def _reset_options():
     yield
     for opt in (B.BND_OPT_FUSED_UNAVAILABLE, B.BND_OPT_THREADS_PER_ROW, B.BND_OPT_VECTORS_PER_THREAD,
-                B.BND_OPT_ONE_WAVEFRONT):
+                B.BND_OPT_ONE_WAVEFRONT, B.BND_OPT_RING_DEPTH):
         L.bnd_set_option(opt, 0)
 
 
@@ -64,7 +64,7 @@ def owed_out():
 
 def test_library_exports_every_declared_symbol():
     decl = re.findall(r"^BND_API\s+[\w\s\*]+?\b(bnd_\w+)\s*\(", open(HEADER).read(), flags=re.M)
-    assert len(decl) == len(set(decl)) == 25
+    assert len(decl) == len(set(decl)) == 26
     assert sorted(decl) == sorted(B.SYMBOLS)
     for name in decl:
         assert hasattr(L, name), name
@@ -336,7 +336,8 @@ def test_options_validation():
     for opt, bad in ((B.BND_OPT_FUSED_UNAVAILABLE, 2), (B.BND_OPT_THREADS_PER_ROW, 100),
                      (B.BND_OPT_THREADS_PER_ROW, 2048), (B.BND_OPT_VECTORS_PER_THREAD, 3),
                      (B.BND_OPT_VECTORS_PER_THREAD, 5), (B.BND_OPT_VECTORS_PER_THREAD, 18),
-                     (B.BND_OPT_ONE_WAVEFRONT, 3), (B.BND_OPT_ONE_WAVEFRONT, -1)):
+                     (B.BND_OPT_ONE_WAVEFRONT, 3), (B.BND_OPT_ONE_WAVEFRONT, -1),
+                     (B.BND_OPT_RING_DEPTH, 4), (B.BND_OPT_RING_DEPTH, 1), (B.BND_OPT_RING_DEPTH, 16)):
         assert L.bnd_set_option(opt, bad) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(99, 0) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(B.BND_OPT_THREADS_PER_ROW, 256) == 0
@@ -517,3 +518,28 @@ def test_missing_library_raises():
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert out.returncode == 0, out.stderr
     assert out.stdout.startswith("raised:") and "is not built" in out.stdout
+
+
+
+def test_ring_depth_option():
+    """The ring depth takes 0 (automatic), 2 or 8; a forced 8 needs a launch with one wavefront
+    per row of 8 vectors per lane and is refused, before anything is launched, for any other."""
+    for v in (2, 8, 0):
+        assert L.bnd_set_option(B.BND_OPT_RING_DEPTH, v) == 0 and L.bnd_get_option(B.BND_OPT_RING_DEPTH) == v
+    depth = ctypes.c_int(-1)
+    assert L.bnd_last_launch_ring_depth(ctypes.byref(depth)) == 0 and depth.value in (0, 2, 8)
+    assert L.bnd_last_launch_ring_depth(None) == 0
+    assert L.bnd_set_option(B.BND_OPT_RING_DEPTH, 8) == 0
+    o = owed_out()
+    arr = (VP * 2)(*[fake((p + 1) << 24) for p in range(2)])
+    for hh, ld in ((2048, 2048), (H, H)):  # a 4-wide one-wavefront row, then a multi-wave launch
+        h = create(T=8, rows=4, ld=ld, Hh=hh)
+        assert L.bnd_written(h, fake(), ld) == 0
+        assert L.bnd_publish_partials(h, arr, 2, ld, ctypes.byref(o)) == 0
+        if hh == 2048:
+            assert L.bnd_set_option(B.BND_OPT_ONE_WAVEFRONT, B.BND_ONE_WAVEFRONT_ALWAYS) == 0
+        else:
+            assert L.bnd_set_option(B.BND_OPT_ONE_WAVEFRONT, B.BND_ONE_WAVEFRONT_NEVER) == 0
+        st = L.bnd_fold_norm(h, o.value, fake(1 << 31), 1e-6, fake(1 << 30), ld, None)
+        assert st == B.BND_ERR_NO_PATH and b"deep ring" in L.bnd_last_error()
+        assert L.bnd_stream_state(h) == B.BND_PENDING

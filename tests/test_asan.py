@@ -35,8 +35,8 @@ HOST_DRIVER = r"""
 namespace bnd {
 hipError_t launch_read(Source, int, bool, const RowArgs&, const Launch&, hipStream_t) { return hipSuccess; }
 hipError_t launch_complete(Source, int, bool, const RowArgs&, const Launch&, hipStream_t) { return hipSuccess; }
-int wave_read_rows_per_cu(Source, bool, int vpt) { return vpt == 8 ? 12 : 8; }
-int wave_complete_rows_per_cu(Source, Tail, int vpt) { return vpt == 8 ? 16 : 8; }
+int wave_read_rows_per_cu(Source, bool, int vpt, bool deep) { return deep ? 8 : vpt == 8 ? 12 : 8; }
+int wave_complete_rows_per_cu(Source, Tail, int vpt, bool deep) { return deep ? 8 : vpt == 8 ? 16 : 8; }
 }  // namespace bnd
 
 static int fails = 0;
@@ -47,7 +47,7 @@ static void* fake(uint64_t k) { return (void*)(uintptr_t)(0x7F0000000000ull + (k
 // the one-wavefront width, 0 for a multi-wave shape, -1 on an error. With the stubs above a
 // round is 12 rows per CU at 8 vectors per lane and 8 elsewhere for the reads, 16 and 8 for
 // the completes, on the 256 CUs assumed without a device.
-static int auto_width(int64_t H, int64_t rows, bool complete) {
+static int auto_width(int64_t H, int64_t rows, bool complete, int* depth = nullptr) {
   bnd_stream* s = nullptr;
   bnd_owed o = BND_OWED_NONE, o2 = BND_OWED_NONE;
   const void* parts[2] = {fake(4), fake(5)};
@@ -58,6 +58,7 @@ static int auto_width(int64_t H, int64_t rows, bool complete) {
   bnd_stream_destroy(s);
   int64_t r = 0; int th = 0, v = 0, one = 0;
   if (rc != BND_OK || bnd_last_launch_shape(&r, &th, &v, &one) != BND_OK || r != rows) return -1;
+  if (depth && bnd_last_launch_ring_depth(depth) != BND_OK) return -1;
   return one ? v : 0;
 }
 
@@ -117,7 +118,13 @@ int main() {
   int64_t r = 0; int th = 0, v = 0, one = 0;
   EXPECT(bnd_last_launch_shape(&r, &th, &v, &one) == BND_OK && r == 2048);
   // one wavefront per row from 6 rows per CU, over one round or a last round full enough
-  EXPECT(auto_width(4096, 1535, false) == 0);
+  int depth = -1;
+  EXPECT(auto_width(4096, 1023, false) == 0);     // under 4 rows per CU
+  EXPECT(auto_width(4096, 1024, false, &depth) == 8 && depth == 8);  // 4 .. 7 per CU: the deep ring
+  EXPECT(auto_width(4096, 2047, true, &depth) == 8 && depth == 8);
+  EXPECT(auto_width(4096, 1535, false) == 8);
+  EXPECT(auto_width(4096, 2048, false, &depth) == 8 && depth == 2);  // from 8 rows per CU: two in flight
+  EXPECT(auto_width(2048, 1024, false, &depth) == 0 && depth == 0);  // other widths: 6 rows per CU
   EXPECT(auto_width(4096, 1536, false) == 8);
   EXPECT(auto_width(4096, 3072, false) == 8);     // one round of 3072
   EXPECT(auto_width(4096, 4096, false) == 0);     // last round 1/3 full

@@ -33,7 +33,7 @@ def orc():
 def _reset_options():
     yield
     for opt in (bnd.BND_OPT_FUSED_UNAVAILABLE, bnd.BND_OPT_THREADS_PER_ROW,
-                bnd.BND_OPT_VECTORS_PER_THREAD, bnd.BND_OPT_ONE_WAVEFRONT):
+                bnd.BND_OPT_VECTORS_PER_THREAD, bnd.BND_OPT_ONE_WAVEFRONT, bnd.BND_OPT_RING_DEPTH):
         bnd.set_option(opt, 0)
 
 
@@ -50,24 +50,26 @@ class forced_shape:
     squares is reduced in an order fixed by the shape, so comparisons of y between calls with
     different row counts are bit-exact only under one shape."""
 
-    def __init__(self, threads, vpt, one_wave=bnd.BND_ONE_WAVEFRONT_AUTO):
-        self.threads, self.vpt, self.one_wave = threads, vpt, one_wave
+    def __init__(self, threads, vpt, one_wave=bnd.BND_ONE_WAVEFRONT_AUTO, depth=0):
+        self.threads, self.vpt, self.one_wave, self.depth = threads, vpt, one_wave, depth
 
     def __enter__(self):
         bnd.set_option(bnd.BND_OPT_THREADS_PER_ROW, self.threads)
         bnd.set_option(bnd.BND_OPT_VECTORS_PER_THREAD, self.vpt)
         bnd.set_option(bnd.BND_OPT_ONE_WAVEFRONT, self.one_wave)
+        bnd.set_option(bnd.BND_OPT_RING_DEPTH, self.depth)
 
     def __exit__(self, *exc):
         bnd.set_option(bnd.BND_OPT_THREADS_PER_ROW, 0)
         bnd.set_option(bnd.BND_OPT_VECTORS_PER_THREAD, 0)
         bnd.set_option(bnd.BND_OPT_ONE_WAVEFRONT, bnd.BND_ONE_WAVEFRONT_AUTO)
+        bnd.set_option(bnd.BND_OPT_RING_DEPTH, 0)
 
 
-def forced_wave(vpt):
-    """The one-wavefront kernel of `vpt` vectors per lane (2 .. 14, even): under the ALWAYS mode a
-    forced count names the one-wavefront width."""
-    return forced_shape(64, vpt, bnd.BND_ONE_WAVEFRONT_ALWAYS)
+def forced_wave(vpt, depth=2):
+    """The one-wavefront kernel of `vpt` vectors per lane (2 .. 16, even): under the ALWAYS mode a
+    forced count names the one-wavefront width; depth 8 takes the 8-wide kernel's deep ring."""
+    return forced_shape(64, vpt, bnd.BND_ONE_WAVEFRONT_ALWAYS, depth)
 
 
 class Guarded:
@@ -804,6 +806,62 @@ def test_wave_rows(orc, vpt, T, H, P, pad, rb, rows, fp8):
     assert bnd.last_launch_shape()[1:] == (64, vpt, True)
 
 
+DEEP_SHAPES = [  # T, H, P, pad, row_begin, rows: the 8-wide kernel with the deep ring
+    (300, 4096, 8, 0, 0, None),
+    (77, 3600, 3, 8, 0, None),
+    (9, 3080, 16, 0, 2, 5),      # 385 vectors: the narrowest rows of the 8-wide kernel
+    (3, 8, 1, 0, 0, None),
+]
+
+
+@pytest.mark.parametrize("T,H,P,pad,rb,rows", DEEP_SHAPES)
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_deep_ring_rows(orc, T, H, P, pad, rb, rows, fp8):
+    """The deep ring (every vector of a source in flight) against the oracle, and bitwise against
+    the ring of two: one wavefront sums every element in the same order whatever the depth."""
+    d = workloads.fold_inputs(460 + T + P, T, H, P)
+    with forced_wave(8, depth=8):
+        a, _ = assert_fold_matches(orc, d, f"deep ring T={T} H={H} P={P} slice={rb}+{rows}", fp8=fp8, pad=pad,
+                                   row_begin=rb, rows=rows)
+        assert bnd.last_launch_shape()[1:] == (64, 8, True) and bnd.last_launch_ring_depth() == 8
+    with forced_wave(8):
+        b = run_fold(d, fp8=fp8, pad=pad, row_begin=rb, rows=rows)
+        assert bnd.last_launch_ring_depth() == 2
+    assert torch.equal(a["res"].buf, b["res"].buf)
+    if fp8:
+        assert torch.equal(a["q"].buf, b["q"].buf) and torch.equal(a["scale_buf"], b["scale_buf"])
+    else:
+        assert torch.equal(a["y"].buf, b["y"].buf)
+
+
+def test_deep_ring_moe_and_completes(orc):
+    """The deep ring for the MoE finalize (out-of-range picks included) and the completes, against
+    the oracle and bitwise against the ring of two."""
+    d = workloads.moe_inputs(470, 40, 4096, 16, 8)
+    idx = d["idx"].clone()
+    idx[9] = -1
+    idx[30] = d["expert_rows"].shape[0]
+    d["idx"] = idx
+    with forced_wave(8, depth=8):
+        ra, ya = run_moe(orc, d, 3, 30, "deep ring MoE k=8")
+        assert bnd.last_launch_ring_depth() == 8
+    with forced_wave(8):
+        rb_, yb = run_moe(orc, d, 3, 30, "ring of two MoE k=8")
+    assert torch.equal(ra.buf, rb_.buf) and torch.equal(ya.buf, yb.buf)
+    dp = workloads.fold_inputs(471, 37, 4096, 8)
+    extra = workloads.to_bf16(workloads.normal_f32(471, 12345, (37, 4096), 0.0, 0.25))
+    for kind in ("complete_only", "add_to_output", "snapshot"):
+        ex = extra if kind == "add_to_output" else None
+        with forced_wave(8, depth=8):
+            a = _complete(dp, kind, row_begin=2, rows=33, extra=ex)
+            assert bnd.last_launch_ring_depth() == 8
+        with forced_wave(8):
+            b = _complete(dp, kind, row_begin=2, rows=33, extra=ex)
+        e, mag = _oracle_complete(orc, dp, kind, row_begin=2, rows=33, extra=ex)
+        tolerance.check_bf16(bits(a.view), e, mag, f"deep ring {kind}")
+        assert torch.equal(a.buf, b.buf), kind
+
+
 WAVE_WIDTHS = [(8, 4096), (14, 7168), (4, 2048), (6, 3072), (10, 5120), (12, 6144), (2, 1024)]
 WAVE_COMPLETE_WIDTHS = WAVE_WIDTHS + [(16, 8192)]  # the completes go one width further
 
@@ -1158,7 +1216,13 @@ def test_automatic_launch_shapes():
     assert fold(2048, 8192, 8)[3] is False                              # rows too long for a read
     assert fold(2048, 8192, 8, kind="complete_only") == (2048, 64, 16, True)
     assert fold(2048, 8192, 8, kind="snapshot") == (2048, 64, 16, True)
-    assert fold(1024, 4096, 8)[3] is False                              # too few rows per CU
+    assert fold(1024, 4096, 8) == (1024, 64, 8, True)                   # 4 rows per CU: the deep ring
+    assert bnd.last_launch_ring_depth() == 8
+    assert fold(1536, 4096, 8, kind="complete_only") == (1536, 64, 8, True)
+    assert bnd.last_launch_ring_depth() == 8
+    assert fold(2048, 4096, 8) == (2048, 64, 8, True) and bnd.last_launch_ring_depth() == 2
+    assert fold(1023, 4096, 8)[3] is False                              # too few rows per CU
+    assert fold(1024, 2048, 8)[3] is False                              # the deep ring is 8-wide only
     assert fold(128, 4096, 4)[3] is False                               # a decode boundary
     d = workloads.moe_inputs(5, 2048, 4096, 16, 8)
     E, idx, gate = _moe_device(d)

@@ -28,8 +28,8 @@ hipError_t launch_read(Source, int, bool, const RowArgs&, const Launch&, hipStre
 hipError_t launch_complete(Source, int, bool, const RowArgs&, const Launch&, hipStream_t) {
   return hipSuccess;
 }
-int wave_read_rows_per_cu(Source, bool, int vpt) { return vpt == 8 ? 12 : 8; }
-int wave_complete_rows_per_cu(Source, Tail, int vpt) { return vpt == 8 ? 16 : 8; }
+int wave_read_rows_per_cu(Source, bool, int vpt, bool deep) { return deep ? 8 : vpt == 8 ? 12 : 8; }
+int wave_complete_rows_per_cu(Source, Tail, int vpt, bool deep) { return deep ? 8 : vpt == 8 ? 16 : 8; }
 }  // namespace bnd
 """
 
@@ -42,7 +42,7 @@ import test_abi_host as T
 L = B._lib
 
 def reset():
-    for opt in (1, 2, 3, 4):
+    for opt in (1, 2, 3, 4, 5):
         L.bnd_set_option(opt, 0)
 
 n = 0

@@ -26,8 +26,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, 
          "-Rpass-analysis=kernel-resource-usage"]
 
 NAME = re.compile(r"Function Name: _ZN3bnd11read_kernelILNS_6SourceE(\d)ELi(\d+)ELi(\d)ELb([01])E")
-WAVE_NAME = re.compile(r"Function Name: _ZN3bnd16wave_read_kernelILNS_6SourceE(\d)ELi(\d+)ELb([01])E")
-WAVE_COMPLETE_NAME = re.compile(r"Function Name: _ZN3bnd20wave_complete_kernelILNS_6SourceE(\d)ELi(\d+)ELNS_4TailE(\d)E")
+WAVE_NAME = re.compile(r"Function Name: _ZN3bnd16wave_read_kernelILNS_6SourceE(\d)ELi(\d+)ELb([01])ELi(\d+)E")
+WAVE_COMPLETE_NAME = re.compile(
+    r"Function Name: _ZN3bnd20wave_complete_kernelILNS_6SourceE(\d)ELi(\d+)ELNS_4TailE(\d)ELi(\d+)E")
 ANY_NAME = re.compile(r"Function Name: ")
 TAILS = {0: "None", 1: "Extra", 2: "Residual"}
 FIELD = re.compile(r"remark: +(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)")
@@ -49,14 +50,14 @@ def _resources(tmp_path, files):
                 table[current] = {}
                 continue
             m = WAVE_NAME.search(line)
-            if m:  # one wavefront per row: (kind, runtime source count, vectors per lane, fp8)
-                current = ("Wave" + SOURCES[int(m.group(1))], 0, int(m.group(2)), m.group(3) == "1")
+            if m:  # one wavefront per row: (kind, ring depth, vectors per lane, fp8)
+                current = ("Wave" + SOURCES[int(m.group(1))], int(m.group(4)), int(m.group(2)), m.group(3) == "1")
                 table[current] = {}
                 continue
             m = WAVE_COMPLETE_NAME.search(line)
-            if m:  # one-wavefront complete: (kind, tail, vectors per lane, False)
-                current = ("WaveComplete" + SOURCES[int(m.group(1))], TAILS[int(m.group(3))], int(m.group(2)),
-                           False)
+            if m:  # one-wavefront complete: (kind, tail and ring depth, vectors per lane, False)
+                current = ("WaveComplete" + SOURCES[int(m.group(1))], (TAILS[int(m.group(3))], int(m.group(4))),
+                           int(m.group(2)), False)
                 table[current] = {}
                 continue
             if ANY_NAME.search(line):  # a kernel this test does not track
@@ -80,18 +81,23 @@ def test_every_instance_reported(resources):
     # 16 source counts x 3 vector counts x bf16/fp8 for partials; 3 x 2 each for input and residual
     assert sum(1 for k in resources if k[0] == "Partials") == 96
     assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
-    # one wavefront per row: partials bf16 and fp8, MoE bf16, at 4, 6, ..., 14 vectors per lane
-    waves = sorted((k[0], k[2], k[3]) for k in resources if k[0] in ("WavePartials", "WaveMoe"))
-    assert waves == sorted((kind, vpt, fp8) for vpt in range(2, 15, 2)
-                           for kind, fp8 in (("WavePartials", False), ("WavePartials", True), ("WaveMoe", False))), waves
+    # one wavefront per row: partials bf16 and fp8, MoE bf16, at 2, 4, ..., 14 vectors per lane with
+    # a ring of 2, and at 8 vectors per lane also with the deep ring of 8
+    waves = sorted((k[0], k[1], k[2], k[3]) for k in resources if k[0] in ("WavePartials", "WaveMoe"))
+    kinds = (("WavePartials", False), ("WavePartials", True), ("WaveMoe", False))
+    want = [(kind, 2, vpt, fp8) for vpt in range(2, 15, 2) for kind, fp8 in kinds]
+    want += [(kind, 8, 8, fp8) for kind, fp8 in kinds]
+    assert waves == sorted(want), waves
 
 
 def test_one_wave_completes_reported(resources):
     # partials with no tail, the extra row or the residual; MoE picks with no tail or the extra row
     got = sorted((k[0], k[1], k[2]) for k in resources if k[0].startswith("WaveComplete"))
-    assert got == sorted((kind, tail, vpt) for vpt in range(2, 17, 2) for kind, tail in (
-        ("WaveCompletePartials", "None"), ("WaveCompletePartials", "Extra"), ("WaveCompletePartials", "Residual"),
-        ("WaveCompleteMoe", "None"), ("WaveCompleteMoe", "Extra"))), got
+    kinds = (("WaveCompletePartials", "None"), ("WaveCompletePartials", "Extra"), ("WaveCompletePartials", "Residual"),
+             ("WaveCompleteMoe", "None"), ("WaveCompleteMoe", "Extra"))
+    want = [(kind, (tail, 2), vpt) for vpt in range(2, 17, 2) for kind, tail in kinds]
+    want += [(kind, (tail, 8), 8) for kind, tail in kinds]  # the deep ring
+    assert got == sorted(want), got
 
 
 def test_one_wave_rows_keep_two_waves_per_simd(resources):
