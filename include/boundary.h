@@ -297,8 +297,8 @@ typedef enum bnd_option {
    * takes one wavefront per row where it is measured faster: a call that
    * takes owed work with rows of 1544 <= H <= 7168 (8192 for complete_only,
    * add_to_output and snapshot) and at least 6 rows per CU (4 for rows of
-   * 3080 <= H <= 4096, which take the deep ring below 8 rows per CU; see
-   * BND_OPT_RING_DEPTH), or a call on owed partials with rows of 776 <= H <= 1024 and at
+   * 3080 <= H <= 4096; rows of H <= 4096 take the deep ring below 8 rows
+   * per CU, see BND_OPT_RING_DEPTH), or a call on owed partials with rows of 776 <= H <= 1024 and at
    * least 12 rows per CU, and either no more rows than the kernel holds on
    * the chip at once or a last round of resident rows at least 3/4 full for
    * the folds and MoE finalize, 1/3 full for complete_only, add_to_output and
@@ -309,9 +309,11 @@ typedef enum bnd_option {
    * completes) fails with NO_PATH; NEVER never takes it. */
   BND_OPT_ONE_WAVEFRONT = 4,
   /* Loads each one-wavefront row keeps in flight: 0 = automatic (the deep
-   * ring of 8 for the 8-vector kernels, H = 3080 .. 4096, when a launch has 4
-   * to 7 rows per CU; 2 otherwise), 2, or 8 (only for a launch with one
-   * wavefront per row of 8 vectors per lane; NO_PATH for any other). */
+   * ring, every vector of a source in flight, for the 4-, 6- and 8-vector
+   * kernels when a launch has 6 to 7 rows per CU, H = 1544 .. 3072, or 4 to
+   * 7, H = 3080 .. 4096; 2 otherwise), 2, or the deep ring of 4, 6 or 8
+   * (only for a launch with one wavefront per row of that many vectors per
+   * lane; NO_PATH for any other). */
   BND_OPT_RING_DEPTH = 5
 } bnd_option;
 
@@ -331,7 +333,7 @@ BND_API int64_t bnd_get_option(bnd_option opt);
 BND_API bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_thread,
                                          int* one_wavefront);
 /* The load ring depth of the calling thread's last launch through this
- * library: 2 or 8 for one wavefront per row, 0 for several wavefronts (and
+ * library: 2, 4, 6 or 8 for one wavefront per row, 0 for several wavefronts (and
  * before the thread's first launch). `depth` may be NULL. Always BND_OK. */
 BND_API bnd_status bnd_last_launch_ring_depth(int* depth);
 

@@ -215,7 +215,7 @@ struct WaveFit {
   int last_den = 1;
   bool narrow = false;  // whether the automatic shape may take the narrowest width, 2
   int max_vpt = 0;      // the widest one-wavefront kernel of the call
-  int deep_rows_per_cu = 0;  // the same as rows_per_cu for the 8-wide kernel with the deep ring
+  int deep_rows_per_cu[bnd::kWaveDeepWidths] = {};  // the same for the kernels with the deep ring (widths 4 .. 8)
 };
 
 WaveFit wave_fit_read(bnd::Source src, bool fp8) {
@@ -227,7 +227,8 @@ WaveFit wave_fit_read(bnd::Source src, bool fp8) {
   f.max_vpt = bnd::kWaveReadVptMax;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_read_rows_per_cu(src, fp8, v);
-  f.deep_rows_per_cu = bnd::wave_read_rows_per_cu(src, fp8, bnd::kWaveDeepVpt, true);
+  for (int v = bnd::kWaveDeepMin; v <= bnd::kWaveDeepMax; v += 2)
+    f.deep_rows_per_cu[bnd::deep_slot(v)] = bnd::wave_read_rows_per_cu(src, fp8, v, true);
   return f;
 }
 
@@ -240,7 +241,8 @@ WaveFit wave_fit_complete(bnd::Source src, bnd::Tail tail) {
   f.max_vpt = bnd::kWaveVptMax;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_complete_rows_per_cu(src, tail, v);
-  f.deep_rows_per_cu = bnd::wave_complete_rows_per_cu(src, tail, bnd::kWaveDeepVpt, true);
+  for (int v = bnd::kWaveDeepMin; v <= bnd::kWaveDeepMax; v += 2)
+    f.deep_rows_per_cu[bnd::deep_slot(v)] = bnd::wave_complete_rows_per_cu(src, tail, v, true);
   return f;
 }
 
@@ -262,13 +264,15 @@ void warm_launch_queries() {
         bnd::wave_complete_rows_per_cu(Source::Moe, t, w);
       }
     }
-    for (bool fp8 : {false, true}) {
-      bnd::wave_read_rows_per_cu(Source::Partials, fp8, bnd::kWaveDeepVpt, true);
-      bnd::wave_read_rows_per_cu(Source::Moe, fp8, bnd::kWaveDeepVpt, true);
-    }
-    for (bnd::Tail t : {bnd::Tail::None, bnd::Tail::Extra, bnd::Tail::Residual}) {
-      bnd::wave_complete_rows_per_cu(Source::Partials, t, bnd::kWaveDeepVpt, true);
-      bnd::wave_complete_rows_per_cu(Source::Moe, t, bnd::kWaveDeepVpt, true);
+    for (int w = bnd::kWaveDeepMin; w <= bnd::kWaveDeepMax; w += 2) {
+      for (bool fp8 : {false, true}) {
+        bnd::wave_read_rows_per_cu(Source::Partials, fp8, w, true);
+        bnd::wave_read_rows_per_cu(Source::Moe, fp8, w, true);
+      }
+      for (bnd::Tail t : {bnd::Tail::None, bnd::Tail::Extra, bnd::Tail::Residual}) {
+        bnd::wave_complete_rows_per_cu(Source::Partials, t, w, true);
+        bnd::wave_complete_rows_per_cu(Source::Moe, t, w, true);
+      }
     }
   });
 }
@@ -308,9 +312,11 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
     // rows per CU (6 for the others).
     const bool two = width == 2;
     const bool fills = two ? wave.narrow && 4 * nvec > 3 * 2 * bnd::kWave : nvec > 3 * bnd::kWave;
-    // The 8-wide kernels with the deep ring take launches of 4 to 7 rows per CU (one round).
-    const bool deep_fits = width == bnd::kWaveDeepVpt && depth != 2 && rows >= 4 * cus && rows < 8 * cus &&
-                           rows <= (int64_t)wave.deep_rows_per_cu * cus;
+    // The kernels with the deep ring take launches of 6 to 7 rows per CU at widths 4 and 6, and
+    // of 4 to 7 at width 8 (one round).
+    const int d = bnd::deep_slot(width);
+    const bool deep_fits = d >= 0 && depth != 2 && rows >= (width == 8 ? 4 : 6) * cus && rows < 8 * cus &&
+                           rows <= (int64_t)wave.deep_rows_per_cu[d] * cus;
     const bool auto_wave = one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && width <= wave.max_vpt &&
                            fills;
     if (auto_wave && deep_fits) {
@@ -346,12 +352,12 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
       return fail(BND_ERR_NO_PATH, "%d vectors per lane (one wavefront per row) needs 64 threads, not %d", vpt,
                   threads);
     threads = bnd::kWave;
-    if (depth == bnd::kWaveDeepDepth) {
-      if (vpt != bnd::kWaveDeepVpt)
-        return fail(BND_ERR_NO_PATH, "the deep ring is built for %d vectors per lane, not %d", bnd::kWaveDeepVpt, vpt);
+    if (depth > 2) {
+      if (vpt != depth)
+        return fail(BND_ERR_NO_PATH, "the deep ring of %d is built for %d vectors per lane, not %d", depth, depth, vpt);
       deep = true;
     }
-  } else if (depth == bnd::kWaveDeepDepth) {
+  } else if (depth > 2) {
     return fail(BND_ERR_NO_PATH, "the deep ring is for one wavefront per row; this launch has %d threads per row",
                 threads != 0 ? threads : round_threads((nvec + vpt - 1) / vpt));
   }
@@ -501,7 +507,7 @@ bnd_status bnd_last_launch_shape(int64_t* rows, int* threads, int* vectors_per_t
 }
 
 bnd_status bnd_last_launch_ring_depth(int* depth) {
-  if (depth) *depth = g_last_launch.one_wave ? (g_last_launch.deep ? bnd::kWaveDeepDepth : 2) : 0;
+  if (depth) *depth = g_last_launch.one_wave ? (g_last_launch.deep ? g_last_launch.vpt : 2) : 0;
   return ok();
 }
 
@@ -533,8 +539,9 @@ bnd_status bnd_set_option(bnd_option opt, int64_t value) {
       g_one_wave_mode.store((int)value);
       return ok();
     case BND_OPT_RING_DEPTH:
-      if (value != 0 && value != 2 && value != bnd::kWaveDeepDepth)
-        return fail(BND_ERR_INVALID_ARG, "ring depth: 0 (automatic), 2 or %d", bnd::kWaveDeepDepth);
+      if (value != 0 && value != 2 && (value > bnd::kWaveDeepMax || bnd::deep_slot((int)value) < 0))
+        return fail(BND_ERR_INVALID_ARG, "ring depth: 0 (automatic), 2, or %d .. %d (even) for that many vectors "
+                    "per lane", bnd::kWaveDeepMin, bnd::kWaveDeepMax);
       g_depth_override.store((int)value);
       return ok();
   }

@@ -18,10 +18,15 @@ constexpr std::array<KernelFn, 3> kWaveKernels[kWaveWidths] = {
 static_assert(kWaveWidths == 8 && wave_slot(2) == 0 && wave_slot(kWaveReadVptMax) == 6,
               "one table row per width, the last one empty");
 
-// the 8-wide kernels with the deep ring, by the same columns
-constexpr std::array<KernelFn, 3> kWaveDeep = {{&wave_read_kernel<Source::Partials, kWaveDeepVpt, false, kWaveDeepDepth>,
-                                                &wave_read_kernel<Source::Partials, kWaveDeepVpt, true, kWaveDeepDepth>,
-                                                &wave_read_kernel<Source::Moe, kWaveDeepVpt, false, kWaveDeepDepth>}};
+// the 4-, 6- and 8-wide kernels with the deep ring (depth = width), by the same columns
+template <int VPT>
+constexpr std::array<KernelFn, 3> wave_read_deep_row() {
+  return {{&wave_read_kernel<Source::Partials, VPT, false, VPT>, &wave_read_kernel<Source::Partials, VPT, true, VPT>,
+           &wave_read_kernel<Source::Moe, VPT, false, VPT>}};
+}
+constexpr std::array<KernelFn, 3> kWaveDeep[kWaveDeepWidths] = {wave_read_deep_row<4>(), wave_read_deep_row<6>(),
+                                                                 wave_read_deep_row<8>()};
+static_assert(kWaveDeepWidths == 3 && deep_slot(8) == 2, "one deep table row per width");
 
 // the table column of a call, or -1 when it has no one-wavefront kernel
 int wave_kind(Source src, bool fp8) {
@@ -31,24 +36,25 @@ int wave_kind(Source src, bool fp8) {
 }
 
 std::atomic<int> g_rows_per_cu[kWaveWidths][3];  // 0: not read yet, -1: unknown
-std::atomic<int> g_deep_rows_per_cu[3];
+std::atomic<int> g_deep_rows_per_cu[kWaveDeepWidths][3];
 }  // namespace
 
 int wave_read_rows_per_cu(Source src, bool fp8, int vpt, bool deep) {
   const int kind = wave_kind(src, fp8), w = wave_slot(vpt);
-  if (kind < 0 || w < 0 || vpt > kWaveReadVptMax || (deep && vpt != kWaveDeepVpt)) return 0;
-  if (deep) return occupancy_rows(kWaveDeep[kind], g_deep_rows_per_cu[kind]);
+  const int d = deep_slot(vpt);
+  if (kind < 0 || w < 0 || vpt > kWaveReadVptMax || (deep && d < 0)) return 0;
+  if (deep) return occupancy_rows(kWaveDeep[d][kind], g_deep_rows_per_cu[d][kind]);
   return occupancy_rows(kWaveKernels[w][kind], g_rows_per_cu[w][kind]);
 }
 
 hipError_t launch_read_wave(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
   const int kind = wave_kind(src, fp8), w = wave_slot(l.vpt);
   if (!l.one_wave || w < 0 || l.vpt > kWaveReadVptMax || kind < 0 || l.threads != kWave || a.nvec > kWave * l.vpt ||
-      n < 1 || n > kMaxSources || (l.deep && l.vpt != kWaveDeepVpt))
+      n < 1 || n > kMaxSources || (l.deep && deep_slot(l.vpt) < 0))
     return hipErrorInvalidValue;
   RowArgs b = a;
   b.nsrc = n;
-  return launch_kernel(l.deep ? kWaveDeep[kind] : kWaveKernels[w][kind], b, l, stream);
+  return launch_kernel(l.deep ? kWaveDeep[deep_slot(l.vpt)][kind] : kWaveKernels[w][kind], b, l, stream);
 }
 
 }  // namespace bnd

@@ -19,13 +19,16 @@ constexpr std::array<KernelFn, 5> kWaveComplete[kWaveWidths] = {
     wave_complete_row<10>(), wave_complete_row<12>(), wave_complete_row<14>(), wave_complete_row<16>()};
 static_assert(kWaveWidths == 8 && wave_slot(kWaveVptMax) == 7, "one table row per width");
 
-// the 8-wide kernels with the deep ring, by the same columns
-constexpr std::array<KernelFn, 5> kWaveCompleteDeep = {
-    {&wave_complete_kernel<Source::Partials, kWaveDeepVpt, Tail::None, kWaveDeepDepth>,
-     &wave_complete_kernel<Source::Partials, kWaveDeepVpt, Tail::Extra, kWaveDeepDepth>,
-     &wave_complete_kernel<Source::Partials, kWaveDeepVpt, Tail::Residual, kWaveDeepDepth>,
-     &wave_complete_kernel<Source::Moe, kWaveDeepVpt, Tail::None, kWaveDeepDepth>,
-     &wave_complete_kernel<Source::Moe, kWaveDeepVpt, Tail::Extra, kWaveDeepDepth>}};
+// the 4-, 6- and 8-wide kernels with the deep ring (depth = width), by the same columns
+template <int VPT>
+constexpr std::array<KernelFn, 5> wave_complete_deep_row() {
+  return {{&wave_complete_kernel<Source::Partials, VPT, Tail::None, VPT>,
+           &wave_complete_kernel<Source::Partials, VPT, Tail::Extra, VPT>,
+           &wave_complete_kernel<Source::Partials, VPT, Tail::Residual, VPT>,
+           &wave_complete_kernel<Source::Moe, VPT, Tail::None, VPT>, &wave_complete_kernel<Source::Moe, VPT, Tail::Extra, VPT>}};
+}
+constexpr std::array<KernelFn, 5> kWaveCompleteDeep[kWaveDeepWidths] = {
+    wave_complete_deep_row<4>(), wave_complete_deep_row<6>(), wave_complete_deep_row<8>()};
 
 // the table column of a call, or -1 when it has no one-wavefront kernel
 int wave_kind(Source src, Tail tail) {
@@ -35,13 +38,14 @@ int wave_kind(Source src, Tail tail) {
 }
 
 std::atomic<int> g_rows_per_cu[kWaveWidths][5];  // 0: not read yet, -1: unknown
-std::atomic<int> g_deep_rows_per_cu[5];
+std::atomic<int> g_deep_rows_per_cu[kWaveDeepWidths][5];
 }  // namespace
 
 int wave_complete_rows_per_cu(Source src, Tail tail, int vpt, bool deep) {
   const int kind = wave_kind(src, tail), w = wave_slot(vpt);
-  if (kind < 0 || w < 0 || (deep && vpt != kWaveDeepVpt)) return 0;
-  if (deep) return occupancy_rows(kWaveCompleteDeep[kind], g_deep_rows_per_cu[kind]);
+  const int d = deep_slot(vpt);
+  if (kind < 0 || w < 0 || (deep && d < 0)) return 0;
+  if (deep) return occupancy_rows(kWaveCompleteDeep[d][kind], g_deep_rows_per_cu[d][kind]);
   return occupancy_rows(kWaveComplete[w][kind], g_rows_per_cu[w][kind]);
 }
 
@@ -49,11 +53,11 @@ hipError_t launch_complete_wave(Source src, int n, Tail tail, const RowArgs& a, 
                                 hipStream_t stream) {
   const int kind = wave_kind(src, tail), w = wave_slot(l.vpt);
   if (!l.one_wave || w < 0 || kind < 0 || l.threads != kWave || a.nvec > kWave * l.vpt || n < 1 ||
-      n > kMaxSources || (l.deep && l.vpt != kWaveDeepVpt))
+      n > kMaxSources || (l.deep && deep_slot(l.vpt) < 0))
     return hipErrorInvalidValue;
   RowArgs b = a;
   b.nsrc = n;
-  return launch_kernel(l.deep ? kWaveCompleteDeep[kind] : kWaveComplete[w][kind], b, l, stream);
+  return launch_kernel(l.deep ? kWaveCompleteDeep[deep_slot(l.vpt)][kind] : kWaveComplete[w][kind], b, l, stream);
 }
 
 }  // namespace bnd

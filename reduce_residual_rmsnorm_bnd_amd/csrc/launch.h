@@ -16,11 +16,16 @@ constexpr int kWave = 64;
 // every width up to kWaveVptMax; the reads leave the widest one empty.
 constexpr int kWaveVptMin = 2;
 constexpr int kWaveReadVptMax = 14;
-// The 8-wide kernels also come with a deep ring, every vector of a source in
-// flight (depth 8 instead of 2), for launches of too few rows per CU to keep
-// the memory busy with two loads in flight per wave.
-constexpr int kWaveDeepVpt = 8;
-constexpr int kWaveDeepDepth = 8;
+// The 4-, 6- and 8-wide kernels also come with a deep ring, every vector of a
+// source in flight (a depth equal to the width instead of 2), for launches of
+// too few rows per CU to keep the memory busy with two loads in flight per
+// wave.
+constexpr int kWaveDeepMin = 4;
+constexpr int kWaveDeepMax = 8;
+constexpr int kWaveDeepWidths = (kWaveDeepMax - kWaveDeepMin) / 2 + 1;
+constexpr int deep_slot(int vpt) {
+  return vpt >= kWaveDeepMin && vpt <= kWaveDeepMax && vpt % 2 == 0 ? (vpt - kWaveDeepMin) / 2 : -1;
+}
 constexpr int kWaveVptMax = 16;
 constexpr int kWaveWidths = (kWaveVptMax - kWaveVptMin) / 2 + 1;
 // the table slot of a one-wavefront width, or -1 for a width without kernels
@@ -71,7 +76,7 @@ struct Launch {
   int threads = 0;  // workgroup size, multiple of 64
   int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; for one wavefront per row 2 .. 14, even
   bool one_wave = false;  // one wavefront per row (wave_read_kernel, wave_complete_kernel; threads = 64)
-  bool deep = false;      // one wavefront per row with the deep ring (vpt = kWaveDeepVpt)
+  bool deep = false;      // one wavefront per row with the deep ring (depth = vpt, 4 .. 8)
   hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
   hipEvent_t stop = nullptr;
 };
@@ -99,7 +104,7 @@ hipError_t launch_complete_wave(Source src, int n, Tail tail, const RowArgs& a, 
 
 // Rows of one launch that a compute unit of the current device holds at once
 // with the one-wavefront read or complete kernel of vpt (2 .. 16, even)
-// vectors per lane, with the deep ring when `deep` (vpt = kWaveDeepVpt only):
+// vectors per lane, with the deep ring when `deep` (vpt 4, 6 or 8 only):
 // its occupancy in 64-thread workgroups, from the HIP runtime, read once per
 // kernel; 0 when no such kernel exists or the runtime cannot tell.
 int wave_read_rows_per_cu(Source src, bool fp8, int vpt, bool deep = false);

@@ -337,7 +337,8 @@ def test_options_validation():
                      (B.BND_OPT_THREADS_PER_ROW, 2048), (B.BND_OPT_VECTORS_PER_THREAD, 3),
                      (B.BND_OPT_VECTORS_PER_THREAD, 5), (B.BND_OPT_VECTORS_PER_THREAD, 18),
                      (B.BND_OPT_ONE_WAVEFRONT, 3), (B.BND_OPT_ONE_WAVEFRONT, -1),
-                     (B.BND_OPT_RING_DEPTH, 4), (B.BND_OPT_RING_DEPTH, 1), (B.BND_OPT_RING_DEPTH, 16)):
+                     (B.BND_OPT_RING_DEPTH, 1), (B.BND_OPT_RING_DEPTH, 3), (B.BND_OPT_RING_DEPTH, 10),
+                     (B.BND_OPT_RING_DEPTH, 16)):
         assert L.bnd_set_option(opt, bad) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(99, 0) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(B.BND_OPT_THREADS_PER_ROW, 256) == 0
@@ -522,12 +523,13 @@ def test_missing_library_raises():
 
 
 def test_ring_depth_option():
-    """The ring depth takes 0 (automatic), 2 or 8; a forced 8 needs a launch with one wavefront
-    per row of 8 vectors per lane and is refused, before anything is launched, for any other."""
-    for v in (2, 8, 0):
+    """The ring depth takes 0 (automatic), 2, or 4, 6 or 8; a forced 8 needs a launch with one
+    wavefront per row of 8 vectors per lane and is refused, before anything is launched, for any
+    other."""
+    for v in (2, 4, 6, 8, 0):
         assert L.bnd_set_option(B.BND_OPT_RING_DEPTH, v) == 0 and L.bnd_get_option(B.BND_OPT_RING_DEPTH) == v
     depth = ctypes.c_int(-1)
-    assert L.bnd_last_launch_ring_depth(ctypes.byref(depth)) == 0 and depth.value in (0, 2, 8)
+    assert L.bnd_last_launch_ring_depth(ctypes.byref(depth)) == 0 and depth.value in (0, 2, 4, 6, 8)
     assert L.bnd_last_launch_ring_depth(None) == 0
     assert L.bnd_set_option(B.BND_OPT_RING_DEPTH, 8) == 0
     o = owed_out()

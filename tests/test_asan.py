@@ -124,7 +124,12 @@ int main() {
   EXPECT(auto_width(4096, 2047, true, &depth) == 8 && depth == 8);
   EXPECT(auto_width(4096, 1535, false) == 8);
   EXPECT(auto_width(4096, 2048, false, &depth) == 8 && depth == 2);  // from 8 rows per CU: two in flight
-  EXPECT(auto_width(2048, 1024, false, &depth) == 0 && depth == 0);  // other widths: 6 rows per CU
+  EXPECT(auto_width(2048, 1024, false, &depth) == 0 && depth == 0);  // widths 4 and 6: from 6 rows per CU
+  EXPECT(auto_width(2048, 1535, false) == 0);
+  EXPECT(auto_width(2048, 1536, false, &depth) == 4 && depth == 4);  // 6 .. 7 per CU: the deep ring
+  EXPECT(auto_width(3072, 2047, true, &depth) == 6 && depth == 6);
+  EXPECT(auto_width(3072, 2048, false, &depth) == 6 && depth == 2);
+  EXPECT(auto_width(6144, 1536, false, &depth) == 12 && depth == 2);  // none for the wider rows
   EXPECT(auto_width(4096, 1536, false) == 8);
   EXPECT(auto_width(4096, 3072, false) == 8);     // one round of 3072
   EXPECT(auto_width(4096, 4096, false) == 0);     // last round 1/3 full

@@ -68,7 +68,7 @@ class forced_shape:
 
 def forced_wave(vpt, depth=2):
     """The one-wavefront kernel of `vpt` vectors per lane (2 .. 16, even): under the ALWAYS mode a
-    forced count names the one-wavefront width; depth 8 takes the 8-wide kernel's deep ring."""
+    forced count names the one-wavefront width; a depth of 4, 6 or 8 takes that width's deep ring."""
     return forced_shape(64, vpt, bnd.BND_ONE_WAVEFRONT_ALWAYS, depth)
 
 
@@ -806,25 +806,30 @@ def test_wave_rows(orc, vpt, T, H, P, pad, rb, rows, fp8):
     assert bnd.last_launch_shape()[1:] == (64, vpt, True)
 
 
-DEEP_SHAPES = [  # T, H, P, pad, row_begin, rows: the 8-wide kernel with the deep ring
-    (300, 4096, 8, 0, 0, None),
-    (77, 3600, 3, 8, 0, None),
-    (9, 3080, 16, 0, 2, 5),      # 385 vectors: the narrowest rows of the 8-wide kernel
-    (3, 8, 1, 0, 0, None),
+DEEP_SHAPES = [  # vectors per lane, T, H, P, pad, row_begin, rows: the kernels with the deep ring
+    (8, 300, 4096, 8, 0, 0, None),
+    (8, 77, 3600, 3, 8, 0, None),
+    (8, 9, 3080, 16, 0, 2, 5),      # 385 vectors: the narrowest rows of the 8-wide kernel
+    (8, 3, 8, 1, 0, 0, None),
+    (6, 150, 3072, 4, 0, 0, None),
+    (6, 21, 2056, 16, 0, 3, 17),    # 257 vectors: the narrowest rows of the 6-wide kernel
+    (4, 200, 2048, 8, 0, 0, None),
+    (4, 31, 1544, 5, 8, 1, 29),     # 193 vectors
+    (4, 3, 8, 1, 0, 0, None),
 ]
 
 
-@pytest.mark.parametrize("T,H,P,pad,rb,rows", DEEP_SHAPES)
+@pytest.mark.parametrize("vpt,T,H,P,pad,rb,rows", DEEP_SHAPES)
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-def test_deep_ring_rows(orc, T, H, P, pad, rb, rows, fp8):
+def test_deep_ring_rows(orc, vpt, T, H, P, pad, rb, rows, fp8):
     """The deep ring (every vector of a source in flight) against the oracle, and bitwise against
     the ring of two: one wavefront sums every element in the same order whatever the depth."""
     d = workloads.fold_inputs(460 + T + P, T, H, P)
-    with forced_wave(8, depth=8):
-        a, _ = assert_fold_matches(orc, d, f"deep ring T={T} H={H} P={P} slice={rb}+{rows}", fp8=fp8, pad=pad,
-                                   row_begin=rb, rows=rows)
-        assert bnd.last_launch_shape()[1:] == (64, 8, True) and bnd.last_launch_ring_depth() == 8
-    with forced_wave(8):
+    with forced_wave(vpt, depth=vpt):
+        a, _ = assert_fold_matches(orc, d, f"deep ring x{vpt} T={T} H={H} P={P} slice={rb}+{rows}", fp8=fp8,
+                                   pad=pad, row_begin=rb, rows=rows)
+        assert bnd.last_launch_shape()[1:] == (64, vpt, True) and bnd.last_launch_ring_depth() == vpt
+    with forced_wave(vpt):
         b = run_fold(d, fp8=fp8, pad=pad, row_begin=rb, rows=rows)
         assert bnd.last_launch_ring_depth() == 2
     assert torch.equal(a["res"].buf, b["res"].buf)
@@ -834,28 +839,30 @@ def test_deep_ring_rows(orc, T, H, P, pad, rb, rows, fp8):
         assert torch.equal(a["y"].buf, b["y"].buf)
 
 
-def test_deep_ring_moe_and_completes(orc):
+@pytest.mark.parametrize("vpt", [8, 6, 4])
+def test_deep_ring_moe_and_completes(orc, vpt):
     """The deep ring for the MoE finalize (out-of-range picks included) and the completes, against
     the oracle and bitwise against the ring of two."""
-    d = workloads.moe_inputs(470, 40, 4096, 16, 8)
+    H = vpt * 512
+    d = workloads.moe_inputs(470 + vpt, 40, H, 16, 8)
     idx = d["idx"].clone()
     idx[9] = -1
     idx[30] = d["expert_rows"].shape[0]
     d["idx"] = idx
-    with forced_wave(8, depth=8):
-        ra, ya = run_moe(orc, d, 3, 30, "deep ring MoE k=8")
-        assert bnd.last_launch_ring_depth() == 8
-    with forced_wave(8):
-        rb_, yb = run_moe(orc, d, 3, 30, "ring of two MoE k=8")
+    with forced_wave(vpt, depth=vpt):
+        ra, ya = run_moe(orc, d, 3, 30, f"deep ring x{vpt} MoE k=8")
+        assert bnd.last_launch_ring_depth() == vpt
+    with forced_wave(vpt):
+        rb_, yb = run_moe(orc, d, 3, 30, f"ring of two x{vpt} MoE k=8")
     assert torch.equal(ra.buf, rb_.buf) and torch.equal(ya.buf, yb.buf)
-    dp = workloads.fold_inputs(471, 37, 4096, 8)
-    extra = workloads.to_bf16(workloads.normal_f32(471, 12345, (37, 4096), 0.0, 0.25))
+    dp = workloads.fold_inputs(471 + vpt, 37, H, 8)
+    extra = workloads.to_bf16(workloads.normal_f32(471 + vpt, 12345, (37, H), 0.0, 0.25))
     for kind in ("complete_only", "add_to_output", "snapshot"):
         ex = extra if kind == "add_to_output" else None
-        with forced_wave(8, depth=8):
+        with forced_wave(vpt, depth=vpt):
             a = _complete(dp, kind, row_begin=2, rows=33, extra=ex)
-            assert bnd.last_launch_ring_depth() == 8
-        with forced_wave(8):
+            assert bnd.last_launch_ring_depth() == vpt
+        with forced_wave(vpt):
             b = _complete(dp, kind, row_begin=2, rows=33, extra=ex)
         e, mag = _oracle_complete(orc, dp, kind, row_begin=2, rows=33, extra=ex)
         tolerance.check_bf16(bits(a.view), e, mag, f"deep ring {kind}")
@@ -1222,7 +1229,11 @@ def test_automatic_launch_shapes():
     assert bnd.last_launch_ring_depth() == 8
     assert fold(2048, 4096, 8) == (2048, 64, 8, True) and bnd.last_launch_ring_depth() == 2
     assert fold(1023, 4096, 8)[3] is False                              # too few rows per CU
-    assert fold(1024, 2048, 8)[3] is False                              # the deep ring is 8-wide only
+    assert fold(1024, 2048, 8)[3] is False                              # widths 4, 6: from 6 rows per CU
+    assert fold(1536, 2048, 8) == (1536, 64, 4, True) and bnd.last_launch_ring_depth() == 4
+    assert fold(1792, 3072, 8, kind="complete_only") == (1792, 64, 6, True)
+    assert bnd.last_launch_ring_depth() == 6
+    assert fold(2048, 3072, 8) == (2048, 64, 6, True) and bnd.last_launch_ring_depth() == 2
     assert fold(128, 4096, 4)[3] is False                               # a decode boundary
     d = workloads.moe_inputs(5, 2048, 4096, 16, 8)
     E, idx, gate = _moe_device(d)

@@ -82,11 +82,11 @@ def test_every_instance_reported(resources):
     assert sum(1 for k in resources if k[0] == "Partials") == 96
     assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
     # one wavefront per row: partials bf16 and fp8, MoE bf16, at 2, 4, ..., 14 vectors per lane with
-    # a ring of 2, and at 8 vectors per lane also with the deep ring of 8
+    # a ring of 2, and at 4, 6 and 8 vectors per lane also with the deep ring of as many
     waves = sorted((k[0], k[1], k[2], k[3]) for k in resources if k[0] in ("WavePartials", "WaveMoe"))
     kinds = (("WavePartials", False), ("WavePartials", True), ("WaveMoe", False))
     want = [(kind, 2, vpt, fp8) for vpt in range(2, 15, 2) for kind, fp8 in kinds]
-    want += [(kind, 8, 8, fp8) for kind, fp8 in kinds]
+    want += [(kind, vpt, vpt, fp8) for vpt in (4, 6, 8) for kind, fp8 in kinds]
     assert waves == sorted(want), waves
 
 
@@ -96,7 +96,7 @@ def test_one_wave_completes_reported(resources):
     kinds = (("WaveCompletePartials", "None"), ("WaveCompletePartials", "Extra"), ("WaveCompletePartials", "Residual"),
              ("WaveCompleteMoe", "None"), ("WaveCompleteMoe", "Extra"))
     want = [(kind, (tail, 2), vpt) for vpt in range(2, 17, 2) for kind, tail in kinds]
-    want += [(kind, (tail, 8), 8) for kind, tail in kinds]  # the deep ring
+    want += [(kind, (tail, vpt), vpt) for vpt in (4, 6, 8) for kind, tail in kinds]  # the deep ring
     assert got == sorted(want), got
 
 
