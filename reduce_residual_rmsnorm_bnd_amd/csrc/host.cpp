@@ -539,7 +539,7 @@ bnd_status bnd_set_option(bnd_option opt, int64_t value) {
       g_one_wave_mode.store((int)value);
       return ok();
     case BND_OPT_RING_DEPTH:
-      if (value != 0 && value != 2 && (value > bnd::kWaveDeepMax || bnd::deep_slot((int)value) < 0))
+      if (value != 0 && value != 2 && (value < bnd::kWaveDeepMin || value > bnd::kWaveDeepMax || value % 2 != 0))
         return fail(BND_ERR_INVALID_ARG, "ring depth: 0 (automatic), 2, or %d .. %d (even) for that many vectors "
                     "per lane", bnd::kWaveDeepMin, bnd::kWaveDeepMax);
       g_depth_override.store((int)value);

@@ -338,7 +338,8 @@ def test_options_validation():
                      (B.BND_OPT_VECTORS_PER_THREAD, 5), (B.BND_OPT_VECTORS_PER_THREAD, 18),
                      (B.BND_OPT_ONE_WAVEFRONT, 3), (B.BND_OPT_ONE_WAVEFRONT, -1),
                      (B.BND_OPT_RING_DEPTH, 1), (B.BND_OPT_RING_DEPTH, 3), (B.BND_OPT_RING_DEPTH, 10),
-                     (B.BND_OPT_RING_DEPTH, 16)):
+                     (B.BND_OPT_RING_DEPTH, 16), (B.BND_OPT_RING_DEPTH, 4 - 2**32),
+                     (B.BND_OPT_VECTORS_PER_THREAD, 8 - 2**32), (B.BND_OPT_THREADS_PER_ROW, 256 - 2**32)):
         assert L.bnd_set_option(opt, bad) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(99, 0) == B.BND_ERR_INVALID_ARG
     assert L.bnd_set_option(B.BND_OPT_THREADS_PER_ROW, 256) == 0
