@@ -288,7 +288,7 @@ typedef enum bnd_option {
    * the folds, complete_only, add_to_output, and snapshot of a Pending
    * stream; 16 only for complete_only, add_to_output and snapshot). Under BND_ONE_WAVEFRONT_ALWAYS every forced count names the
    * one-wavefront width (2 and 4 included; an odd count fails); under
-   * BND_ONE_WAVEFRONT_NEVER a count of 6 .. 14 fails. A shape that cannot
+   * BND_ONE_WAVEFRONT_NEVER a count of 6 .. 16 fails. A shape that cannot
    * cover H, or a one-wavefront count for any other call, fails with
    * NO_PATH. */
   BND_OPT_THREADS_PER_ROW = 2,

@@ -74,7 +74,7 @@ struct RowArgs {
 struct Launch {
   int rows = 0;     // grid size
   int threads = 0;  // workgroup size, multiple of 64
-  int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; for one wavefront per row 2 .. 14, even
+  int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; for one wavefront per row 2 .. 16, even
   bool one_wave = false;  // one wavefront per row (wave_read_kernel, wave_complete_kernel; threads = 64)
   bool deep = false;      // one wavefront per row with the deep ring (depth = vpt, 4 .. 8)
   hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
