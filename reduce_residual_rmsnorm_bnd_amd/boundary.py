@@ -146,8 +146,8 @@ def last_launch_shape() -> tuple[int, int, int, bool]:
 
 
 def last_launch_ring_depth() -> int:
-    """Loads in flight per one-wavefront row in this thread's last launch (2 or 8; 0 for a launch
-    with several wavefronts per row)."""
+    """Loads in flight per one-wavefront row in this thread's last launch (2, or 4, 6 or 8 for the
+    deep ring of that width; 0 for a launch with several wavefronts per row)."""
     depth = ctypes.c_int()
     _check(lib().bnd_last_launch_ring_depth(ctypes.byref(depth)))
     return depth.value

@@ -479,9 +479,10 @@ __global__ __launch_bounds__(kMaxThreads) void complete_kernel(const RowArgs a) 
 // modulo the depth whatever the source. Two at every width: deeper rings
 // measured 3-5% faster at 4096 rows for the 4- and 6-wide reads but 1-2%
 // slower at 2048, and up to 10% slower for the 12-wide read. The kernels take
-// the depth as a template argument; the 8-wide ones are also built with every
-// vector of a source in flight (depth 8), which the host takes for launches
-// of 4 to 7 rows per CU, where two loads per wave leave the memory idle.
+// the depth as a template argument; the 4-, 6- and 8-wide ones are also built
+// with every vector of a source in flight (a depth equal to the width), which
+// the host takes for launches of 6 to 7 rows per CU (4 to 7 at width 8), where
+// two loads per wave leave the memory idle.
 constexpr int wave_depth(int) { return 2; }
 
 // One source row of the fold: its resource (empty for an invalid MoE pick or a
