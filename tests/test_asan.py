@@ -159,6 +159,9 @@ int main() {
   EXPECT(auto_width(8200, 2048, true) == 0);
   EXPECT(auto_width_moe(1024, 4096) == 0);        // width 2 is not taken for MoE picks
   EXPECT(auto_width_moe(4096, 2048) == 8);
+  EXPECT(auto_width_moe(4096, 1024) == 8 && bnd_last_launch_ring_depth(&depth) == BND_OK && depth == 8);
+  EXPECT(auto_width_moe(2048, 1536) == 4 && bnd_last_launch_ring_depth(&depth) == BND_OK && depth == 4);
+  EXPECT(auto_width_moe(3072, 1024) == 0);        // the deep ring at width 6: from 6 rows per CU
   printf("host walk: %d failures\n", fails);
   return fails ? 1 : 0;
 }

@@ -1256,6 +1256,16 @@ def test_automatic_launch_shapes():
                                    torch.empty(4096, 1024, dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
     assert bnd.last_launch_shape()[3] is False
+    # MoE picks at 6 rows per CU and H = 2048 take the 4-wide deep ring
+    d = workloads.moe_inputs(7, 1536, 2048, 16, 8)
+    E, idx, gate = _moe_device(d)
+    res = torch.zeros(1536, 2048, dtype=torch.bfloat16, device=DEV)
+    s = bnd.bnd_stream_create(1536, 2048, res)
+    bnd.bnd_written(s, res)
+    bnd.bnd_moe_finalize_fold_norm(s, bnd.bnd_publish_moe(s, E, idx, gate, 8), w[:2048], 1e-6,
+                                   torch.empty(1536, 2048, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert bnd.last_launch_shape() == (1536, 64, 4, True) and bnd.last_launch_ring_depth() == 4
 
 
 @pytest.mark.parametrize("mode", [bnd.BND_ONE_WAVEFRONT_NEVER, bnd.BND_ONE_WAVEFRONT_ALWAYS],
