@@ -76,7 +76,52 @@ static int auto_width_moe(int64_t H, int64_t rows) {
   return one ? v : 0;
 }
 
+// Any automatic launch shape covers its row with a shape some kernel has: one wavefront per row at
+// the narrowest even width that covers H (up to 14 for the reads, 16 for the completes), with a
+// ring of 2 or the deep ring of its own width (4 .. 8); otherwise whole wavefronts of 1, 2 or 4
+// vectors per thread. kind: 0 fold, 1 fp8 fold, 2 complete_only, 3 MoE finalize.
+static bool auto_shape_valid(int64_t H, int64_t rows, int kind) {
+  bnd_stream* s = nullptr;
+  bnd_owed o = BND_OWED_NONE, o2 = BND_OWED_NONE;
+  const void* parts[3] = {fake(4), fake(5), fake(6)};
+  if (bnd_stream_create(&s, rows, H, 0, rows, fake(0), H) != BND_OK) return false;
+  int rc = bnd_written(s, fake(0), H);
+  if (kind == 3)
+    rc |= bnd_publish_moe(s, fake(26), 2 * rows, H, (const int32_t*)fake(27), (const float*)fake(28), 2, &o);
+  else
+    rc |= bnd_publish_partials(s, parts, 3, H, &o);
+  if (kind == 0) rc |= bnd_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr);
+  if (kind == 1)
+    rc |= bnd_fold_norm_quant_fp8(s, o, (const float*)fake(1), 1e-6f, (uint8_t*)fake(21), H, (float*)fake(22), nullptr);
+  if (kind == 2) rc |= bnd_complete_only(s, o, fake(25), H, &o2, nullptr);
+  if (kind == 3) rc |= bnd_moe_finalize_fold_norm(s, o, (const float*)fake(1), 1e-6f, fake(2), H, nullptr);
+  bnd_stream_destroy(s);
+  int64_t r = 0; int th = 0, v = 0, one = 0, depth = -1;
+  if (rc != BND_OK || bnd_last_launch_shape(&r, &th, &v, &one) != BND_OK ||
+      bnd_last_launch_ring_depth(&depth) != BND_OK || r != rows)
+    return false;
+  if (one) {
+    const int widest = kind == 2 ? 16 : 14;
+    return th == 64 && v % 2 == 0 && v >= 2 && v <= widest && (int64_t)v * 64 * 8 >= H &&
+           (v == 2 || (int64_t)(v - 2) * 64 * 8 < H) && (depth == 2 || (depth == v && v >= 4 && v <= 8));
+  }
+  return th % 64 == 0 && th >= 64 && th <= 1024 && (v == 1 || v == 2 || v == 4) && (int64_t)th * v * 8 >= H &&
+         depth == 0;
+}
+
 int main() {
+  uint64_t lcg = 0x9E3779B97F4A7C15ull;
+  auto next = [&lcg](uint64_t n) { lcg = lcg * 6364136223846793005ull + 1442695040888963407ull; return (lcg >> 33) % n; };
+  for (int c = 0; c < 400; ++c) {
+    const int64_t Hc = 8 * (int64_t)(1 + next(c % 2 ? 1024 : 4096));  // half the cases at H <= 8192
+    const int64_t rows = 1 + (int64_t)next(c % 3 ? 4096 : 40000);
+    const int kind = c % 4;
+    if (!auto_shape_valid(Hc, rows, kind)) {
+      printf("automatic shape invalid: H=%lld rows=%lld kind=%d: %s\n", (long long)Hc, (long long)rows, kind,
+             bnd_last_error());
+      ++fails;
+    }
+  }
   const int64_t H = 4096;
   bnd_owed o = BND_OWED_NONE, o2 = BND_OWED_NONE;
   const void* parts[8];
