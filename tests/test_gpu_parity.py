@@ -1402,6 +1402,41 @@ def test_random_cases_automatic_shape(orc, i):
     print(f"\n  {what}: launch {th}x{v}{' one wavefront' if one else ''}", flush=True)
 
 
+def _deep_band_case(i):
+    """Case i of the seeded sweep over the batches where the deep ring is chosen or just missed
+    (1024 .. 2047 rows, H = 1544 .. 4096): kind, sizes and slice."""
+    rng = np.random.default_rng(7700 + i)
+    kind = ["fold", "fp8", "moe", "complete_only", "add_to_output", "snapshot"][i % 6]
+    H = int(rng.choice([1544, 2048, 2056, 2600, 3072, 3080, 3600, 4096]))
+    rows = int(rng.integers(1024, 2048))
+    rb = int(rng.integers(0, 64))
+    P = int(rng.integers(1, 9))
+    return kind, rb + rows + int(rng.integers(0, 8)), H, P, rb, rows
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_cases_deep_ring_band(orc, i):
+    kind, T, H, P, rb, rows = _deep_band_case(i)
+    what = f"deep band case {i}: {kind} T={T} H={H} P/k={P} slice={rb}+{rows}"
+    if kind in ("fold", "fp8"):
+        d = workloads.fold_inputs(8700 + i, T, H, P)
+        assert_fold_matches(orc, d, what, fp8=kind == "fp8", row_begin=rb, rows=rows)
+    elif kind == "moe":
+        d = workloads.moe_inputs(8700 + i, T, H, max(P, 2), P)
+        run_moe(orc, d, rb, rows, what)
+    else:
+        d = workloads.fold_inputs(8700 + i, T, H, P)
+        extra = (workloads.to_bf16(workloads.normal_f32(8700 + i, 12345, (T, H), 0.0, 0.25))
+                 if kind == "add_to_output" else None)
+        a = _complete(d, kind, row_begin=rb, rows=rows, extra=extra)
+        e, mag = _oracle_complete(orc, d, kind, row_begin=rb, rows=rows, extra=extra)
+        tolerance.check_bf16(bits(a.view), e, mag, what)
+    r, th, v, one = bnd.last_launch_shape()
+    assert r == rows
+    print(f"\n  {what}: launch {th}x{v}{' one wavefront' if one else ''}, ring {bnd.last_launch_ring_depth()}",
+          flush=True)
+
+
 def test_concurrent_threads_on_separate_streams(orc):
     """Four host threads fold their own batches concurrently, each on its own HIP stream (default
     priority), five times each: every result equals the same call made alone, bitwise, and the
