@@ -321,6 +321,11 @@ typedef enum bnd_option {
 #define BND_ONE_WAVEFRONT_ALWAYS 1
 #define BND_ONE_WAVEFRONT_NEVER 2
 
+/* Options are process-wide (every thread and stream sees the same values) and
+ * are read when a call chooses its launch, so a change applies to the calls
+ * that follow it. bnd_set_option returns BND_ERR_INVALID_ARG, and changes
+ * nothing, for an unknown option or a value outside the ranges above;
+ * bnd_get_option returns -1 for an unknown option. */
 BND_API bnd_status bnd_set_option(bnd_option opt, int64_t value);
 BND_API int64_t bnd_get_option(bnd_option opt);
 
