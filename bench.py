@@ -447,21 +447,23 @@ def decode_chain(torch, bnd, workloads, T, reps_eager, reps_graph, H=4096, P=4, 
             "GBps_graph": bytes_b / graph / 1e9}
 
 
-def launch_floor(torch, n_launches=97, reps_eager=20, reps_graph=50, workgroups=1, threads=512):
+def launch_floor(torch, n_launches=97, reps_eager=20, reps_graph=50, workgroups=1, threads=512, with_args=False):
     """An empty kernel (libboundary_ceiling.so) launched back to back as many times as the decode
     chain launches, eager and replayed from a HIP graph: the per-launch cost with no work, the
     floor under the decode boundary's time per launch. One 512-thread workgroup is the launch
-    shape of a one-row fold at H = 4096."""
+    shape of a one-row fold at H = 4096. With `with_args` the empty kernel takes the boundary
+    kernels' argument block and reads one field of it."""
     from reduce_residual_rmsnorm_bnd_amd import _build
 
     L = ctypes.CDLL(_build.CEILING_LIB_PATH)
-    L.bnd_ceiling_empty.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
-    L.bnd_ceiling_empty.restype = ctypes.c_int
+    fn = L.bnd_ceiling_empty_args if with_args else L.bnd_ceiling_empty
+    fn.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
 
     def chain():
         hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         for _ in range(n_launches):
-            if L.bnd_ceiling_empty(workgroups, threads, hs):
+            if fn(workgroups, threads, hs):
                 raise RuntimeError("empty kernel launch failed")
 
     for _ in range(3):
@@ -487,8 +489,12 @@ def launch_floor(torch, n_launches=97, reps_eager=20, reps_graph=50, workgroups=
         g.replay()
     torch.cuda.synchronize()
     graph = (time.perf_counter() - t0) / (reps_graph * n_launches)
-    return {"launches": n_launches, "workgroups": workgroups, "threads": threads,
-            "us_per_launch_eager": eager * 1e6, "us_per_launch_graph": graph * 1e6}
+    out = {"launches": n_launches, "workgroups": workgroups, "threads": threads,
+           "us_per_launch_eager": eager * 1e6, "us_per_launch_graph": graph * 1e6}
+    if with_args:
+        L.bnd_ceiling_args_bytes.restype = ctypes.c_int
+        out["argument_bytes"] = L.bnd_ceiling_args_bytes()
+    return out
 
 
 def copy_ceiling(torch, n_bytes=1 << 30, reps=20):
@@ -925,6 +931,7 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
     log("decode chain (1 enter + 96 folds), eager and graph")
     leg(sec, "decode", lambda: [decode_chain(torch, bnd, workloads, T, 20, 50) for T in (1, 8, 32, 128)], torch)
     leg(sec, "launch_floor_empty_kernel", lambda: launch_floor(torch), torch)
+    leg(sec, "launch_floor_empty_kernel_boundary_args", lambda: launch_floor(torch, with_args=True), torch)
     leg(sec, "copy_ceiling_1GiB", lambda: copy_ceiling(torch), torch)
     return sec
 

@@ -280,40 +280,26 @@ typedef enum bnd_option {
    * return BND_ERR_UNAVAILABLE, the caller completes and folds unfused).
    * Default 0, or 1 when the environment sets BND_DISABLE_FUSED=1. */
   BND_OPT_FUSED_UNAVAILABLE = 1,
-  /* Launch shape overrides for tuning; 0 = automatic. Threads per row: a
-   * multiple of 64 in [64, 1024]. Vectors (of 8 elements) per thread: 1, 2
-   * or 4 for rows of several wavefronts, or an even count 6 .. 16 for one
-   * wavefront per row with that many vectors per lane (64 threads; H up to
-   * 64 * 8 times the count; only calls that take owed partials or MoE picks:
-   * the folds, complete_only, add_to_output, and snapshot of a Pending
-   * stream; 16 only for complete_only, add_to_output and snapshot). Under BND_ONE_WAVEFRONT_ALWAYS every forced count names the
-   * one-wavefront width (2 and 4 included; an odd count fails); under
-   * BND_ONE_WAVEFRONT_NEVER a count of 6 .. 16 fails. A shape that cannot
-   * cover H, or a one-wavefront count for any other call, fails with
-   * NO_PATH. */
+  /* Launch-shape overrides for tuning; 0 = automatic (the library's measured
+   * choice, which never changes a result: every shape gives the same bits).
+   * Threads per row: a multiple of 64 in [64, 1024]. Vectors (of 8 elements)
+   * per thread: 1, 2 or 4 for rows of several wavefronts; an even count
+   * 6 .. 16 selects one wavefront (64 threads) per row with that many
+   * vectors per lane, for calls that take owed partials or MoE picks only
+   * (up to 14 for the reads, 16 for complete_only, add_to_output, snapshot).
+   * A shape that cannot cover H, or that no kernel of the call has, fails
+   * with NO_PATH. */
   BND_OPT_THREADS_PER_ROW = 2,
   BND_OPT_VECTORS_PER_THREAD = 3,
-  /* When vectors per thread is automatic: BND_ONE_WAVEFRONT_AUTO (default)
-   * takes one wavefront per row where it is measured faster: a call that
-   * takes owed work with rows of 1544 <= H <= 7168 (8192 for complete_only,
-   * add_to_output and snapshot) and at least 6 rows per CU (4 for rows of
-   * 3080 <= H <= 4096; rows of H <= 4096 take the deep ring below 8 rows
-   * per CU, see BND_OPT_RING_DEPTH), or a call on owed partials with rows of 776 <= H <= 1024 and at
-   * least 12 rows per CU, and either no more rows than the kernel holds on
-   * the chip at once or a last round of resident rows at least 3/4 full for
-   * the folds and MoE finalize, 1/3 full for complete_only, add_to_output and
-   * snapshot. ALWAYS requires it: every call runs its one-wavefront kernel of
-   * the narrowest width that covers H (2 .. 14 vectors per lane, 16 for the
-   * completes), and a call that has none (enter, the read of a Written
-   * stream, its snapshot) or rows longer than 7168 elements (8192 for the
-   * completes) fails with NO_PATH; NEVER never takes it. */
+  /* One wavefront per row: BND_ONE_WAVEFRONT_AUTO (default) lets the library
+   * choose; ALWAYS makes every call take its one-wavefront kernel (a forced
+   * vector count then names its width, 2 and 4 included; the narrowest width
+   * that covers H otherwise; NO_PATH where the call has none); NEVER keeps
+   * every call on several wavefronts per row. */
   BND_OPT_ONE_WAVEFRONT = 4,
-  /* Loads each one-wavefront row keeps in flight: 0 = automatic (the deep
-   * ring, every vector of a source in flight, for the 4-, 6- and 8-vector
-   * kernels when a launch has 6 to 7 rows per CU, H = 1544 .. 3072, or 4 to
-   * 7, H = 3080 .. 4096; 2 otherwise), 2, or the deep ring of 4, 6 or 8
-   * (only for a launch with one wavefront per row of that many vectors per
-   * lane; NO_PATH for any other). */
+  /* Loads each one-wavefront row keeps in flight: 0 = automatic, 2, or the
+   * deep ring of 4, 6 or 8 (every vector of a source in flight; only on a
+   * one-wavefront launch of that many vectors per lane, NO_PATH otherwise). */
   BND_OPT_RING_DEPTH = 5
 } bnd_option;
 

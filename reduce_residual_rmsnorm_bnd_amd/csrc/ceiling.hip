@@ -13,6 +13,8 @@
 // gives the cost of a launch with no work, the floor under the per-boundary time of small
 // batches. Built into its own library (libboundary_ceiling.so); the boundary library does not
 // contain it.
+#include <string.h>
+
 #include "kernels.h"
 
 namespace {
@@ -113,6 +115,14 @@ __global__ __launch_bounds__(bnd::kMaxThreads) void gather_kernel(const GatherAr
 
 __global__ __launch_bounds__(bnd::kMaxThreads) void empty_kernel() {}
 
+// An empty kernel that takes the boundary kernels' argument block (RowArgs, by value) and reads
+// one field of it, as every boundary kernel does before its first load: the launch cost with the
+// boundary's kernel arguments and their first scalar load, and no work. The store never runs (the
+// host passes H = 0 and a NULL y).
+__global__ __launch_bounds__(bnd::kMaxThreads) void empty_args_kernel(const bnd::RowArgs a) {
+  if (a.H != 0 && threadIdx.x == 0) a.y[0] = 0;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
@@ -173,6 +183,22 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_empty(int64_t 
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&empty_kernel), dim3((unsigned)workgroups),
                               dim3((unsigned)threads), nullptr, 0, stream);
 }
+
+// Launches empty_args_kernel once on `stream`: as bnd_ceiling_empty, with a zeroed RowArgs block
+// (sizeof(bnd::RowArgs) bytes of kernel arguments).
+extern "C" __attribute__((visibility("default"))) int bnd_ceiling_empty_args(int64_t workgroups, int threads,
+                                                                             hipStream_t stream) {
+  if (workgroups < 1 || workgroups > 0x7fffffff || threads < 64 || threads > bnd::kMaxThreads || threads % 64)
+    return -1;
+  bnd::RowArgs a;
+  memset(&a, 0, sizeof a);
+  void* args[] = {&a};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&empty_args_kernel), dim3((unsigned)workgroups),
+                              dim3((unsigned)threads), args, 0, stream);
+}
+
+// The size in bytes of the boundary kernels' argument block.
+extern "C" __attribute__((visibility("default"))) int bnd_ceiling_args_bytes(void) { return (int)sizeof(bnd::RowArgs); }
 
 // Launches the gathering 9:2 stream once on `stream`:
 //   rows_src   device pointer to [n_src_rows, ld] bf16 rows, eight of which each output row reads

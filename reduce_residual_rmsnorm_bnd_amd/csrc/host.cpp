@@ -161,70 +161,92 @@ int compute_units() {
   return n;
 }
 
-// Launch shape: one workgroup per row; threads * vpt vectors of 8 elements
-// must cover the row. Defaults, from launch-shape sweeps on MI355X:
-//  - one vector per thread while every row of the launch can be resident at
-//    once with that shape (rows * waves per row <= 32 waves per CU): more
-//    waves per row hide more latency, 5-11% faster for 128..1024 rows;
-//  - otherwise two vectors per thread (H <= 16384), four beyond: with two
-//    vectors and P = 8 a kernel needs about 60 VGPRs, eight 4-wave workgroups
-//    fit on a CU and all 2048 rows of a prefill batch are resident together
-//    (8-wave workgroups would need two rounds, 4% slower);
-//  - workgroups of at least 256 threads are rounded up to whole multiples of
-//    256 so every SIMD of the CU gets the same number of waves (7- or 5-wave
-//    workgroups measured 3-6% slower than 8- or 4-wave ones);
-//  - a call that takes owed partials or MoE picks (the folds with bf16 or
-//    fp8 output, complete_only, add_to_output, snapshot) runs one wavefront per
-//    row (64 threads) when its rows hold 193..896 vectors (H = 1544..7168;
-//    1024 vectors, H = 8192, for the completes; the kernel of the narrowest
-//    even width of 4 to 14 (16) vectors per lane that covers the row) and the
-//    launch has at least 6 rows per CU, unless its
-//    last round of resident rows would be mostly empty; so does a call on
-//    owed partials whose rows hold 97..128 vectors (H = 776..1024, the width
-//    of 2) from 12 rows per CU. A round is as many rows as the chip holds at
-//    once: the kernel's occupancy (its 34..255 VGPRs hold 8 to 32 rows per
-//    CU) times the CUs. A launch of one round
-//    always qualifies, a longer one when its last round is at least 3/4 full
-//    for the reads and at least 1/3 full for the completes (both fractions
-//    measured, below). Against the shapes above,
-//    at 2048 rows: 5-12% faster for every such call at H = 4096 and 7168 and
-//    1-13% at H = 2048 .. 6144; between 10% slower and 5% faster at 1536
-//    rows (6 per CU); 17-87% slower at 1024 rows and below (too few waves per
-//    CU). Over whole rounds (3840 .. 8192 rows at H = 2560 .. 7168) 2-9%
-//    faster; with a last round a sixth to a half full 5-14% slower for the
-//    reads, while the completes were still 4-11% faster with their last round
-//    a third to a half full and 2-8% slower below that. The width of 2 at
-//    H = 896 .. 1024: 2-18% slower at 1536 rows, from 6% faster to 14% slower
-//    at 2048, from 7% faster to 2% slower at 3072 and 2-11% faster at 4096 and
-//    8192 for the folds and completes; the MoE finalize was 0-19% slower at
-//    every row count measured, and rows that fill half or three quarters of
-//    its lanes (H = 512, 768) were from 4% faster to 41% slower.
+// ---------------------------------------------------------------------------
+// Launch shape. One workgroup per row, in one of two kernel families:
+//  - one wavefront per row: 64 lanes x `width` vectors of 8 elements, width the
+//    narrowest even count that covers the row (2 .. 14 for the reads, 16 for the
+//    completes), only for calls that take owed partials or MoE picks;
+//  - several wavefronts per row: `threads` x `vpt` vectors (vpt 1, 2 or 4).
+// The automatic choice is the data below, from launch-shape sweeps on MI355X.
+// A "round" is the rows the chip holds at once with a kernel: its occupancy
+// in rows per CU (the HIP runtime's answer for the kernel, which its VGPRs
+// set) times the CUs.
+// ---------------------------------------------------------------------------
+
+// The one-wavefront kernel of a width is taken when the row is long enough for
+// it (its lanes more than 3/4 full at the widths of 2 and 4; a row that needs
+// a wider width always is), the call may take it (width 2: owed partials only,
+// the MoE finalize measured slower there at every row count), and either
+//  - the launch has deep_from <= rows per CU < deep_below and fits in one
+//    round of the kernel with the deep ring (every vector of a source in
+//    flight), which replaces two loads in flight where too few rows per CU
+//    would leave the memory idle; or
+//  - the launch has at least min_rows_per_cu rows per CU and fits in one
+//    round, or its last round is full enough (WaveFit::last_num / last_den).
+// Measured against the multi-wave shapes: 5-12% faster at 2048 rows for every
+// such call at H = 4096 and 7168 and 1-13% at H = 2048 .. 6144; from 10%
+// slower to 5% faster at 6 rows per CU; 17-87% slower at 4 rows per CU and
+// below with two loads in flight; with a last round a sixth to a half full,
+// 5-14% slower for the reads (the completes still 4-11% faster from a third).
+struct WaveRule {
+  int min_vectors;        // shortest row, in 16-byte vectors, that takes the width
+  bool partials_only;     // only calls on owed partials take it
+  int min_rows_per_cu;    // two loads in flight: from this many rows per CU
+  int deep_from, deep_below;  // the deep ring: rows per CU in [deep_from, deep_below)
+};
+
+constexpr WaveRule kWaveRules[bnd::kWaveWidths] = {
+    //  vectors  partials  rows/CU  deep ring
+    {97, true, 12, 0, 0},    // width 2: H = 776 .. 1024
+    {193, false, 6, 6, 8},   // width 4: H = 1544 .. 2048
+    {193, false, 6, 6, 8},   // width 6
+    {193, false, 6, 4, 8},   // width 8: H = 3080 .. 4096
+    {193, false, 6, 0, 0},   // width 10
+    {193, false, 6, 0, 0},   // width 12
+    {193, false, 6, 0, 0},   // width 14
+    {193, false, 6, 0, 0},   // width 16 (the completes)
+};
+static_assert(bnd::kWaveWidths == 8 && bnd::wave_slot(16) == 7, "one rule per width");
+
+// The multi-wave shapes: one vector per thread while the row has at most 256
+// vectors, or at most 1024 and every row of the launch is resident at once
+// (rows x waves per row <= the CU's wave slots x CUs): more waves per row
+// hide more latency, 5-11% faster for 128..1024 rows. Otherwise two vectors
+// per thread up to 2048 vectors (with P = 8 about 60 VGPRs: eight 4-wave rows
+// per CU keep a 2048-row batch resident; 8-wave rows need two rounds, 4%
+// slower), four beyond. Workgroups of 256 threads or more are whole
+// multiples of 256, so every SIMD of the CU gets the same number of waves
+// (7- or 5-wave workgroups measured 3-6% slower).
+constexpr int kWaveSlotsPerCu = 32;
+constexpr int kOneVectorAlways = 256;
+constexpr int kOneVectorResident = 1024;
+constexpr int kTwoVectors = 2048;
+
 int round_threads(int need) {
   const int unit = need >= 256 ? 4 * bnd::kWave : bnd::kWave;
   return ((need + unit - 1) / unit) * unit;
 }
 
-// The call's one-wavefront kernels: whether they exist, the rows per CU the
-// kernel of each width holds at once (0: never taken automatically), and how
-// full a launch's last round of resident rows must be, as a fraction
-// last_num / last_den of a round, for the automatic shape to take them.
+// The call's one-wavefront kernels: whether it has them, whether it takes owed
+// partials, the widest, how full a launch's last round must be, and each
+// kernel's rows per CU.
 struct WaveFit {
   bool ok = false;
-  int rows_per_cu[bnd::kWaveWidths] = {};
-  int last_num = 1;
+  bool partials = false;
+  int max_vpt = 0;
+  int last_num = 1;  // reads: 3/4 of a round; completes: 1/3
   int last_den = 1;
-  bool narrow = false;  // whether the automatic shape may take the narrowest width, 2
-  int max_vpt = 0;      // the widest one-wavefront kernel of the call
-  int deep_rows_per_cu[bnd::kWaveDeepWidths] = {};  // the same for the kernels with the deep ring (widths 4 .. 8)
+  int rows_per_cu[bnd::kWaveWidths] = {};
+  int deep_rows_per_cu[bnd::kWaveDeepWidths] = {};  // the deep-ring kernels (widths 4 .. 8)
 };
 
 WaveFit wave_fit_read(bnd::Source src, bool fp8) {
   WaveFit f;
   f.ok = true;
+  f.partials = src == Source::Partials;
+  f.max_vpt = bnd::kWaveReadVptMax;
   f.last_num = 3;
   f.last_den = 4;
-  f.narrow = src == Source::Partials;
-  f.max_vpt = bnd::kWaveReadVptMax;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_read_rows_per_cu(src, fp8, v);
   for (int v = bnd::kWaveDeepMin; v <= bnd::kWaveDeepMax; v += 2)
@@ -235,10 +257,10 @@ WaveFit wave_fit_read(bnd::Source src, bool fp8) {
 WaveFit wave_fit_complete(bnd::Source src, bnd::Tail tail) {
   WaveFit f;
   f.ok = true;
+  f.partials = src == Source::Partials;
+  f.max_vpt = bnd::kWaveVptMax;
   f.last_num = 1;
   f.last_den = 3;
-  f.narrow = src == Source::Partials;
-  f.max_vpt = bnd::kWaveVptMax;
   for (int v = bnd::kWaveVptMin; v <= bnd::kWaveVptMax; v += 2)
     f.rows_per_cu[bnd::wave_slot(v)] = bnd::wave_complete_rows_per_cu(src, tail, v);
   for (int v = bnd::kWaveDeepMin; v <= bnd::kWaveDeepMax; v += 2)
@@ -254,25 +276,9 @@ void warm_launch_queries() {
   static std::once_flag once;
   std::call_once(once, [] {
     compute_units();
-    for (int w = bnd::kWaveVptMin; w <= bnd::kWaveVptMax; w += 2) {
-      for (bool fp8 : {false, true}) {
-        bnd::wave_read_rows_per_cu(Source::Partials, fp8, w);
-        bnd::wave_read_rows_per_cu(Source::Moe, fp8, w);
-      }
-      for (bnd::Tail t : {bnd::Tail::None, bnd::Tail::Extra, bnd::Tail::Residual}) {
-        bnd::wave_complete_rows_per_cu(Source::Partials, t, w);
-        bnd::wave_complete_rows_per_cu(Source::Moe, t, w);
-      }
-    }
-    for (int w = bnd::kWaveDeepMin; w <= bnd::kWaveDeepMax; w += 2) {
-      for (bool fp8 : {false, true}) {
-        bnd::wave_read_rows_per_cu(Source::Partials, fp8, w, true);
-        bnd::wave_read_rows_per_cu(Source::Moe, fp8, w, true);
-      }
-      for (bnd::Tail t : {bnd::Tail::None, bnd::Tail::Extra, bnd::Tail::Residual}) {
-        bnd::wave_complete_rows_per_cu(Source::Partials, t, w, true);
-        bnd::wave_complete_rows_per_cu(Source::Moe, t, w, true);
-      }
+    for (Source src : {Source::Partials, Source::Moe}) {
+      for (bool fp8 : {false, true}) (void)wave_fit_read(src, fp8);
+      for (bnd::Tail t : {bnd::Tail::None, bnd::Tail::Extra, bnd::Tail::Residual}) (void)wave_fit_complete(src, t);
     }
   });
 }
@@ -287,6 +293,24 @@ bool rounds_fill(int64_t rows, int64_t per_round, int num, int den) {
   return last * den >= per_round * num;
 }
 
+// The automatic one-wavefront choice for a row of nvec vectors (kWaveRules);
+// *deep tells whether it takes the deep ring. `ring_two` is a forced ring of two.
+bool auto_one_wave(int nvec, int64_t rows, int64_t cus, const WaveFit& wave, bool ring_two, bool* deep) {
+  const int width = bnd::wave_width(nvec);
+  const int w = bnd::wave_slot(width);
+  if (!wave.ok || w < 0 || width > wave.max_vpt) return false;
+  const WaveRule& r = kWaveRules[w];
+  if (nvec < r.min_vectors || (r.partials_only && !wave.partials)) return false;
+  const int d = bnd::deep_slot(width);
+  if (d >= 0 && !ring_two && rows >= r.deep_from * cus && rows < r.deep_below * cus &&
+      rows <= (int64_t)wave.deep_rows_per_cu[d] * cus) {
+    *deep = true;
+    return true;
+  }
+  return rows >= r.min_rows_per_cu * cus &&
+         rounds_fill(rows, (int64_t)wave.rows_per_cu[w] * cus, wave.last_num, wave.last_den);
+}
+
 bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l) {
   const int nvec = (int)(H / 8);
   int vpt = g_vpt_override.load();
@@ -294,7 +318,6 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
   const int one_wave_mode = g_one_wave_mode.load();
   const int depth = g_depth_override.load();
   const int64_t cus = compute_units();
-  const int width = bnd::wave_width(nvec);  // the one-wavefront width that covers the row
   const bool forced = vpt != 0;
   // A forced count of 6 .. 16 is one wavefront per row; under ALWAYS every
   // forced count is (2 and 4 included); under NEVER none may be.
@@ -304,36 +327,17 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
     return fail(BND_ERR_NO_PATH, "%d vectors per thread is one wavefront per row, which is switched off", vpt);
   if (!forced && one_wave_mode == BND_ONE_WAVEFRONT_ALWAYS) {
     one_wave = true;
-    vpt = width;
+    vpt = bnd::wave_width(nvec);
   } else if (!forced) {
-    const int w = bnd::wave_slot(width);
-    // The row must fill more than 3/4 of the width's lanes: 193 vectors or more for the widths of
-    // 4 and above, 97 .. 128 for width 2, which only the calls on owed partials take, from 12
-    // rows per CU (6 for the others).
-    const bool two = width == 2;
-    const bool fills = two ? wave.narrow && 4 * nvec > 3 * 2 * bnd::kWave : nvec > 3 * bnd::kWave;
-    // The kernels with the deep ring take launches of 6 to 7 rows per CU at widths 4 and 6, and
-    // of 4 to 7 at width 8 (one round).
-    const int d = bnd::deep_slot(width);
-    const bool deep_fits = d >= 0 && depth != 2 && rows >= (width == 8 ? 4 : 6) * cus && rows < 8 * cus &&
-                           rows <= (int64_t)wave.deep_rows_per_cu[d] * cus;
-    const bool auto_wave = one_wave_mode == BND_ONE_WAVEFRONT_AUTO && wave.ok && w >= 0 && width <= wave.max_vpt &&
-                           fills;
-    if (auto_wave && deep_fits) {
+    if (one_wave_mode == BND_ONE_WAVEFRONT_AUTO && auto_one_wave(nvec, rows, cus, wave, depth == 2, &deep)) {
       one_wave = true;
-      deep = true;
-      vpt = width;
-    } else if (auto_wave && rows >= (two ? 12 : 6) * cus &&
-               rounds_fill(rows, wave.rows_per_cu[w] * cus, wave.last_num, wave.last_den)) {
-      one_wave = true;
-      vpt = width;
-    } else if (nvec <= 256) {
-      vpt = 1;
-    } else if (nvec <= 1024 &&
-               rows * (int64_t)(round_threads(nvec) / bnd::kWave) <= cus * 32) {
+      vpt = bnd::wave_width(nvec);
+    } else if (nvec <= kOneVectorAlways ||
+               (nvec <= kOneVectorResident &&
+                rows * (int64_t)(round_threads(nvec) / bnd::kWave) <= cus * kWaveSlotsPerCu)) {
       vpt = 1;
     } else {
-      vpt = nvec <= 2048 ? 2 : 4;
+      vpt = nvec <= kTwoVectors ? 2 : 4;
     }
   }
   if (one_wave) {

@@ -177,34 +177,97 @@ __device__ __forceinline__ float wave_max(float v) {
   return lane63(v);
 }
 
-// Row totals across the workgroup's wavefronts: one LDS slot per wave and a
-// single barrier; every thread then adds the slots in wave order, so all
-// threads hold the same, order-fixed result.
-template <bool kWithMax>
-__device__ __forceinline__ void block_reduce(float& ss, float& mx, float* lds_sum, float* lds_max) {
-  ss = wave_sum(ss);
-  if constexpr (kWithMax) mx = wave_max(mx);
-  const int nw = blockDim.x / kWave;
-  if (nw == 1) return;
-  const int wid = threadIdx.x / kWave;
-  if ((threadIdx.x % kWave) == 0) {
-    lds_sum[wid] = ss;
-    if constexpr (kWithMax) lds_max[wid] = mx;
+// The sum of squares of a row, in one order that does not depend on the launch
+// shape, so that a row gets the same inv (and so the same y and fp8 codes) from
+// every kernel and workgroup size, in a full call and in a share of its rows:
+//   q_v  = the squares of vector v's eight elements added in element order,
+//          one fma each, from 0 (vector_ss);
+//   A_l  = q_l + q_{l+64} + q_{l+128} + ..., added left to right, for each of
+//          the 64 lanes l (the vectors a lane of a one-wavefront row owns, in
+//          the order it owns them);
+//   sum  = wave_sum over the 64 A_l.
+// Vectors past the end of the row count as q = +0, which leaves every sum
+// unchanged, so the number of lanes and vectors a launch has beyond the row
+// does not matter either.
+__device__ __forceinline__ float vector_ss(const float (&x)[8]) {
+  float q = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q = fmaf(x[e], x[e], q);
+  return q;
+}
+
+// The row's total from a workgroup of blockDim.x threads (a multiple of 64),
+// thread t holding the q of vectors t, t + blockDim.x, ... (VPT of them): with
+// several wavefronts every q goes to LDS by its vector index and, after one
+// barrier, every lane l adds the q of vectors l, l + 64, ... in that order and
+// the wavefront sums the 64 lane totals, so all threads hold the same result.
+// With kWithMax the row's max of mx (non-negative values) too, through one LDS
+// slot per wave (a max does not depend on its order).
+template <int VPT, bool kWithMax>
+__device__ __forceinline__ void row_reduce(const float (&q)[VPT], float& ss, float& mx, float* lds_q,
+                                           float* lds_max) {
+  const int nthr = blockDim.x;
+  const int nw = nthr / kWave;
+  const int tid = threadIdx.x;
+  float lane_total = 0.0f;
+  if (nw == 1) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) lane_total += q[v];
+    ss = wave_sum(lane_total);
+    if constexpr (kWithMax) mx = wave_max(mx);
+    return;
+  }
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) lds_q[tid + v * nthr] = q[v];
+  if constexpr (kWithMax) {
+    mx = wave_max(mx);
+    if ((tid % kWave) == 0) lds_max[tid / kWave] = mx;
   }
   __syncthreads();
-  float t = 0.0f, m = 0.0f;
-  for (int i = 0; i < nw; ++i) {
-    t += lds_sum[i];
-    if constexpr (kWithMax) m = fmaxf(m, lds_max[i]);
+  const int lane = tid % kWave;
+  const int n = nw * VPT;  // vectors per lane l: l, l + 64, ..., l + 64 (n - 1)
+  for (int j = 0; j < n; ++j) lane_total += lds_q[lane + j * kWave];
+  ss = wave_sum(lane_total);
+  if constexpr (kWithMax) {
+    float m = 0.0f;
+    for (int i = 0; i < nw; ++i) m = fmaxf(m, lds_max[i]);
+    mx = m;
   }
-  ss = t;
-  mx = m;
 }
 
 // ---------------------------------------------------------------------------
 // Loading and completing the contribution of one row: x[v][e] for the
 // thread's VPT vectors. Lanes past the end of the row hold zeros.
 // ---------------------------------------------------------------------------
+
+// A MoE row's picks: lane j < k holds the index and gate of pick j, fetched
+// with one load each when the row starts (lanes >= k read 0 through the
+// resource's bounds), so resolving a pick later is a register read
+// (v_readlane), not a dependent memory access, and no load waits on another:
+// a dropped pick's gate is replaced by 0 after both loads have returned.
+struct RowPicks {
+  int idx = 0;
+  float gate = 0.0f;
+};
+
+__device__ __forceinline__ RowPicks load_picks(const RowArgs& a, int64_t row, int k, int lane) {
+  const Rsrc ir = row_rsrc(a.idx + row * k, k * 4);
+  const Rsrc gr = row_rsrc(a.gate + row * k, k * 4);
+  RowPicks p;
+  p.idx = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, lane * 4, 0, 0);
+  p.gate = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, lane * 4, 0, 0));
+  return p;
+}
+
+// Pick j of a row (wave-uniform): its expert row, -1 when the index is outside
+// the buffer, and its gate, 0 for such a dropped pick whatever the gate holds.
+__device__ __forceinline__ void resolve_pick(const RowArgs& a, const RowPicks& picks, int j, int64_t& er, float& g) {
+  const int64_t e = __builtin_amdgcn_readlane(picks.idx, j);
+  const float gj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(picks.gate), j));
+  const bool valid = e >= 0 && e < a.n_expert_rows;
+  er = valid ? e : -1;
+  g = valid ? gj : 0.0f;
+}
 
 // Loads are issued by every lane without a guard: a lane past the end of the
 // row addresses beyond its row resource and reads 0, which keeps the loads
@@ -264,14 +327,26 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
       if constexpr (kB < VPT) __builtin_amdgcn_sched_barrier(0);
     }
   } else if constexpr (S == Source::Moe) {
+    // The row's k indices and gates, wave-uniform scalar loads all issued before any is used. A
+    // dropped pick adds g * 0 with g = 0: nothing, whatever its gate holds (NaN or inf too). The
+    // empty asm takes each loaded gate as an operand, so the load is unconditional and the select
+    // below picks between registers (a select on a load would otherwise become a branch around
+    // the load, one memory round trip per pick).
     int64_t er[N];
     float g[N];
+    int ev[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int64_t e = a.idx[row * N + j];
-      const bool valid = e >= 0 && e < a.n_expert_rows;
-      er[j] = valid ? e : -1;
+      ev[j] = a.idx[row * N + j];
       g[j] = a.gate[row * N + j];
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) asm volatile("" : "+s"(g[j]));
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const bool valid = ev[j] >= 0 && ev[j] < a.n_expert_rows;
+      er[j] = valid ? ev[j] : -1;
+      g[j] = valid ? g[j] : 0.0f;
     }
     constexpr int kB = load_batch(N, VPT);
 #pragma unroll
@@ -280,7 +355,7 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
       uint4 r[kB];
 #pragma unroll
       for (int j = 0; j < N; ++j) {
-        // an invalid pick gets an empty resource: its loads return 0 and it is skipped anyway
+        // an invalid pick gets an empty resource: its loads return 0 and its gate is 0
         const Rsrc src = row_rsrc(a.experts + (er[j] < 0 ? 0 : er[j]) * a.ld_e, er[j] < 0 ? 0 : row_bytes);
 #pragma unroll
         for (int b = 0; b < kB; ++b) c[j][b] = load16(src, off[v0 + b]);
@@ -343,7 +418,7 @@ __device__ __forceinline__ void load_weight(const RowArgs& a, int tid, int nthr,
 // ---------------------------------------------------------------------------
 template <Source S, int N, int VPT, bool FP8>
 __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
-  __shared__ float lds_sum[kMaxThreads / kWave];
+  __shared__ float lds_q[kMaxThreads * VPT];  // the row's per-vector sums of squares, by vector
   __shared__ float lds_max[kMaxThreads / kWave];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -359,18 +434,16 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
   float w[VPT][8];
   load_weight<VPT>(a, tid, nthr, w);
 
-  float ss = 0.0f, mx = 0.0f;
+  float ss = 0.0f, mx = 0.0f, q[VPT];
 #pragma unroll
-  for (int v = 0; v < VPT; ++v)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(x[v][e], x[v][e], ss);
+  for (int v = 0; v < VPT; ++v) q[v] = vector_ss(x[v]);
   if constexpr (FP8) {
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[v][e] * w[v][e]));
   }
-  block_reduce<FP8>(ss, mx, lds_sum, lds_max);
+  row_reduce<VPT, FP8>(q, ss, mx, lds_q, lds_max);
   const float inv = 1.0f / sqrtf(ss / (float)a.H + a.eps);
 
   const int row_bytes = a.H * 2;
@@ -387,7 +460,7 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
     for (int v = 0; v < VPT; ++v) {
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (x[v][e] * inv) * w[v][e];
+      for (int e = 0; e < 8; ++e) y[e] = (x[v][e] * w[v][e]) * inv;  // the one-wavefront read's order
       if (ok[v]) store16(yr, (tid + v * nthr) * 16, f32_to_bf16x8(y));
     }
   } else {
@@ -492,24 +565,10 @@ struct RowSource {
   float g;
 };
 
-// A MoE row's picks: lane j < k holds the index and gate of pick j, fetched
-// with one load each when the row starts, so resolving a pick later is a
-// register read (v_readlane), not a dependent memory access. Lanes >= k read 0.
-struct RowPicks {
-  int idx = 0;
-  float gate = 0.0f;
-};
-
 template <Source S>
 __device__ __forceinline__ RowPicks row_picks(const RowArgs& a, int64_t row, int lane) {
-  RowPicks k;
-  if constexpr (S == Source::Moe) {
-    const Rsrc ir = row_rsrc(a.idx + row * a.nsrc, a.nsrc * 4);
-    const Rsrc gr = row_rsrc(a.gate + row * a.nsrc, a.nsrc * 4);
-    k.idx = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, lane * 4, 0, 0);
-    k.gate = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, lane * 4, 0, 0));
-  }
-  return k;
+  if constexpr (S == Source::Moe) return load_picks(a, row, a.nsrc, lane);
+  return RowPicks{};
 }
 
 template <Source S>
@@ -519,10 +578,12 @@ __device__ __forceinline__ RowSource row_source(const RowArgs& a, const RowPicks
   if constexpr (S == Source::Partials) {
     return {row_rsrc(a.src[p] + row * a.ld_src, rb), 1.0f};
   } else {
-    const int64_t e = __builtin_amdgcn_readlane(picks.idx, p);
-    const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(picks.gate), p));
-    const bool valid = e >= 0 && e < a.n_expert_rows;
-    return {row_rsrc(a.experts + (valid ? e : 0) * a.ld_e, valid ? rb : 0), g};
+    // a dropped pick reads zeros through an empty resource with a zero gate: it adds nothing,
+    // whatever its gate holds
+    int64_t e;
+    float g;
+    resolve_pick(a, picks, p, e, g);
+    return {row_rsrc(a.experts + (e < 0 ? 0 : e) * a.ld_e, e < 0 ? 0 : rb), g};
   }
 }
 
@@ -627,9 +688,9 @@ __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[v][e] = t[e] + x[v][e];  // residual + contribution
     store16(res, (lane + v * kWave) * 16, f32_to_bf16x8(x[v]));
+    ss += vector_ss(x[v]);  // this lane's vectors in index order: the shape-free order of row_reduce
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ss = fmaf(x[v][e], x[v][e], ss);
       x[v][e] = x[v][e] * w[e];
       mx = fmaxf(mx, fabsf(x[v][e]));
     }

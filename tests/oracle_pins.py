@@ -237,7 +237,8 @@ def pin_bruteforce_moe(o):
     for seed, T, H, ne, k, rb in [(31, 3, 8, 6, 2, 0), (32, 4, 16, 8, 3, 1), (33, 2, 8, 4, 4, 0)]:
         E, idx, gate, res_full, w = _tiny_moe_case(seed, T, H, ne, k)
         if seed == 33:
-            idx[1] = E.shape[0] + 5   # an index outside the buffer contributes nothing
+            idx[1] = E.shape[0] + 5   # an index outside the buffer contributes nothing,
+            gate[1] = np.float32("nan")  # whatever its gate holds
         rows = T - rb
         out = o.moe_fold_norm(E, idx, gate, k, res_full[rb:].copy(), w, eps, row_begin=rb,
                               rows=rows)

@@ -22,8 +22,9 @@ def _lib():
     L.bnd_ceiling_mix.argtypes = [ctypes.POINTER(VP), ctypes.c_int, VP, VP, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, VP]
     L.bnd_ceiling_mix.restype = ctypes.c_int
-    L.bnd_ceiling_empty.argtypes = [ctypes.c_int64, ctypes.c_int, VP]
-    L.bnd_ceiling_empty.restype = ctypes.c_int
+    for fn in (L.bnd_ceiling_empty, L.bnd_ceiling_empty_args):
+        fn.argtypes = [ctypes.c_int64, ctypes.c_int, VP]
+        fn.restype = ctypes.c_int
     L.bnd_ceiling_gather_9r2w.argtypes = [VP, ctypes.c_int64, VP, VP, VP, VP, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_int, ctypes.c_int, VP]
     L.bnd_ceiling_gather_9r2w.restype = ctypes.c_int
@@ -61,6 +62,7 @@ def test_ceiling_refuses_bad_shapes():
     assert L.bnd_ceiling_mix_9r2w(src, o0, None, 4, 4096, 4096, 512, 1, None) == -1  # 9:2 needs two outputs
     for wg, threads in ((0, 64), (1, 32), (1, 100), (1, 2048), (1 << 31, 64)):
         assert L.bnd_ceiling_empty(wg, threads, None) == -1, (wg, threads)
+        assert L.bnd_ceiling_empty_args(wg, threads, None) == -1, (wg, threads)
     E, idx, s8 = VP(a), VP(a + (30 << 24)), VP(a + (31 << 24))
     bad_gather = [
         (None, 64, idx, s8, o0, o1, 4, 4096, 4096, 64, 8),    # no source rows
@@ -80,6 +82,7 @@ def test_empty_kernel_launches():
     L = _lib()
     assert L.bnd_ceiling_empty(1, 512, torch.cuda.current_stream().cuda_stream) == 0
     assert L.bnd_ceiling_empty(300, 64, torch.cuda.current_stream().cuda_stream) == 0
+    assert L.bnd_ceiling_empty_args(1, 512, torch.cuda.current_stream().cuda_stream) == 0
     torch.cuda.synchronize()
 
 

@@ -46,9 +46,9 @@ class forced_shape:
     one_wave, the one-wavefront mode instead (ALWAYS: the narrowest one-wavefront kernel that
     covers H, which is how the 4-vector kernel is reached).
 
-    The residual is elementwise and does not depend on the launch shape; the read's sum of
-    squares is reduced in an order fixed by the shape, so comparisons of y between calls with
-    different row counts are bit-exact only under one shape."""
+    No result depends on the launch shape: the residual is elementwise, and every kernel reduces
+    a row's sum of squares in the same order, so y, the fp8 codes and scales are bitwise the same
+    under every shape (test_every_launch_shape_gives_the_same_bits)."""
 
     def __init__(self, threads, vpt, one_wave=bnd.BND_ONE_WAVEFRONT_AUTO, depth=0):
         self.threads, self.vpt, self.one_wave, self.depth = threads, vpt, one_wave, depth
@@ -265,14 +265,14 @@ def test_moe_full_and_slice(orc):
     d = workloads.moe()
     full_res, full_y = run_moe(orc, d, 0, d["T"], "MoE T=2048 H=4096 k=8")
     rb, rows = workloads.MOE_SLICE
+    full_shape = bnd.last_launch_shape()
     sl_res, sl_y = run_moe(orc, d, rb, rows, "MoE slice rows 768..1023")
-    # the slice stores exactly the residual rows of the full call, whatever the launch shapes
+    slice_shape = bnd.last_launch_shape()
+    print(f"\n  MoE launch shapes: full {full_shape}, slice {slice_shape}", flush=True)
+    # the share stores exactly the rows of the full call, each under the library's own launch
+    # choice (which differs between the two)
     assert torch.equal(sl_res.view, full_res.view[rb:rb + rows])
-    # and under one launch shape exactly the same y
-    with forced_shape(256, 2):
-        _, fy = run_moe(orc, d, 0, d["T"], "MoE full, 256x2")
-        _, sy = run_moe(orc, d, rb, rows, "MoE slice, 256x2")
-    assert torch.equal(sy.view, fy.view[rb:rb + rows])
+    assert torch.equal(sl_y.view, full_y.view[rb:rb + rows])
 
 
 @pytest.mark.parametrize("T", [1, 8, 32, 128])
@@ -386,6 +386,15 @@ def test_moe_edge_cases(orc):
     idx[17] = d["expert_rows"].shape[0]
     d["idx"] = idx
     run_moe(orc, d, 0, 40, "MoE k=16 with out-of-range indices")
+    # nothing, whatever the dropped pick's gate holds
+    gate = d["gate"].clone()
+    gate[5] = float("nan")
+    gate[17] = float("inf")
+    d["gate"] = gate
+    for shape in ((256, 1), (64, 2, bnd.BND_ONE_WAVEFRONT_ALWAYS)):
+        with forced_shape(*shape):
+            res, y = run_moe(orc, d, 0, 40, f"MoE k=16, dropped picks with NaN and inf gates, {shape}")
+        assert torch.isfinite(y.view.float()).all() and torch.isfinite(res.view.float()).all()
     d1 = workloads.moe_inputs(12, 9, 264, 4, 1)  # k = 1, ragged H
     run_moe(orc, d1, 3, 5, "MoE k=1 slice")
 
@@ -438,14 +447,105 @@ def test_invariant_moe_over_stacked_partials_is_fold(orc):
 
 
 def test_invariant_slice_equals_full_rows(orc):
+    """A share's rows are bitwise the full call's rows, under the automatic shapes and with the
+    full call and the shares under different forced shapes."""
     d = workloads.fold_inputs(24, 64, 4096, 8)
-    for shape in ((256, 2), (512, 1)):
-        with forced_shape(*shape):
-            full = run_fold(d)
-            for rb, rows in ((0, 8), (24, 16), (56, 8), (63, 1)):
+    full = run_fold(d)
+    full_fp8 = run_fold(d, fp8=True)
+    for shape in (None, (256, 2), (512, 1), (64, 8, bnd.BND_ONE_WAVEFRONT_ALWAYS)):
+        for rb, rows in ((0, 8), (24, 16), (56, 8), (63, 1)):
+            if shape is None:
                 part = run_fold(d, row_begin=rb, rows=rows)
-                assert torch.equal(part["y"].view, full["y"].view[rb:rb + rows])
-                assert torch.equal(part["res"].view, full["res"].view[rb:rb + rows])
+                part_fp8 = run_fold(d, row_begin=rb, rows=rows, fp8=True)
+            else:
+                with forced_shape(*shape):
+                    part = run_fold(d, row_begin=rb, rows=rows)
+                    part_fp8 = run_fold(d, row_begin=rb, rows=rows, fp8=True)
+            assert torch.equal(part["y"].view, full["y"].view[rb:rb + rows]), (shape, rb, rows)
+            assert torch.equal(part["res"].view, full["res"].view[rb:rb + rows])
+            assert torch.equal(part_fp8["q"].view, full_fp8["q"].view[rb:rb + rows]), (shape, rb, rows)
+            assert torch.equal(part_fp8["scale_buf"][1:rows + 1], full_fp8["scale_buf"][1 + rb:1 + rb + rows])
+
+
+MULTI_WAVE_SHAPES = [(64, 1), (128, 1), (256, 1), (512, 1), (1024, 1), (64, 2), (128, 2), (256, 2),
+                     (320, 2), (512, 2), (64, 4), (128, 4), (192, 4), (256, 4)]
+
+
+def _launch_shapes(H):
+    """Every multi-wave shape and one-wavefront width (ring of two, and the deep ring where it is
+    built) that covers a row of H elements: (label, forced_shape arguments, multi-wave?)."""
+    nvec = H // 8
+    out = [("auto", None, True)]
+    out += [(f"{t}x{v}", (t, v), True) for t, v in MULTI_WAVE_SHAPES if t * v >= nvec]
+    for w in range(2, 15, 2):
+        if 64 * w >= nvec:
+            out.append((f"wave{w}", (64, w, bnd.BND_ONE_WAVEFRONT_ALWAYS), False))
+            if w in (4, 6, 8):
+                out.append((f"wave{w}deep", (64, w, bnd.BND_ONE_WAVEFRONT_ALWAYS, w), False))
+    return out
+
+
+@pytest.mark.parametrize("H", [1016, 3600, 4096, 7168])
+def test_every_launch_shape_gives_the_same_bits(orc, H):
+    """Every kernel reduces a row's sum of squares in one order, so the residual, y, the fp8 codes
+    and their scales are bitwise the same under every launch shape: folds with bf16 and fp8 output,
+    the MoE finalize, enter and the read of a Written stream. The automatic shape's results are
+    also checked against the oracle."""
+    T = 37
+    d = workloads.fold_inputs(600 + H, T, H, 8)
+    dm = workloads.moe_inputs(700 + H, T, H, 16, 8)
+
+    def call(kind):
+        if kind == "fold":
+            g = run_fold(d)
+            return g["res"].view, g["y"].view
+        if kind == "fp8":
+            g = run_fold(d, fp8=True)
+            return g["res"].view, g["q"].view, g["scale_buf"][1:T + 1]
+        if kind == "moe":
+            res, y = _moe_only(dm, 0, T)
+            return res.view, y.view
+        # enter, then the read of the Written stream it leaves
+        res, y, y2 = Guarded(T, H), Guarded(T, H), Guarded(T, H)
+        st = bnd.bnd_stream_create(T, H, res.view)
+        bnd.bnd_enter_norm(st, d["residual"].to(DEV), d["weight"].to(DEV), d["eps"], y.view)
+        bnd.bnd_fold_norm(st, bnd.BND_OWED_NONE, d["weight"].to(DEV), d["eps"], y2.view)
+        torch.cuda.synchronize()
+        return res.view, y.view, y2.view
+
+    assert_fold_matches(orc, d, f"H={H} automatic shape")
+    assert_fold_matches(orc, d, f"H={H} automatic shape fp8", fp8=True)
+    run_moe(orc, dm, 0, T, f"MoE H={H} automatic shape")
+    base = {}
+    checked = 0
+    for label, shape, multi in _launch_shapes(H):
+        for kind in ("fold", "fp8", "moe") + (("enter",) if multi else ()):
+            if shape is None:
+                got = call(kind)
+            else:
+                with forced_shape(*shape):
+                    got = call(kind)
+            if kind not in base:
+                base[kind] = got
+                continue
+            for a, b in zip(got, base[kind]):
+                assert torch.equal(a, b), f"{kind} under {label} differs from the automatic shape"
+            checked += 1
+    print(f"\n  H={H}: {checked} calls under forced shapes bitwise equal to the automatic shape", flush=True)
+
+
+def _moe_only(d, row_begin, rows):
+    """The MoE finalize through the library without the oracle: (residual, y) guarded buffers."""
+    T, H, k = d["T"], d["H"], d["k"]
+    E, idx, gate = _moe_device(d)
+    res = Guarded(rows, H).from_host(d["residual"][row_begin:row_begin + rows])
+    y = Guarded(rows, H)
+    s = bnd.bnd_stream_create(T, H, res.view, row_begin, rows)
+    bnd.bnd_written(s, res.view)
+    owed = bnd.bnd_publish_moe(s, E, idx, gate, k)
+    bnd.bnd_moe_finalize_fold_norm(s, owed, d["weight"].to(DEV), d["eps"], y.view)
+    torch.cuda.synchronize()
+    return res, y
 
 
 # ------------------------------------------------------------------ unfused fallback
@@ -651,19 +751,16 @@ def test_rsv_shares_tile_the_batch(orc, fp8):
     d = workloads.fold_inputs(81, T, 4096, 8)
     key = "q" if fp8 else "y"
     full = run_fold(d, fp8=fp8)
-    with forced_shape(256, 2):
-        full_f = run_fold(d, fp8=fp8)
     for r in range(len(RSV_COUNTS)):
         rb, rows, t = bnd.bnd_rsv_share(RSV_COUNTS, r)
         assert t == T
+        # each share under the library's own launch choice, which differs with its row count
         part = run_fold(d, row_begin=rb, rows=rows, fp8=fp8)
         assert torch.equal(part["res"].view, full["res"].view[rb:rb + rows])
-        with forced_shape(256, 2):
-            part_f = run_fold(d, row_begin=rb, rows=rows, fp8=fp8)
-        assert torch.equal(part_f[key].view, full_f[key].view[rb:rb + rows])
+        assert torch.equal(part[key].view, full[key].view[rb:rb + rows]), f"share {r}"
         if fp8:
-            assert torch.equal(part_f["scale_buf"][1:rows + 1],
-                               full_f["scale_buf"][1 + rb:1 + rb + rows])
+            assert torch.equal(part["scale_buf"][1:rows + 1],
+                               full["scale_buf"][1 + rb:1 + rb + rows])
     for r in (2, 5):
         rb, rows, _ = bnd.bnd_rsv_share(RSV_COUNTS, r)
         assert_fold_matches(orc, d, f"RSv share {r} ({rows} rows at {rb})", fp8=fp8, row_begin=rb,
@@ -678,7 +775,7 @@ def test_rsv_moe_shares(orc):
         rb, rows, _ = bnd.bnd_rsv_share(counts, r)
         res, y = run_moe(orc, d, rb, rows, f"MoE RSv share {r}")
         assert torch.equal(res.view, full_res.view[rb:rb + rows])
-        assert torch.equal(y.view, full_y.view[rb:rb + rows])  # same shape: fewer rows than CUs
+        assert torch.equal(y.view, full_y.view[rb:rb + rows])
 
 
 # ------------------------------------------------------------------ add_to_output, snapshot
@@ -895,16 +992,14 @@ def test_wave_rows_edge_cases(orc, vpt, H):
 
 @pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
 def test_wave_rows_residual_matches_other_shapes(orc, vpt, H):
-    """The residual is elementwise: bitwise the same for every launch shape; y agrees with the
-    oracle under each."""
+    """One wavefront per row and the multi-wave shape give bitwise the same residual and y."""
     d = workloads.fold_inputs(32, 64, H, 8)
     with forced_wave(vpt):
         a = run_fold(d)
     with forced_shape(512, 2):
         b = run_fold(d)
     assert torch.equal(a["res"].view, b["res"].view)
-    diff = (bits(a["y"].view).astype(np.int32) - bits(b["y"].view).astype(np.int32))
-    assert np.abs(diff).max() <= 1, "y of two launch shapes more than one bf16 step apart"
+    assert torch.equal(a["y"].view, b["y"].view)
 
 
 def test_wave_rows_moe(orc):
@@ -1142,46 +1237,49 @@ def test_wave_rows_over_several_rounds(orc):
     """Launches for which the automatic shape takes one wavefront per row over more than one round
     of resident rows, against the oracle on every row: a fold, an fp8 fold and a MoE finalize over
     two whole rounds (4096 rows at H = 7168) and a complete_only whose last round is half full
-    (6144 rows at H = 4096)."""
-    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
-        pytest.skip("round sizes are for 256 compute units")
-    d = workloads.fold_inputs(420, 4096, 7168, 3)
-    assert_fold_matches(orc, d, "fold T=4096 H=7168 P=3, two rounds")
-    assert bnd.last_launch_shape() == (4096, 64, 14, True)
-    assert_fold_matches(orc, d, "fp8 fold T=4096 H=7168 P=3, two rounds", fp8=True)
-    assert bnd.last_launch_shape() == (4096, 64, 14, True)
-    dm = workloads.moe_inputs(422, 4096, 7168, 16, 4)
-    run_moe(orc, dm, 0, 4096, "MoE finalize T=4096 H=7168 k=4, two rounds")
-    assert bnd.last_launch_shape() == (4096, 64, 14, True)
+    (6144 rows at H = 4096), as row counts of 16 and 24 per CU."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    T = 16 * cus  # 4096 rows on 256 CUs
+    d = workloads.fold_inputs(420, T, 7168, 3)
+    assert_fold_matches(orc, d, f"fold T={T} H=7168 P=3, two rounds")
+    assert bnd.last_launch_shape() == (T, 64, 14, True)
+    assert_fold_matches(orc, d, f"fp8 fold T={T} H=7168 P=3, two rounds", fp8=True)
+    assert bnd.last_launch_shape() == (T, 64, 14, True)
+    dm = workloads.moe_inputs(422, T, 7168, 16, 4)
+    run_moe(orc, dm, 0, T, f"MoE finalize T={T} H=7168 k=4, two rounds")
+    assert bnd.last_launch_shape() == (T, 64, 14, True)
     del dm
-    d = workloads.fold_inputs(421, 6144, 4096, 3)
+    T = 24 * cus  # 6144 rows on 256 CUs
+    d = workloads.fold_inputs(421, T, 4096, 3)
     out = _complete(d, "complete_only")
-    assert bnd.last_launch_shape() == (6144, 64, 8, True)
+    assert bnd.last_launch_shape() == (T, 64, 8, True)
     ex, mag = _oracle_complete(orc, d, "complete_only")
-    tolerance.check_bf16(bits(out.view), ex, mag, "complete_only T=6144 H=4096 P=3, 1.5 rounds")
+    tolerance.check_bf16(bits(out.view), ex, mag, f"complete_only T={T} H=4096 P=3, 1.5 rounds")
 
 
 def test_automatic_one_wave_at_its_shortest_rows(orc):
     """The shortest rows the automatic shape gives one wavefront (H = 1544: 193 vectors, so only
     lane 0 holds a fourth) and the longest it does not (H = 1536), at 6 rows per CU, against the
     oracle."""
-    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
-        pytest.skip("the row count is 6 per CU on 256 compute units")
+    T = 6 * torch.cuda.get_device_properties(0).multi_processor_count
     for H, one in ((1544, True), (1536, False)):
-        d = workloads.fold_inputs(424 + H, 1536, H, 3)
+        d = workloads.fold_inputs(424 + H, T, H, 3)
         for fp8 in (False, True):
-            assert_fold_matches(orc, d, f"fold T=1536 H={H} P=3 fp8={fp8}", fp8=fp8)
+            assert_fold_matches(orc, d, f"fold T={T} H={H} P=3 fp8={fp8}", fp8=fp8)
             assert bnd.last_launch_shape()[3] is one
             if one:
                 assert bnd.last_launch_shape()[2] == 4
 
 
 def test_automatic_launch_shapes():
-    """The launch shapes the library picks on a 256-CU MI355X: one wavefront per row from 6 rows
-    per CU where a launch's rows fit on the chip in one round, or where its last round of
-    resident rows is full enough (3/4 for the reads, 1/3 for the completes)."""
-    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
-        pytest.skip("shape expectations are for 256 compute units")
+    """The launch shapes the library picks: one wavefront per row from 6 rows per CU where a
+    launch's rows fit on the chip in one round, or where its last round of resident rows is full
+    enough (3/4 for the reads, 1/3 for the completes). Row counts are written for the 256 CUs of
+    an MI355X and scaled to the device's CU count (c)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def c(n):
+        return n * cus // 256
     w = torch.ones(8192, device=DEV)
 
     def fold(T, H, P, fp8=False, kind="fold"):
@@ -1202,44 +1300,44 @@ def test_automatic_launch_shapes():
         torch.cuda.synchronize()
         return bnd.last_launch_shape()
 
-    assert fold(2048, 4096, 8) == (2048, 64, 8, True)                   # prefill boundary
-    assert fold(2048, 7168, 8, fp8=True) == (2048, 64, 14, True)        # quantised boundary
-    assert fold(2048, 4096, 8, kind="complete_only") == (2048, 64, 8, True)
-    assert fold(2048, 7168, 8, kind="snapshot") == (2048, 64, 14, True)
-    assert fold(1536, 4096, 8) == (1536, 64, 8, True)                   # 6 rows per CU
-    assert fold(2048, 2048, 8) == (2048, 64, 4, True)                   # other hidden sizes
-    assert fold(2048, 5120, 8) == (2048, 64, 10, True)
-    assert fold(2048, 6144, 8) == (2048, 64, 12, True)
-    assert fold(4096, 7168, 8) == (4096, 64, 14, True)                  # two whole rounds of 2048
-    assert fold(6144, 4096, 8) == (6144, 64, 8, True)                   # two whole rounds of 3072
-    assert fold(3072, 7168, 8)[3] is False                              # last round half full
-    assert fold(4096, 4096, 8)[3] is False                              # last round a third full
-    assert fold(6144, 4096, 8, kind="complete_only") == (6144, 64, 8, True)  # rounds of 4096, 1/2
-    assert fold(3584, 7168, 8, kind="complete_only")[3] is False        # rounds of 3072, 1/6
-    assert fold(4096, 1024, 8) == (4096, 64, 2, True)                   # width 2 from 12 rows per CU
-    assert fold(4096, 1024, 8, kind="complete_only") == (4096, 64, 2, True)
-    assert fold(2048, 1024, 8)[3] is False                              # width 2: too few rows
-    assert fold(4096, 768, 8)[3] is False                               # rows too short
-    assert fold(2048, 8192, 8)[3] is False                              # rows too long for a read
-    assert fold(2048, 8192, 8, kind="complete_only") == (2048, 64, 16, True)
-    assert fold(2048, 8192, 8, kind="snapshot") == (2048, 64, 16, True)
-    assert fold(1024, 4096, 8) == (1024, 64, 8, True)                   # 4 rows per CU: the deep ring
+    assert fold(c(2048), 4096, 8) == (c(2048), 64, 8, True)                   # prefill boundary
+    assert fold(c(2048), 7168, 8, fp8=True) == (c(2048), 64, 14, True)        # quantised boundary
+    assert fold(c(2048), 4096, 8, kind="complete_only") == (c(2048), 64, 8, True)
+    assert fold(c(2048), 7168, 8, kind="snapshot") == (c(2048), 64, 14, True)
+    assert fold(c(1536), 4096, 8) == (c(1536), 64, 8, True)                   # 6 rows per CU
+    assert fold(c(2048), 2048, 8) == (c(2048), 64, 4, True)                   # other hidden sizes
+    assert fold(c(2048), 5120, 8) == (c(2048), 64, 10, True)
+    assert fold(c(2048), 6144, 8) == (c(2048), 64, 12, True)
+    assert fold(c(4096), 7168, 8) == (c(4096), 64, 14, True)                  # two whole rounds of 2048
+    assert fold(c(6144), 4096, 8) == (c(6144), 64, 8, True)                   # two whole rounds of 3072
+    assert fold(c(3072), 7168, 8)[3] is False                              # last round half full
+    assert fold(c(4096), 4096, 8)[3] is False                              # last round a third full
+    assert fold(c(6144), 4096, 8, kind="complete_only") == (c(6144), 64, 8, True)  # rounds of 4096, 1/2
+    assert fold(c(3584), 7168, 8, kind="complete_only")[3] is False        # rounds of 3072, 1/6
+    assert fold(c(4096), 1024, 8) == (c(4096), 64, 2, True)                   # width 2 from 12 rows per CU
+    assert fold(c(4096), 1024, 8, kind="complete_only") == (c(4096), 64, 2, True)
+    assert fold(c(2048), 1024, 8)[3] is False                              # width 2: too few rows
+    assert fold(c(4096), 768, 8)[3] is False                               # rows too short
+    assert fold(c(2048), 8192, 8)[3] is False                              # rows too long for a read
+    assert fold(c(2048), 8192, 8, kind="complete_only") == (c(2048), 64, 16, True)
+    assert fold(c(2048), 8192, 8, kind="snapshot") == (c(2048), 64, 16, True)
+    assert fold(c(1024), 4096, 8) == (c(1024), 64, 8, True)                   # 4 rows per CU: the deep ring
     assert bnd.last_launch_ring_depth() == 8
-    assert fold(1536, 4096, 8, kind="complete_only") == (1536, 64, 8, True)
+    assert fold(c(1536), 4096, 8, kind="complete_only") == (c(1536), 64, 8, True)
     assert bnd.last_launch_ring_depth() == 8
-    assert fold(2048, 4096, 8) == (2048, 64, 8, True) and bnd.last_launch_ring_depth() == 2
-    assert fold(1023, 4096, 8)[3] is False                              # too few rows per CU
-    assert fold(1024, 2048, 8)[3] is False                              # widths 4, 6: from 6 rows per CU
-    assert fold(1536, 2048, 8) == (1536, 64, 4, True) and bnd.last_launch_ring_depth() == 4
-    assert fold(1792, 3072, 8, kind="complete_only") == (1792, 64, 6, True)
+    assert fold(c(2048), 4096, 8) == (c(2048), 64, 8, True) and bnd.last_launch_ring_depth() == 2
+    assert fold(c(1024) - 1, 4096, 8)[3] is False                              # too few rows per CU
+    assert fold(c(1024), 2048, 8)[3] is False                              # widths 4, 6: from 6 rows per CU
+    assert fold(c(1536), 2048, 8) == (c(1536), 64, 4, True) and bnd.last_launch_ring_depth() == 4
+    assert fold(c(1792), 3072, 8, kind="complete_only") == (c(1792), 64, 6, True)
     assert bnd.last_launch_ring_depth() == 6
-    assert fold(2048, 3072, 8) == (2048, 64, 6, True) and bnd.last_launch_ring_depth() == 2
+    assert fold(c(2048), 3072, 8) == (c(2048), 64, 6, True) and bnd.last_launch_ring_depth() == 2
     assert fold(128, 4096, 4)[3] is False                               # a decode boundary
-    d = workloads.moe_inputs(5, 2048, 4096, 16, 8)
+    d = workloads.moe_inputs(5, c(2048), 4096, 16, 8)
     E, idx, gate = _moe_device(d)
-    for rb, rows, shape in ((0, 2048, (2048, 64, 8, True)), (768, 256, (256, 512, 1, False))):
+    for rb, rows, shape in ((0, c(2048), (c(2048), 64, 8, True)), (c(768), c(256), (c(256), 512, 1, False))):
         res = torch.zeros(rows, 4096, dtype=torch.bfloat16, device=DEV)
-        s = bnd.bnd_stream_create(2048, 4096, res, rb, rows)
+        s = bnd.bnd_stream_create(c(2048), 4096, res, rb, rows)
         bnd.bnd_written(s, res)
         owed = bnd.bnd_publish_moe(s, E, idx, gate, 8)
         bnd.bnd_moe_finalize_fold_norm(s, owed, w[:4096], 1e-6, torch.empty(rows, 4096, dtype=torch.bfloat16,
@@ -1247,13 +1345,13 @@ def test_automatic_launch_shapes():
         torch.cuda.synchronize()
         assert bnd.last_launch_shape() == shape, (rb, rows)
     # the width of 2 is never taken for MoE picks
-    d = workloads.moe_inputs(6, 4096, 1024, 16, 8)
+    d = workloads.moe_inputs(6, c(4096), 1024, 16, 8)
     E, idx, gate = _moe_device(d)
-    res = torch.zeros(4096, 1024, dtype=torch.bfloat16, device=DEV)
-    s = bnd.bnd_stream_create(4096, 1024, res)
+    res = torch.zeros(c(4096), 1024, dtype=torch.bfloat16, device=DEV)
+    s = bnd.bnd_stream_create(c(4096), 1024, res)
     bnd.bnd_written(s, res)
     bnd.bnd_moe_finalize_fold_norm(s, bnd.bnd_publish_moe(s, E, idx, gate, 8), w[:1024], 1e-6,
-                                   torch.empty(4096, 1024, dtype=torch.bfloat16, device=DEV))
+                                   torch.empty(c(4096), 1024, dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
     assert bnd.last_launch_shape()[3] is False
     # MoE picks at 6 rows per CU and H = 2048 take the 4-wide deep ring
@@ -1265,7 +1363,7 @@ def test_automatic_launch_shapes():
     bnd.bnd_moe_finalize_fold_norm(s, bnd.bnd_publish_moe(s, E, idx, gate, 8), w[:2048], 1e-6,
                                    torch.empty(1536, 2048, dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
-    assert bnd.last_launch_shape() == (1536, 64, 4, True) and bnd.last_launch_ring_depth() == 4
+    assert bnd.last_launch_shape() == (c(1536), 64, 4, True) and bnd.last_launch_ring_depth() == 4
 
 
 @pytest.mark.parametrize("mode", [bnd.BND_ONE_WAVEFRONT_NEVER, bnd.BND_ONE_WAVEFRONT_ALWAYS],
