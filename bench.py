@@ -928,6 +928,16 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
                 "frac": nb / tr["kernel_s"] / 1e9 / PEAK_HBM_GBPS, "algorithmic_bytes": nb}
 
     leg(sec, "rsv_share_511_of_2047_H4096_P8", rsv, torch)
+    def tiny():
+        dt = workloads.tiny()
+        step, nb, keep = fold_case(torch, bnd, dt, 2)
+        tt = timer.run(step, 2, 20, 256)
+        return {"T": dt["T"], "H": dt["H"], "P": dt["P"], **kernel_fields(tt, bnd), "algorithmic_bytes": nb,
+                "us_per_call_back_to_back": back_to_back_us(torch, lambda i: step(i, None, None), 2),
+                "note": "launch-latency bound: 41,984 bytes per call"}
+
+    log("tiny fold (T=16 H=256 P=2)")
+    leg(sec, "tiny_T16_H256_P2", tiny, torch)
     log("decode chain (1 enter + 96 folds), eager and graph")
     leg(sec, "decode", lambda: [decode_chain(torch, bnd, workloads, T, 20, 50) for T in (1, 8, 32, 128)], torch)
     leg(sec, "launch_floor_empty_kernel", lambda: launch_floor(torch), torch)

@@ -327,26 +327,18 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
       if constexpr (kB < VPT) __builtin_amdgcn_sched_barrier(0);
     }
   } else if constexpr (S == Source::Moe) {
-    // The row's k indices and gates, wave-uniform scalar loads all issued before any is used. A
-    // dropped pick adds g * 0 with g = 0: nothing, whatever its gate holds (NaN or inf too). The
-    // empty asm takes each loaded gate as an operand, so the load is unconditional and the select
-    // below picks between registers (a select on a load would otherwise become a branch around
-    // the load, one memory round trip per pick).
+    // A dropped pick (index outside the expert rows) reads zeros through an empty resource and
+    // its product is not added, so it contributes nothing whatever its gate holds (NaN or inf
+    // too). The choice is made on the sum, not on the loaded gate: a select on a loaded value
+    // may be compiled as a branch around the load, one memory round trip per pick.
     int64_t er[N];
     float g[N];
-    int ev[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      ev[j] = a.idx[row * N + j];
+      const int64_t e = a.idx[row * N + j];
+      const bool valid = e >= 0 && e < a.n_expert_rows;
+      er[j] = valid ? e : -1;
       g[j] = a.gate[row * N + j];
-    }
-#pragma unroll
-    for (int j = 0; j < N; ++j) asm volatile("" : "+s"(g[j]));
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const bool valid = ev[j] >= 0 && ev[j] < a.n_expert_rows;
-      er[j] = valid ? ev[j] : -1;
-      g[j] = valid ? g[j] : 0.0f;
     }
     constexpr int kB = load_batch(N, VPT);
 #pragma unroll
@@ -355,7 +347,7 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
       uint4 r[kB];
 #pragma unroll
       for (int j = 0; j < N; ++j) {
-        // an invalid pick gets an empty resource: its loads return 0 and its gate is 0
+        // an invalid pick gets an empty resource: its loads return 0 and its product is dropped
         const Rsrc src = row_rsrc(a.experts + (er[j] < 0 ? 0 : er[j]) * a.ld_e, er[j] < 0 ? 0 : row_bytes);
 #pragma unroll
         for (int b = 0; b < kB; ++b) c[j][b] = load16(src, off[v0 + b]);
@@ -371,7 +363,7 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
         for (int j = 0; j < N; ++j) {
           bf16x8_to_f32(c[j][b], t);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[e] = fmaf(g[j], t[e], s[e]);
+          for (int e = 0; e < 8; ++e) s[e] = er[j] >= 0 ? fmaf(g[j], t[e], s[e]) : s[e];
         }
         bf16x8_to_f32(r[b], rv);
 #pragma unroll
