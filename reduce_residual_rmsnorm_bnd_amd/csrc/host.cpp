@@ -218,6 +218,11 @@ static_assert(bnd::kWaveWidths == 8 && bnd::wave_slot(16) == 7, "one rule per wi
 // multiples of 256, so every SIMD of the CU gets the same number of waves
 // (7- or 5-wave workgroups measured 3-6% slower).
 constexpr int kWaveSlotsPerCu = 32;
+// Reads with one vector per thread on fewer rows than CUs (decode boundaries)
+// take the kernels with non-temporal stores: 3% faster per boundary; launches
+// that give every CU a row or more keep sc1 stores (non-temporal: the 256-row
+// MoE share 3% and the 2048-row calls 3.6% slower). The completes always
+// store with sc1.
 constexpr int kOneVectorAlways = 256;
 constexpr int kOneVectorResident = 1024;
 constexpr int kTwoVectors = 2048;
@@ -380,6 +385,7 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
   l->vpt = vpt;
   l->one_wave = one_wave;
   l->deep = deep;
+  l->nt_stores = !one_wave && vpt == 1 && rows < cus;
   l->start = g_time_start;
   l->stop = g_time_stop;
   g_chosen = *l;

@@ -16,6 +16,10 @@ constexpr KernelFn kPlain[2][3][2] = {
     {{&read_kernel<Source::Residual, 0, 1, false>, &read_kernel<Source::Residual, 0, 1, true>},
      {&read_kernel<Source::Residual, 0, 2, false>, &read_kernel<Source::Residual, 0, 2, true>},
      {&read_kernel<Source::Residual, 0, 4, false>, &read_kernel<Source::Residual, 0, 4, true>}}};
+// one vector per thread with non-temporal stores (launches of fewer rows than CUs)
+constexpr KernelFn kPlainNt[2][2] = {
+    {&read_kernel<Source::Input, 0, 1, false, true>, &read_kernel<Source::Input, 0, 1, true, true>},
+    {&read_kernel<Source::Residual, 0, 1, false, true>, &read_kernel<Source::Residual, 0, 1, true, true>}};
 }  // namespace
 
 hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
@@ -29,7 +33,8 @@ hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Laun
     case Source::Input:
     case Source::Residual: {
       const int slot = vpt_slot(l.vpt);
-      if (slot < 0) return hipErrorInvalidValue;
+      if (slot < 0 || (l.nt_stores && l.vpt != 1)) return hipErrorInvalidValue;
+      if (l.nt_stores) return launch_kernel(kPlainNt[src == Source::Input ? 0 : 1][fp8 ? 1 : 0], a, l, stream);
       return launch_kernel(kPlain[src == Source::Input ? 0 : 1][slot][fp8 ? 1 : 0], a, l, stream);
     }
   }

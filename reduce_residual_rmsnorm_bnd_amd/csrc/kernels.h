@@ -49,7 +49,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // the one-wavefront read relies on the resource alone.
 // Cache policy: rows are read exactly once, so loads are non-temporal (nt);
 // stores carry sc1 (write-through past the XCD's L2). Both measured faster on
-// MI355X than the default policy for this 9:2 read:write stream.
+// MI355X than the default policy for this 9:2 read:write stream. The
+// multi-wave reads with one vector per thread are also built with
+// non-temporal stores, which the host takes for launches of fewer rows than
+// CUs (decode boundaries): 3% faster there, and 3-3.6% slower on launches of
+// one row per CU and more.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -58,6 +62,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor: 32-bit data format, raw addressing
 constexpr int kLoadOnce = 2;            // cache policy bits: nt
 constexpr int kStoreStream = 16;        // cache policy bits: sc1
+constexpr int kStoreOnce = 2;           // cache policy bits: nt
 
 __device__ __forceinline__ Rsrc row_rsrc(const void* row, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, bytes, kRsrcWord3);
@@ -68,14 +73,16 @@ __device__ __forceinline__ uint4 load16(Rsrc r, int byte_off) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+template <int kPolicy = kStoreStream>
 __device__ __forceinline__ void store16(Rsrc r, int byte_off, uint4 v) {
   const u32x4 u = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(u, r, byte_off, 0, kStoreStream);
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, byte_off, 0, kPolicy);
 }
 
+template <int kPolicy = kStoreStream>
 __device__ __forceinline__ void store8(Rsrc r, int byte_off, uint2 v) {
   const u32x2 u = {v.x, v.y};
-  __builtin_amdgcn_raw_buffer_store_b64(u, r, byte_off, 0, kStoreStream);
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, byte_off, 0, kPolicy);
 }
 
 __device__ __forceinline__ void bf16x8_to_f32(uint4 v, float f[8]) {
@@ -282,8 +289,9 @@ constexpr int load_batch(int n, int vpt) {
     if (4 * (n + 1) * kb + 16 * vpt + 12 <= 128) return kb;
   return 1;
 }
-// kFold = false computes the contribution s alone (complete_only).
-template <Source S, int N, int VPT, bool kFold = true>
+// kFold = false computes the contribution s alone (complete_only). kPolicy is
+// the cache policy of the enter's copy of the input into the residual.
+template <Source S, int N, int VPT, bool kFold = true, int kPolicy = kStoreStream>
 __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int tid, int nthr,
                                               const bool (&ok)[VPT], float (&x)[VPT][8]) {
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
@@ -379,7 +387,7 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
     for (int v = 0; v < VPT; ++v) {
       const uint4 raw = load16(src, off[v]);
       if constexpr (S == Source::Input) {
-        if (ok[v] && a.copy_input) store16(res, off[v], raw);
+        if (ok[v] && a.copy_input) store16<kPolicy>(res, off[v], raw);
       }
       bf16x8_to_f32(raw, x[v]);
     }
@@ -408,8 +416,10 @@ __device__ __forceinline__ void load_weight(const RowArgs& a, int tid, int nthr,
 // ---------------------------------------------------------------------------
 // The boundary read kernel: complete, fold, RMSNorm, stores.
 // ---------------------------------------------------------------------------
-template <Source S, int N, int VPT, bool FP8>
+// kNt: non-temporal stores (launches of fewer rows than CUs), else sc1.
+template <Source S, int N, int VPT, bool FP8, bool kNt = false>
 __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
+  constexpr int kPol = kNt ? kStoreOnce : kStoreStream;
   __shared__ float lds_q[kMaxThreads * VPT];  // the row's per-vector sums of squares, by vector
   __shared__ float lds_max[kMaxThreads / kWave];
   const int64_t row = blockIdx.x;
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
   for (int v = 0; v < VPT; ++v) ok[v] = (tid + v * nthr) < a.nvec;
 
   float x[VPT][8];
-  load_and_fold<S, N, VPT>(a, row, tid, nthr, ok, x);
+  load_and_fold<S, N, VPT, true, kPol>(a, row, tid, nthr, ok, x);
   // with four vectors per thread the weights wait until the loads are summed
   if constexpr (VPT >= 4) __builtin_amdgcn_sched_barrier(0);
   float w[VPT][8];
@@ -443,7 +453,7 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
     const Rsrc res = row_rsrc(a.res + row * a.ld_res, row_bytes);
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
-      if (ok[v]) store16(res, (tid + v * nthr) * 16, f32_to_bf16x8(x[v]));
+      if (ok[v]) store16<kPol>(res, (tid + v * nthr) * 16, f32_to_bf16x8(x[v]));
   }
 
   if constexpr (!FP8) {
@@ -453,7 +463,7 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = (x[v][e] * w[v][e]) * inv;  // the one-wavefront read's order
-      if (ok[v]) store16(yr, (tid + v * nthr) * 16, f32_to_bf16x8(y));
+      if (ok[v]) store16<kPol>(yr, (tid + v * nthr) * 16, f32_to_bf16x8(y));
     }
   } else {
     // y_h = (x_h w_h) inv. Rounding is monotone, so max_h |y_h| is exactly
@@ -469,7 +479,7 @@ __global__ __launch_bounds__(kMaxThreads) void read_kernel(const RowArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = (x[v][e] * w[v][e]) * inv;
         fp8_inputs<decltype(divide)::value>(y, scale, rcp, t);
-        if (ok[v]) store8(qr, (tid + v * nthr) * 8, f32_to_e4m3x8(t));
+        if (ok[v]) store8<kPol>(qr, (tid + v * nthr) * 8, f32_to_e4m3x8(t));
       }
     };
     if (fp8_divide(rcp))  // uniform across the row
@@ -811,9 +821,9 @@ __global__ __launch_bounds__(kWave) void wave_complete_kernel(const RowArgs a) {
 // ---------------------------------------------------------------------------
 using KernelFn = void (*)(RowArgs);
 
-template <Source S, int VPT, bool FP8, int... I>
+template <Source S, int VPT, bool FP8, bool kNt = false, int... I>
 constexpr std::array<KernelFn, sizeof...(I)> read_table(std::integer_sequence<int, I...>) {
-  return {{&read_kernel<S, I + 1, VPT, FP8>...}};
+  return {{&read_kernel<S, I + 1, VPT, FP8, kNt>...}};
 }
 
 template <Source S, int VPT, bool kFold, int... I>

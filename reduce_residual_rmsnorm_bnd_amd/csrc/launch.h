@@ -77,6 +77,7 @@ struct Launch {
   int vpt = 0;      // 16-byte vectors per thread: 1, 2 or 4; for one wavefront per row 2 .. 16, even
   bool one_wave = false;  // one wavefront per row (wave_read_kernel, wave_complete_kernel; threads = 64)
   bool deep = false;      // one wavefront per row with the deep ring (depth = vpt, 4 .. 8)
+  bool nt_stores = false;  // multi-wave reads, one vector per thread: the non-temporal-store kernels
   hipEvent_t start = nullptr;  // when set, recorded around the kernel itself (hipExtLaunchKernel)
   hipEvent_t stop = nullptr;
 };
