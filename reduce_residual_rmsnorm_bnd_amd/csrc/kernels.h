@@ -15,14 +15,15 @@
 //      resident buffers);
 //   2. fold: x = r + s in fp32 (guide, "Residual update and input read": the
 //      plain update is an add and the read keeps the fp32 sum);
-//   3. read: sum of squares over the row with a wave64 DPP reduction (and one
-//      LDS step across wavefronts when a row has several), inv =
-//      1/sqrt(ss/H + eps) (correctly rounded divide and square root),
-//      y = x * inv * w;
+//   3. read: sum of squares over the row in one order whatever the launch
+//      shape (per vector, then per lane in vector order, then a wave64 DPP
+//      sum; see row_reduce), inv = 1/sqrt(ss/H + eps) (correctly rounded
+//      divide and square root), y = (x * w) * inv;
 //   4. store the residual as bf16 (round to nearest even, v_cvt_pk_bf16_f32)
 //      and y as bf16, or as OCP e4m3 codes (v_cvt_pk_fp8_f32) with a
 //      per-row fp32 scale.
-// No atomics: the result is bitwise reproducible run to run.
+// No atomics: the result is bitwise reproducible run to run, and the same for
+// every launch shape.
 #pragma once
 
 #include <hip/hip_ext.h>
