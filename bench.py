@@ -117,13 +117,13 @@ def nearest_rank(sorted_values, q: float) -> float:
 
 def sampling_plan(steps: int):
     """The timed launches that record their own start/stop events: every `every`-th one from the
-    first, and the last, with `every` = steps // 2 clamped to 1..32, so that a run of any length
-    has both ends of its timed region on the device clock and at most about one launch in 32 (one
-    in ten for the shortest runs) pays for the event packets. Returns (every, the sampled step
-    indices, ascending)."""
+    first, and the last, with `every` = steps - 1 clamped to 1..32, so that a run of any length
+    has both ends of its timed region on the device clock, a short run (up to 33 steps) samples
+    only those two, and a long one one launch in 32 (the event packets add a few microseconds to
+    each sampled launch). Returns (every, the sampled step indices, ascending)."""
     if steps < 1:
         raise ValueError(f"need at least one timed step, not {steps}")
-    every = max(1, min(32, steps // 2))
+    every = max(1, min(32, steps - 1))
     sampled = list(range(0, steps, every))
     if sampled[-1] != steps - 1:
         sampled.append(steps - 1)

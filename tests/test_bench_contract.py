@@ -106,13 +106,15 @@ def test_timed_run_any_step_count(steps):
 def test_sampling_plan():
     assert bench.sampling_plan(1) == (1, [0])
     assert bench.sampling_plan(2) == (1, [0, 1])
-    assert bench.sampling_plan(20) == (10, [0, 10, 19])
+    assert bench.sampling_plan(20) == (19, [0, 19])
+    assert bench.sampling_plan(33) == (32, [0, 32])
     assert bench.sampling_plan(1024) == (32, list(range(0, 1024, 32)) + [1023])
     for steps in range(1, 300):
         every, sampled = bench.sampling_plan(steps)
         assert 1 <= every <= 32 and sampled[0] == 0 and sampled[-1] == steps - 1
         assert sampled == sorted(set(sampled))
         assert len(sampled) <= steps // every + 2
+        assert steps > 33 or len(sampled) == min(steps, 2)
     with pytest.raises(ValueError):
         bench.sampling_plan(0)
 
