@@ -67,7 +67,10 @@ extern "C" {
 
 #define BND_MAX_SOURCES 16        /* partials P and MoE picks k: 1..16 */
 #define BND_MAX_HIDDEN 32768      /* H: multiple of 8 in [8, 32768] */
-#define BND_MAX_ROWS 2147483647   /* T and expert rows: one launch grid, the int32 index range */
+#define BND_MAX_ROWS 2147483647   /* T and expert rows: one launch grid, the int32 index range. A call's
+                                   * launch also needs rows x threads per row <= 2^32 - 1 (a dispatch
+                                   * counts work-items in 32 bits): at H = 4096 at least 8,388,607
+                                   * rows fit; a call past its launch's limit returns NO_PATH. */
 #define BND_MAX_LD 2147483647     /* leading dimensions, in elements */
 
 /* Stream states, guide section "Residual stream" (state table). */

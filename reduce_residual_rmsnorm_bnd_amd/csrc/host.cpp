@@ -380,6 +380,10 @@ bnd_status choose_launch(int64_t H, int64_t rows, const WaveFit& wave, Launch* l
     return fail(BND_ERR_NO_PATH, "launch shape %d threads x %d vectors cannot cover H = %lld", threads,
                 vpt, (long long)H);
   if (rows > 0x7fffffff) return fail(BND_ERR_NO_PATH, "too many rows for one grid");
+  // a dispatch packet counts its grid in work-items, in 32 bits
+  if ((uint64_t)rows * (uint64_t)threads > 0xffffffffull)
+    return fail(BND_ERR_NO_PATH, "%lld rows of %d threads exceed one dispatch's 2^32 - 1 work-items", (long long)rows,
+                threads);
   l->rows = (int)rows;
   l->threads = threads;
   l->vpt = vpt;

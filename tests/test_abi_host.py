@@ -467,6 +467,24 @@ def test_size_limits_without_overflow():
     L.bnd_stream_destroy(h)
 
 
+def test_launch_past_the_dispatch_work_item_count_is_refused():
+    """A dispatch counts its grid in work-items with 32 bits: a call whose launch would need more
+    (here 2^31 - 1 rows of H = 4096) is refused before the launch and keeps its state."""
+    h = VP()
+    rows = 2**31 - 1
+    span = 1 << 45  # the operands' byte ranges (2^44 bytes each) do not overlap
+    assert L.bnd_stream_create(ctypes.byref(h), rows, H, 0, rows, fake(), H) == B.BND_OK
+    assert L.bnd_written(h, fake(), H) == B.BND_OK
+    o = owed_out()
+    arr = (VP * 2)(fake(span), fake(2 * span))
+    assert L.bnd_publish_partials(h, arr, 2, H, ctypes.byref(o)) == B.BND_OK
+    st = L.bnd_fold_norm(h, o, fake(7 * span), 1e-6, fake(3 * span), H, None)
+    assert st == B.BND_ERR_NO_PATH, L.bnd_last_error()
+    assert b"work-items" in L.bnd_last_error()
+    assert L.bnd_stream_state(h) == B.BND_PENDING
+    L.bnd_stream_destroy(h)
+
+
 def test_one_wavefront_modes():
     assert L.bnd_get_option(B.BND_OPT_ONE_WAVEFRONT) == B.BND_ONE_WAVEFRONT_AUTO
     for v in (B.BND_ONE_WAVEFRONT_ALWAYS, B.BND_ONE_WAVEFRONT_NEVER, B.BND_ONE_WAVEFRONT_AUTO):
