@@ -144,7 +144,7 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix(
       row_elems % 8 || ld < row_elems || ld % 8 || row_elems * 2 > 0x7fffffff)
     return -1;
   if (threads < 64 || threads > bnd::kMaxThreads || threads % 64 || (vpt != 1 && vpt != 2 && vpt != 4 && vpt != 8) ||
-      (int64_t)threads * vpt * 8 < row_elems)
+      (int64_t)threads * vpt * 8 < row_elems || rows * threads > 0xffffffffll)
     return -1;
   MixArgs a = {};
   for (int p = 0; p < n_src; ++p) {
@@ -178,7 +178,8 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix_9r2w(
 // argument (nothing launched), or the hipError_t of the launch.
 extern "C" __attribute__((visibility("default"))) int bnd_ceiling_empty(int64_t workgroups, int threads,
                                                                         hipStream_t stream) {
-  if (workgroups < 1 || workgroups > 0x7fffffff || threads < 64 || threads > bnd::kMaxThreads || threads % 64)
+  if (workgroups < 1 || workgroups > 0x7fffffff || threads < 64 || threads > bnd::kMaxThreads || threads % 64 ||
+      workgroups * threads > 0xffffffffll)
     return -1;
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&empty_kernel), dim3((unsigned)workgroups),
                               dim3((unsigned)threads), nullptr, 0, stream);
@@ -188,7 +189,8 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_empty(int64_t 
 // (sizeof(bnd::RowArgs) bytes of kernel arguments).
 extern "C" __attribute__((visibility("default"))) int bnd_ceiling_empty_args(int64_t workgroups, int threads,
                                                                              hipStream_t stream) {
-  if (workgroups < 1 || workgroups > 0x7fffffff || threads < 64 || threads > bnd::kMaxThreads || threads % 64)
+  if (workgroups < 1 || workgroups > 0x7fffffff || threads < 64 || threads > bnd::kMaxThreads || threads % 64 ||
+      workgroups * threads > 0xffffffffll)
     return -1;
   bnd::RowArgs a;
   memset(&a, 0, sizeof a);
@@ -215,7 +217,7 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_gather_9r2w(
       row_elems < 8 || row_elems % 8 || ld < row_elems || ld % 8 || row_elems * 2 > 0x7fffffff)
     return -1;
   if (threads < 64 || threads > bnd::kMaxThreads || threads % 64 || (vpt != 1 && vpt != 2 && vpt != 4 && vpt != 8) ||
-      (int64_t)threads * vpt * 8 < row_elems)
+      (int64_t)threads * vpt * 8 < row_elems || rows * threads > 0xffffffffll)
     return -1;
   if (!aligned16(rows_src) || !aligned16(src8) || !aligned16(out0) || !aligned16(out1) ||
       (reinterpret_cast<uintptr_t>(idx) & 3))

@@ -60,7 +60,7 @@ def test_ceiling_refuses_bad_shapes():
     for n in (0, 17):  # source counts outside 1..16
         assert L.bnd_ceiling_mix(src16, n, o0, None, 4, 4096, 4096, 512, 1, None) == -1, n
     assert L.bnd_ceiling_mix_9r2w(src, o0, None, 4, 4096, 4096, 512, 1, None) == -1  # 9:2 needs two outputs
-    for wg, threads in ((0, 64), (1, 32), (1, 100), (1, 2048), (1 << 31, 64)):
+    for wg, threads in ((0, 64), (1, 32), (1, 100), (1, 2048), (1 << 31, 64), (1 << 26, 128)):
         assert L.bnd_ceiling_empty(wg, threads, None) == -1, (wg, threads)
         assert L.bnd_ceiling_empty_args(wg, threads, None) == -1, (wg, threads)
     E, idx, s8 = VP(a), VP(a + (30 << 24)), VP(a + (31 << 24))
