@@ -35,7 +35,8 @@
  *   - `hip_stream` is a hipStream_t (NULL = the null stream). Kernels run
  *     asynchronously on it; inputs must stay alive and unmodified until the
  *     consuming kernel has completed in stream order.
- *   - Outputs must not overlap the residual or any input.
+ *   - Outputs must not overlap the residual or any input (the norm weight
+ *     included), and a residual the call writes must not overlap the weight.
  *   - Errors: every check happens on the host before any launch. On an error
  *     nothing is launched, no output byte changes and the stream's state is
  *     unchanged (a fusion candidate must refuse before touching its inputs,

@@ -695,6 +695,9 @@ bnd_status bnd_enter_norm(bnd_stream* s, const void* x, int64_t ld_x, const floa
   Range in[2] = {rows_range(s->residual, s->rows, s->ld_res, s->H, 2),
                  entering ? rows_range(x, s->rows, ld_x, s->H, 2) : Range{}};
   if (overlap(yr, in[0]) || overlap(yr, in[1])) return fail(BND_ERR_INVALID_ARG, "y overlaps the residual or x");
+  const Range wr = rows_range(w, 1, s->H, s->H, 4);
+  if (overlap(yr, wr) || (entering && !alias && overlap(in[0], wr)))
+    return fail(BND_ERR_INVALID_ARG, "the weight overlaps y or the residual the call writes");
   if (entering && !alias && overlap(in[0], in[1]))
     return fail(BND_ERR_INVALID_ARG, "x partly overlaps the residual storage");
   if (any) {
@@ -745,6 +748,11 @@ static bnd_status fold_read(bnd_stream* s, bnd_owed owed, bnd_kind kind, bool fp
   }
   for (int i = 0; i < n_out; ++i)
     if ((st = check_output_disjoint(s, fp8 ? (i ? "scale" : "q") : "y", outs[i], true))) return st;
+  const Range wr = rows_range(w, 1, s->H, s->H, 4);
+  for (int i = 0; i < n_out; ++i)
+    if (overlap(outs[i], wr)) return fail(BND_ERR_INVALID_ARG, "%s overlaps the weight", fp8 ? (i ? "scale" : "q") : "y");
+  if (fold && overlap(rows_range(s->residual, s->rows, s->ld_res, s->H, 2), wr))
+    return fail(BND_ERR_INVALID_ARG, "the residual (written by the fold) overlaps the weight");
   if (any) {
     // a fold reads the owed partials or picks; a Written stream's read, the stored residual
     const Source src = !fold ? Source::Residual : kind == BND_KIND_MOE ? Source::Moe : Source::Partials;

@@ -256,6 +256,10 @@ def test_fold_validation_refuses_before_launch():
         (L.bnd_fold_norm_quant_fp8, (h, o, w, 1e-6, fake((1 << 30) + 4), H, fake(1 << 29), None)),
         (L.bnd_fold_norm_quant_fp8, (h, o, w, 1e-6, y, H + 4, fake(1 << 29), None)),
         (L.bnd_fold_norm_quant_fp8, (h, o, w, 1e-6, y, H, y, None)),       # q overlaps scale
+        (L.bnd_fold_norm, (h, o, w, 1e-6, fake((1 << 31) + 4096), H, None)),  # y overlaps the weight
+        (L.bnd_fold_norm, (h, o, fake(8192), 1e-6, y, H, None)),           # the fold writes over the weight
+        (L.bnd_fold_norm_quant_fp8, (h, o, w, 1e-6, fake(1 << 31), H, fake(1 << 29), None)),  # q is the weight
+        (L.bnd_fold_norm_quant_fp8, (h, o, w, 1e-6, y, H, fake((1 << 31) + 64), None)),  # scale in the weight
     ]
     for fn, args in cases:
         st = fn(*args)
@@ -406,6 +410,9 @@ def test_enter_validation():
     # y overlapping x
     assert L.bnd_enter_norm(h, fake(1 << 28), H, w, 1e-6, fake(1 << 28), H, None) == B.BND_ERR_INVALID_ARG
     assert L.bnd_enter_norm(h, None, H, w, 1e-6, fake(1 << 30), H, None) == B.BND_ERR_INVALID_ARG
+    # y overlapping the weight, and an entering copy that would write over the weight
+    assert L.bnd_enter_norm(h, fake(1 << 28), H, w, 1e-6, fake((1 << 31) - 64), H, None) == B.BND_ERR_INVALID_ARG
+    assert L.bnd_enter_norm(h, fake(1 << 28), H, fake(4096), 1e-6, fake(1 << 30), H, None) == B.BND_ERR_INVALID_ARG
     assert L.bnd_stream_state(h) == B.BND_INITIAL
 
 
