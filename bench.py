@@ -549,7 +549,11 @@ def stream_ceiling(torch, T: int, H: int, n_src: int, n_out: int, kernel_us: dic
                      vp(bufs[n_src + 1].data_ptr()) if n_out == 2 else vp()))
     stream = vp(torch.cuda.current_stream().cuda_stream)
     shapes = {}
-    for threads, vpt in ((256, 2), (512, 1), (128, 4), (64, 8)):
+    # every shape of one row per workgroup whose threads x vectors cover the row once (not twice)
+    cover = [(t, v) for t in (64, 128, 256, 512, 1024) for v in (1, 2, 4, 8) if H <= t * v * 8 < 2 * H]
+    if not cover:
+        raise ValueError(f"no one-row-per-workgroup shape of the streaming kernel covers H = {H}")
+    for threads, vpt in cover:
         def launch(i, threads=threads, vpt=vpt):
             _, src, o0, o1 = sets[i]
             rc = L.bnd_ceiling_mix(src, n_src, o0, o1, T, H, H, threads, vpt, stream)
@@ -848,17 +852,27 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
     leg(sec, "stream_ceiling_9r2w_T2048_H4096",
         lambda: stream_ceiling(torch, d["T"], d["H"], 9, 2, {"fold": fold_us}), torch)
 
+    fp8_us = {}
+
     def fp8():
         log("quantised read (T=2048 H=7168 P=8, fp8 out)")
         dq = workloads.quantised()
         n_q = max(2, -(-ROTATE_BYTES // ((dq["P"] + 2) * dq["T"] * dq["H"] * 2 + dq["T"] * dq["H"])))
         step, nb, keep = fold_case(torch, bnd, dq, n_q, fp8=True)
         tq = timer.run(step, n_q, 20, 256)
+        fp8_us["fp8"] = back_to_back_us(torch, lambda i: step(i, None, None), n_q)
         return {"tokens_per_s_kernel": 2048 / tq["kernel_s"], **kernel_fields(tq, bnd),
                 "GBps": nb / tq["kernel_s"] / 1e9, "frac": nb / tq["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
-                "algorithmic_bytes": nb}
+                "algorithmic_bytes": nb, "back_to_back_us": fp8_us["fp8"]}
 
     leg(sec, "fp8_T2048_H7168_P8", fp8, torch)
+    # the fp8 read writes a bf16 residual row and a row of one-byte codes: between the 9:1 and 9:2
+    # streams at its width
+    log("9:1 and 9:2 streaming ceilings at H = 7168 (the quantised read's width)")
+    leg(sec, "stream_ceiling_9r1w_T2048_H7168",
+        lambda: stream_ceiling(torch, 2048, 7168, 9, 1, {"fp8": fp8_us.get("fp8")}), torch)
+    leg(sec, "stream_ceiling_9r2w_T2048_H7168",
+        lambda: stream_ceiling(torch, 2048, 7168, 9, 2, {"fp8": fp8_us.get("fp8")}), torch)
 
     log("MoE finalize (T=2048 H=4096 k=8), full rows and rows 768..1023")
     dm = workloads.moe()
