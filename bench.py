@@ -891,8 +891,7 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
             out["back_to_back_us"] = moe_us[rows]
         return out
 
-    # the full-row calls first: after the share's 47 rotation sets (6 GB allocated and freed) a
-    # 2048-row MoE finalize measures about 4% slower whatever its form (allocation history)
+    # the full-row calls first, then the share with its 47 rotation sets
     leg(sec, "moe_full_T2048_H4096_k8", lambda: moe(0, 2048, False, True), torch)
     leg(sec, "moe_terminal_gemma_T2048_H4096_k8", lambda: moe(0, 2048, True, False), torch)
     leg(sec, "moe_slice_rows768_1023", lambda: moe(*workloads.MOE_SLICE, False, True), torch)
