@@ -145,6 +145,77 @@ def test_transition(call, start):
     L.bnd_stream_destroy(h)
 
 
+def _call_owed(h, call, owed):
+    """_call, returning (status, the new owed handle of a call that publishes or completes)."""
+    o = owed_out()
+    if call == "complete_only":
+        return L.bnd_complete_only(h, owed or 0, None, H, ctypes.byref(o), None), o.value
+    if call == "add_to_output":
+        return L.bnd_add_to_output(h, owed or 0, None, H, None, H, ctypes.byref(o), None), o.value
+    if call == "publish_partials":
+        return L.bnd_publish_partials(h, (VP * 1)(None), 1, H, ctypes.byref(o)), o.value
+    if call == "publish_moe":
+        return L.bnd_publish_moe(h, None, 0, H, None, None, 4, ctypes.byref(o)), o.value
+    return _call(h, call, owed), None
+
+
+def test_random_call_sequences_follow_the_state_table():
+    """Seeded random walks of every call over two empty-slice streams, against a model built from
+    the state table alone: status and state after each call, the pending kind, a refused call
+    changing nothing, and handles that are stale or belong to the other stream being refused."""
+    import random
+
+    rng = random.Random(2024)
+    calls = sorted(TABLE["table"])
+    kind_of = {"PENDING_PARTIALS": B.BND_KIND_PARTIALS, "PENDING_MOE": B.BND_KIND_MOE}
+    checked = 0
+    for walk in range(200):
+        hs = [create(), create()]
+        model = ["INITIAL", "INITIAL"]
+        owed = [None, None]
+        stale = [[], []]
+        for _ in range(30):
+            i = rng.randrange(2)
+            h, st_model = hs[i], model[i]
+            call = rng.choice(calls)
+            handle = owed[i]
+            forged = None
+            if call in ("fold_norm", "fold_norm_quant_fp8", "moe_finalize_fold_norm", "complete_only",
+                        "add_to_output", "snapshot") and rng.random() < 0.2:
+                pool = stale[i] + ([owed[1 - i]] if owed[1 - i] else [])
+                if st_model.startswith("PENDING") and pool:
+                    forged = rng.choice(pool)
+                elif st_model == "WRITTEN" and pool and call != "snapshot":
+                    forged = rng.choice(pool)
+            status, new = _call_owed(h, call, forged if forged is not None else handle)
+            want_status, want_state = TABLE["table"][call][st_model]
+            if forged is not None and want_status == "OK":
+                want_status, want_state = "FOREIGN_OUTPUT", st_model
+            assert status == STATUS[want_status], (walk, call, st_model, forged, L.bnd_last_error())
+            if want_state == "PENDING":
+                if status != B.BND_OK:
+                    want_state = st_model
+                elif call == "publish_moe":
+                    want_state = "PENDING_MOE"
+                elif call == "snapshot":
+                    want_state = st_model
+                else:  # publish_partials, or a complete that leaves one plain partial owed
+                    want_state = "PENDING_PARTIALS"
+            assert L.bnd_stream_state(h) == STATE[want_state.split("_")[0]], (walk, call, st_model)
+            if want_state.startswith("PENDING"):
+                assert L.bnd_stream_pending_kind(h) == kind_of[want_state]
+            if status == B.BND_OK and want_state != st_model or new:
+                if owed[i]:
+                    stale[i].append(owed[i])
+                owed[i] = new if new else (owed[i] if want_state.startswith("PENDING") and
+                                           call == "snapshot" else None)
+            model[i] = want_state
+            checked += 1
+        for h in hs:
+            L.bnd_stream_destroy(h)
+    assert checked == 200 * 30
+
+
 def test_pending_without_residual_then_fold_writes_it():
     h = create()
     o = owed_out()
