@@ -53,6 +53,11 @@ MUTANTS = {
                             "double v = y[h] / (double)scale;\n    if (v > 448.0) v = 448.0;\n"
                             "    if (v < -448.0) v = -448.0;"),
     "moe_index_ignored": ("int64_t e = idx[t * k + j];", "int64_t e = t * k + j;"),
+    "invalid_pick_clamped": ("if (e < 0 || e >= n_rows) continue;", "if (e < 0 || e >= n_rows) e = 0;"),
+    "partials_slice_relative": ("complete_partials_row(H, P, partials, ld_p, row_begin + i, b.s, b.mag);\n    apply_update_row",
+                                "complete_partials_row(H, P, partials, ld_p, i, b.s, b.mag);\n    apply_update_row"),
+    "moe_slice_relative": ("complete_moe_row(H, k, E, ld_e, n_rows_e, idx, gate, row_begin + i, b.s, b.mag);\n    apply_update_row",
+                           "complete_moe_row(H, k, E, ld_e, n_rows_e, idx, gate, i, b.s, b.mag);\n    apply_update_row"),
     "extra_dropped": ("if (extra) add_extra_row(H, extra + (row_begin + i) * ld_x, b.s, b.mag);",
                       "(void)extra;"),
     "extra_not_global_row": ("if (extra) add_extra_row(H, extra + (row_begin + i) * ld_x, b.s, b.mag);",
