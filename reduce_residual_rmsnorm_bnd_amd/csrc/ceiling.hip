@@ -103,6 +103,14 @@ __global__ __launch_bounds__(bnd::kMaxThreads) void gather_kernel(const GatherAr
       const uint4 t = bnd::load16(r, off[v]);
       acc[v].x ^= t.x; acc[v].y ^= t.y; acc[v].z ^= t.z; acc[v].w ^= t.w;
     }
+    // With eight vectors per thread a row's 72 loads (288 VGPRs) cannot all be in flight within
+    // the 128 VGPRs of a 1024-thread workgroup: one source's loads at a time, as in mix_kernel,
+    // instead of a spill to scratch.
+    if constexpr (VPT >= 8) {
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) asm volatile("" : "+v"(acc[v].x), "+v"(acc[v].y), "+v"(acc[v].z), "+v"(acc[v].w));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   const bnd::Rsrc o0 = bnd::row_rsrc(a.out0 + row * a.ld, a.row_bytes);
   const bnd::Rsrc o1 = bnd::row_rsrc(a.out1 + row * a.ld, a.row_bytes);

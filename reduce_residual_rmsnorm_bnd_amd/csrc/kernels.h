@@ -281,13 +281,26 @@ __device__ __forceinline__ void resolve_pick(const RowArgs& a, const RowPicks& p
 // row addresses beyond its row resource and reads 0, which keeps the loads
 // branch-free so they can all be in flight together.
 //
+// Keeps a step's arithmetic at its place in the pipeline: the empty asm reads
+// and writes the eight sums, so they are computed before it, and the
+// scheduling fence after it keeps later loads behind it. (A fence alone does
+// not stop the compiler from sinking the adds towards their later uses.)
+__device__ __forceinline__ void pin8(float (&x)[8]) {
+  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
+}
+
 // Vectors whose source loads are in flight together. A batch of kb vectors
 // holds 4*(N+1)*kb VGPRs of raw loads next to the row's fp32 values and
-// weights (16*VPT); the largest kb <= VPT that keeps the estimate within the
-// 128 VGPRs of a 1024-thread workgroup avoids scratch spills.
-constexpr int load_batch(int n, int vpt) {
+// weights (16*VPT) and `per_source` more for each source's bookkeeping (two
+// for a MoE pick); the largest kb <= VPT that keeps the estimate within the
+// 128 VGPRs of a 1024-thread workgroup avoids scratch spills. Each finished
+// batch's sums are pinned in place before the next batch's loads: otherwise
+// the compiler sinks them towards the stores and every batch's raw loads stay
+// live together (a 16-source snapshot with four vectors per thread spilled
+// 636 bytes per lane that way).
+constexpr int load_batch(int n, int vpt, int per_source = 0) {
   for (int kb = vpt; kb > 1; kb /= 2)
-    if (4 * (n + 1) * kb + 16 * vpt + 12 <= 128) return kb;
+    if (4 * (n + 1) * kb + 16 * vpt + 12 + per_source * n <= 128) return kb;
   return 1;
 }
 // kFold = false computes the contribution s alone (complete_only). kPolicy is
@@ -331,6 +344,7 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
         bf16x8_to_f32(r[b], rv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[v0 + b][e] = rv[e] + s[e];
+        if constexpr (kB < VPT) pin8(x[v0 + b]);
       }
       // keep the next batch's loads behind this batch's sums (register budget)
       if constexpr (kB < VPT) __builtin_amdgcn_sched_barrier(0);
@@ -349,7 +363,7 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
       er[j] = valid ? e : -1;
       g[j] = a.gate[row * N + j];
     }
-    constexpr int kB = load_batch(N, VPT);
+    constexpr int kB = load_batch(N, VPT, 2);
 #pragma unroll
     for (int v0 = 0; v0 < VPT; v0 += kB) {
       uint4 c[N][kB];
@@ -377,6 +391,7 @@ __device__ __forceinline__ void load_and_fold(const RowArgs& a, int64_t row, int
         bf16x8_to_f32(r[b], rv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[v0 + b][e] = rv[e] + s[e];
+        if constexpr (kB < VPT) pin8(x[v0 + b]);
       }
       // keep the next batch's loads behind this batch's sums (register budget)
       if constexpr (kB < VPT) __builtin_amdgcn_sched_barrier(0);
@@ -588,14 +603,6 @@ __device__ __forceinline__ RowSource row_source(const RowArgs& a, const RowPicks
     resolve_pick(a, picks, p, e, g);
     return {row_rsrc(a.experts + (e < 0 ? 0 : e) * a.ld_e, e < 0 ? 0 : rb), g};
   }
-}
-
-// Keeps a step's arithmetic at its place in the pipeline: the empty asm reads
-// and writes the eight sums, so they are computed before it, and the
-// scheduling fence after it keeps later loads behind it. (A fence alone does
-// not stop the compiler from sinking the adds towards their later uses.)
-__device__ __forceinline__ void pin8(float (&x)[8]) {
-  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
 }
 
 __device__ __forceinline__ void load_weight8(const Rsrc& wr, int vec, u32x4& lo, u32x4& hi) {

@@ -1179,6 +1179,39 @@ def test_wave_complete(orc, kind, vpt, T, H, P, rb, rows):
     assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16)), f"{what}: differs from the other shape"
 
 
+@pytest.mark.parametrize("P", [8, 16])
+def test_multi_wave_completes_every_shape(orc, P):
+    """complete_only, add_to_output, snapshot and the MoE complete under every multi-wave shape that
+    covers the row, four vectors per thread included (where the many-source snapshot kernels once
+    spilled to scratch): each against the oracle, and bitwise equal to the automatic shape."""
+    T, H = 37, 4096
+    d = workloads.fold_inputs(900 + P, T, H, P)
+    dm = workloads.moe_inputs(910 + P, T, H, P, P)
+    extra = workloads.to_bf16(workloads.normal_f32(920 + P, 12345, (T, H), 0.0, 0.25))
+    kinds = {"complete_only": (d, False, None), "add_to_output": (d, False, extra), "snapshot": (d, False, None),
+             "moe complete_only": (dm, True, None)}
+    exact = {}
+    for kind, (inp, moe, ex) in kinds.items():
+        exact[kind] = _oracle_complete(orc, inp, kind.split()[-1], extra=ex, moe=moe)
+    shapes = [("auto", None)] + [(f"{t}x{v}", (t, v)) for t, v in MULTI_WAVE_SHAPES if t * v >= H // 8]
+    base = {}
+    for label, shape in shapes:
+        for kind, (inp, moe, ex) in kinds.items():
+            if shape is None:
+                out = _complete(inp, kind.split()[-1], extra=ex, moe=moe)
+            else:
+                with forced_shape(*shape):
+                    out = _complete(inp, kind.split()[-1], extra=ex, moe=moe)
+                assert bnd.last_launch_shape()[1:] == (shape[0], shape[1], False)
+            what = f"{kind} P/k={P} under {label}"
+            tolerance.check_bf16(bits(out.view), *exact[kind], what)
+            if kind not in base:
+                base[kind] = out.view.clone()
+            else:
+                assert torch.equal(out.view, base[kind]), f"{what} differs from the automatic shape"
+    print(f"\n  P/k={P}: {len(kinds)} calls under {len(shapes)} shapes", flush=True)
+
+
 @pytest.mark.parametrize("vpt,H", WAVE_COMPLETE_WIDTHS, ids=lambda v: str(v))
 def test_wave_complete_moe(orc, vpt, H):
     d = workloads.moe_inputs(410, 40, H, 16, 8)
