@@ -932,6 +932,8 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
 
     leg(sec, "unfused_fallback_T2048_H4096_P8", unfused, torch)
 
+    rsv_share = {}
+
     def rsv():
         counts = [300, 0, 511, 256, 257, 1, 400, 322]
         rb, rows, Tr = bnd.bnd_rsv_share(counts, 2)
@@ -939,10 +941,17 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
         n_r = max(2, -(-ROTATE_BYTES // (rows * 11 * 4096 * 2)))
         step, nb, keep = fold_case(torch, bnd, dr, n_r, row_begin=rb, rows=rows)
         tr = timer.run(step, n_r, 20, 256)
-        return {"row_begin": rb, "rows": rows, **kernel_fields(tr, bnd), "GBps": nb / tr["kernel_s"] / 1e9,
-                "frac": nb / tr["kernel_s"] / 1e9 / PEAK_HBM_GBPS, "algorithmic_bytes": nb}
+        fields = kernel_fields(tr, bnd)
+        rsv_share.update(rows=rows, us=back_to_back_us(torch, lambda i: step(i, None, None), n_r))
+        return {"row_begin": rb, "rows": rows, **fields, "GBps": nb / tr["kernel_s"] / 1e9,
+                "frac": nb / tr["kernel_s"] / 1e9 / PEAK_HBM_GBPS, "algorithmic_bytes": nb,
+                "back_to_back_us": rsv_share["us"]}
 
     leg(sec, "rsv_share_511_of_2047_H4096_P8", rsv, torch)
+    # the same 9:2 stream over as many rows as the share: two rows per CU, one launch's ramp and drain
+    leg(sec, "stream_ceiling_9r2w_T511_H4096",
+        lambda: stream_ceiling(torch, rsv_share.get("rows", 511), 4096, 9, 2, {"rsv_share": rsv_share.get("us")}),
+        torch)
     def tiny():
         dt = workloads.tiny()
         step, nb, keep = fold_case(torch, bnd, dt, 2)
