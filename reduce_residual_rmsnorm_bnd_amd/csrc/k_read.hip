@@ -8,18 +8,18 @@ hipError_t launch_read_partials(int n, bool fp8, const RowArgs& a, const Launch&
 hipError_t launch_read_moe(int n, const RowArgs& a, const Launch& l, hipStream_t stream);
 
 namespace {
-// [source: input, residual][vpt slot][bf16, fp8]
-constexpr KernelFn kPlain[2][3][2] = {
-    {{&read_kernel<Source::Input, 0, 1, false>, &read_kernel<Source::Input, 0, 1, true>},
-     {&read_kernel<Source::Input, 0, 2, false>, &read_kernel<Source::Input, 0, 2, true>},
-     {&read_kernel<Source::Input, 0, 4, false>, &read_kernel<Source::Input, 0, 4, true>}},
-    {{&read_kernel<Source::Residual, 0, 1, false>, &read_kernel<Source::Residual, 0, 1, true>},
-     {&read_kernel<Source::Residual, 0, 2, false>, &read_kernel<Source::Residual, 0, 2, true>},
-     {&read_kernel<Source::Residual, 0, 4, false>, &read_kernel<Source::Residual, 0, 4, true>}}};
+// enter (bf16 output only: the stack input's read has no fp8 form), by vpt slot
+constexpr KernelFn kInput[3] = {&read_kernel<Source::Input, 0, 1, false>, &read_kernel<Source::Input, 0, 2, false>,
+                                &read_kernel<Source::Input, 0, 4, false>};
+// the read of a Written stream: [vpt slot][bf16, fp8]
+constexpr KernelFn kResidual[3][2] = {
+    {&read_kernel<Source::Residual, 0, 1, false>, &read_kernel<Source::Residual, 0, 1, true>},
+    {&read_kernel<Source::Residual, 0, 2, false>, &read_kernel<Source::Residual, 0, 2, true>},
+    {&read_kernel<Source::Residual, 0, 4, false>, &read_kernel<Source::Residual, 0, 4, true>}};
 // one vector per thread with non-temporal stores (launches of fewer rows than CUs)
-constexpr KernelFn kPlainNt[2][2] = {
-    {&read_kernel<Source::Input, 0, 1, false, true>, &read_kernel<Source::Input, 0, 1, true, true>},
-    {&read_kernel<Source::Residual, 0, 1, false, true>, &read_kernel<Source::Residual, 0, 1, true, true>}};
+constexpr KernelFn kInputNt = &read_kernel<Source::Input, 0, 1, false, true>;
+constexpr KernelFn kResidualNt[2] = {&read_kernel<Source::Residual, 0, 1, false, true>,
+                                     &read_kernel<Source::Residual, 0, 1, true, true>};
 }  // namespace
 
 hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Launch& l, hipStream_t stream) {
@@ -30,12 +30,15 @@ hipError_t launch_read(Source src, int n, bool fp8, const RowArgs& a, const Laun
     case Source::Moe:
       if (fp8) return hipErrorInvalidValue;
       return launch_read_moe(n, a, l, stream);
-    case Source::Input:
+    case Source::Input: {
+      const int slot = vpt_slot(l.vpt);
+      if (fp8 || slot < 0 || (l.nt_stores && l.vpt != 1)) return hipErrorInvalidValue;
+      return launch_kernel(l.nt_stores ? kInputNt : kInput[slot], a, l, stream);
+    }
     case Source::Residual: {
       const int slot = vpt_slot(l.vpt);
       if (slot < 0 || (l.nt_stores && l.vpt != 1)) return hipErrorInvalidValue;
-      if (l.nt_stores) return launch_kernel(kPlainNt[src == Source::Input ? 0 : 1][fp8 ? 1 : 0], a, l, stream);
-      return launch_kernel(kPlain[src == Source::Input ? 0 : 1][slot][fp8 ? 1 : 0], a, l, stream);
+      return launch_kernel(l.nt_stores ? kResidualNt[fp8 ? 1 : 0] : kResidual[slot][fp8 ? 1 : 0], a, l, stream);
     }
   }
   return hipErrorInvalidValue;

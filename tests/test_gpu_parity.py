@@ -505,17 +505,30 @@ def test_every_launch_shape_gives_the_same_bits(orc, H):
         if kind == "moe":
             res, y = _moe_only(dm, 0, T)
             return res.view, y.view
-        # enter, then the read of the Written stream it leaves
-        res, y, y2 = Guarded(T, H), Guarded(T, H), Guarded(T, H)
+        # enter, then the reads of the Written stream it leaves, bf16 and fp8
+        res, y, y2, q = Guarded(T, H), Guarded(T, H), Guarded(T, H), Guarded(T, H, torch.uint8)
+        sc = torch.full((T,), -1.0, dtype=torch.float32, device=DEV)
         st = bnd.bnd_stream_create(T, H, res.view)
         bnd.bnd_enter_norm(st, d["residual"].to(DEV), d["weight"].to(DEV), d["eps"], y.view)
         bnd.bnd_fold_norm(st, bnd.BND_OWED_NONE, d["weight"].to(DEV), d["eps"], y2.view)
+        bnd.bnd_fold_norm_quant_fp8(st, bnd.BND_OWED_NONE, d["weight"].to(DEV), d["eps"], q.view, sc)
         torch.cuda.synchronize()
-        return res.view, y.view, y2.view
+        q.check_guards("written fp8 read")
+        return res.view, y.view, y2.view, q.view, sc
 
     assert_fold_matches(orc, d, f"H={H} automatic shape")
     assert_fold_matches(orc, d, f"H={H} automatic shape fp8", fp8=True)
     run_moe(orc, dm, 0, T, f"MoE H={H} automatic shape")
+    # enter and the Written reads at the automatic shape against the oracle
+    res, y, y2, q, sc = call("enter")
+    w = d["weight"].numpy()
+    ref = orc.enter_norm(bits(d["residual"]), w, d["eps"])
+    assert np.array_equal(bits(res), ref["residual"]), "enter must copy x into the residual"
+    tolerance.check_bf16(bits(y), ref["y_exact"], np.zeros((T, H)), f"H={H} enter y")
+    assert torch.equal(y2, y), "the Written read is the enter's read"
+    rq = orc.fold_norm([np.zeros((T, H), np.uint16)], ref["residual"], w, d["eps"], fp8=True)
+    tolerance.check_fp8(q.cpu().numpy(), rq["q"], f"H={H} written fp8 q")
+    tolerance.check_scale(sc.cpu().numpy(), rq["scale"], f"H={H} written fp8 scale")
     base = {}
     checked = 0
     for label, shape, multi in _launch_shapes(H):
@@ -1195,6 +1208,18 @@ def test_multi_wave_completes_every_shape(orc, P):
         exact[kind] = _oracle_complete(orc, inp, kind.split()[-1], extra=ex, moe=moe)
     shapes = [("auto", None)] + [(f"{t}x{v}", (t, v)) for t, v in MULTI_WAVE_SHAPES if t * v >= H // 8]
     base = {}
+
+    def written_snapshot():
+        # a snapshot of a Written stream: a copy of the residual
+        res = Guarded(T, H).from_host(d["residual"])
+        out = Guarded(T, H)
+        s = bnd.bnd_stream_create(T, H, res.view)
+        bnd.bnd_written(s, res.view)
+        bnd.bnd_snapshot(s, bnd.BND_OWED_NONE, out.view)
+        torch.cuda.synchronize()
+        out.check_guards("written snapshot")
+        assert torch.equal(out.view, res.view), "a snapshot of a Written stream is its residual"
+
     for label, shape in shapes:
         for kind, (inp, moe, ex) in kinds.items():
             if shape is None:
@@ -1209,7 +1234,46 @@ def test_multi_wave_completes_every_shape(orc, P):
                 base[kind] = out.view.clone()
             else:
                 assert torch.equal(out.view, base[kind]), f"{what} differs from the automatic shape"
-    print(f"\n  P/k={P}: {len(kinds)} calls under {len(shapes)} shapes", flush=True)
+        if shape is None:
+            written_snapshot()
+        else:
+            with forced_shape(*shape):
+                written_snapshot()
+    print(f"\n  P/k={P}: {len(kinds) + 1} calls under {len(shapes)} shapes", flush=True)
+
+
+@pytest.mark.parametrize("kind", ["fold", "fp8", "moe", "complete_only", "add_to_output", "snapshot",
+                                  "moe complete_only"])
+def test_every_multi_wave_instance(orc, kind):
+    """Every multi-wave kernel instance the call can reach, each against the oracle: source counts
+    1 .. 16 (partials or picks, each its own kernel) at one, two and four vectors per thread; the
+    reads at one vector also with both store policies (5 rows, fewer than the CUs, take the
+    non-temporal-store kernels; 260 rows the others)."""
+    H = 4096
+    cases = [(5, (512, 1)), (37, (256, 2)), (37, (128, 4))]
+    if kind in ("fold", "fp8", "moe"):
+        cases.append((260, (512, 1)))
+    checked = 0
+    for n in range(1, 17):
+        for T, shape in cases:
+            what = f"{kind} n={n} T={T} under {shape[0]}x{shape[1]}"
+            seed = 1000 + 17 * n + T
+            with forced_shape(*shape):
+                if kind in ("fold", "fp8"):
+                    assert_fold_matches(orc, workloads.fold_inputs(seed, T, H, n), what, fp8=kind == "fp8")
+                elif kind == "moe":
+                    run_moe(orc, workloads.moe_inputs(seed, T, H, max(n, 2), n), 0, T, what)
+                else:
+                    moe = kind.startswith("moe")
+                    d = workloads.moe_inputs(seed, T, H, max(n, 2), n) if moe else workloads.fold_inputs(seed, T, H, n)
+                    ex = (workloads.to_bf16(workloads.normal_f32(seed, 12345, (T, H), 0.0, 0.25))
+                          if kind == "add_to_output" else None)
+                    out = _complete(d, kind.split()[-1], extra=ex, moe=moe)
+                    tolerance.check_bf16(bits(out.view), *_oracle_complete(orc, d, kind.split()[-1], extra=ex, moe=moe),
+                                         what)
+            assert bnd.last_launch_shape() == (T, shape[0], shape[1], False), what
+            checked += 1
+    print(f"\n  {kind}: {checked} instances against the oracle", flush=True)
 
 
 @pytest.mark.parametrize("vpt,H", WAVE_COMPLETE_WIDTHS, ids=lambda v: str(v))

@@ -100,12 +100,15 @@ def test_every_kernel_source_compiled():
 
 
 def test_every_instance_reported(resources):
-    # 16 source counts x 3 vector counts x bf16/fp8 for partials; 3 x 2 each for input and residual;
-    # with one vector per thread also with non-temporal stores
+    # 16 source counts x 3 vector counts x bf16/fp8 for partials; 3 vector counts for the enter (bf16
+    # only) and 3 x 2 for the read of a Written stream; with one vector per thread also with
+    # non-temporal stores
     assert sum(1 for k in resources if k[0] == "Partials") == 96
     assert sum(1 for k in resources if k[0] == "PartialsNt") == 32
-    assert sum(1 for k in resources if k[0] in ("Input", "Residual")) == 12
-    assert sum(1 for k in resources if k[0] in ("InputNt", "ResidualNt")) == 4
+    assert sum(1 for k in resources if k[0] == "Input") == 3
+    assert not any(k[0].startswith("Input") and k[3] for k in resources), "the enter has no fp8 form"
+    assert sum(1 for k in resources if k[0] == "Residual") == 6
+    assert sum(1 for k in resources if k[0] in ("InputNt", "ResidualNt")) == 3
     # MoE reads, bf16 only: 16 pick counts x 3 vector counts, and one vector with non-temporal stores
     assert sum(1 for k in resources if k[0] == "Moe") == 48
     assert sum(1 for k in resources if k[0] == "MoeNt") == 16
