@@ -605,6 +605,26 @@ __device__ __forceinline__ RowSource row_source(const RowArgs& a, const RowPicks
   }
 }
 
+// The first two sources of a row of owed partials (n >= 1, which the dispatchers check): source 0
+// is partial 0; source 1 is partial 1, or for n = 1 the row after the partials (`kTail`: the
+// residual of a fold or a snapshot, the extra row of add_to_output, nothing for complete_only),
+// the same rows row_source and complete_source give. Every pointer is read before the choice,
+// which is then a select: the kernel's argument loads issue together, where a branch per choice
+// cost one dependent round trip each before the row's first loads (about 1% on the 2048-row
+// folds, whose rows all start at once).
+template <Tail kTail>
+__device__ __forceinline__ void first_partials(const RowArgs& a, int64_t row, int n, RowSource& cur,
+                                               RowSource& next) {
+  __builtin_assume(n >= 1);
+  const int rb = a.H * 2;
+  const uint16_t* p0 = a.src[0] + row * a.ld_src;
+  const uint16_t* p1 = a.src[1] + row * a.ld_src;
+  const uint16_t* tail = kTail == Tail::Extra ? a.extra + row * a.ld_extra : a.res + row * a.ld_res;
+  const int tail_bytes = kTail == Tail::Extra ? rb : kTail == Tail::Residual ? (a.has_residual ? rb : 0) : 0;
+  cur = {row_rsrc(p0, rb), 1.0f};
+  next = {row_rsrc(n > 1 ? p1 : tail, n > 1 ? rb : tail_bytes), 1.0f};
+}
+
 __device__ __forceinline__ void load_weight8(const Rsrc& wr, int vec, u32x4& lo, u32x4& hi) {
   // the weight is shared by all rows: default cache policy, it stays in L2
   lo = __builtin_amdgcn_raw_buffer_load_b128(wr, vec * 32, 0, 0);
@@ -660,8 +680,13 @@ __global__ __launch_bounds__(kWave) void wave_read_kernel(const RowArgs a) {
   uint4 ring[D];
   u32x4 wlo[D], whi[D];
   const RowPicks picks = row_picks<S>(a, row, lane);
-  RowSource cur = row_source<S>(a, picks, row, 0);
-  RowSource next = row_source<S>(a, picks, row, 1);
+  RowSource cur, next;
+  if constexpr (S == Source::Partials) {
+    first_partials<Tail::Residual>(a, row, n, cur, next);  // the residual follows the partials
+  } else {
+    cur = row_source<S>(a, picks, row, 0);
+    next = row_source<S>(a, picks, row, 1);
+  }
 #pragma unroll
   for (int v = 0; v < D; ++v) ring[v] = load16(cur.r, (lane + v * kWave) * 16);
   // the weights of the residual pass's first vectors, held until then
@@ -803,8 +828,13 @@ __global__ __launch_bounds__(kWave) void wave_complete_kernel(const RowArgs a) {
   const RowPicks picks = row_picks<S>(a, row, lane);
 
   uint4 ring[D];
-  RowSource cur = complete_source<S, kTail>(a, picks, row, 0);
-  RowSource next = complete_source<S, kTail>(a, picks, row, 1);
+  RowSource cur, next;
+  if constexpr (S == Source::Partials) {
+    first_partials<kTail>(a, row, n, cur, next);
+  } else {
+    cur = complete_source<S, kTail>(a, picks, row, 0);
+    next = complete_source<S, kTail>(a, picks, row, 1);
+  }
 #pragma unroll
   for (int v = 0; v < D; ++v) ring[v] = load16(cur.r, (lane + v * kWave) * 16);
   __builtin_amdgcn_sched_barrier(0);
