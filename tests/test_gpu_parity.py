@@ -986,9 +986,13 @@ WAVE_COMPLETE_WIDTHS = WAVE_WIDTHS + [(16, 8192)]  # the completes go one width 
 @pytest.mark.parametrize("vpt,H", WAVE_WIDTHS, ids=lambda v: str(v))
 def test_wave_rows_edge_cases(orc, vpt, H):
     d = workloads.fold_inputs(31, 12, H, 3)
+    d1 = workloads.fold_inputs(34, 12, H, 1)
     with forced_wave(vpt):
         assert_fold_matches(orc, d, "one wave per row, no residual", with_residual=False)
         assert_fold_matches(orc, d, "one wave per row, no residual fp8", with_residual=False, fp8=True)
+        # one partial: the source after it is the (empty) residual
+        assert_fold_matches(orc, d1, "one wave per row, one partial, no residual", with_residual=False)
+        assert_fold_matches(orc, d1, "one wave per row, one partial, no residual fp8", with_residual=False, fp8=True)
         assert_fold_matches(orc, d, "one wave per row, Gemma weight", gemma=True)
         assert_fold_matches(orc, d, "one wave per row, Gemma weight fp8", gemma=True, fp8=True)
     # zero rows: y = 0, scale 0 and +0 codes; a large outlier row
@@ -1311,11 +1315,13 @@ def test_wave_complete_edge_cases(orc, vpt, H):
     b = _complete(d, "complete_only")
     assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16))
     assert int((a.view[3].view(torch.int16) != 0).sum()) == 0, "a sum of -0 stores +0"
-    # a snapshot of a Pending stream without a residual is bf16(s)
-    with forced_wave(vpt):
-        a = _complete(d, "snapshot", with_residual=False)
-    e, mag = _oracle_complete(orc, d, "snapshot", with_residual=False)
-    tolerance.check_bf16(bits(a.view), e, mag, "snapshot without a residual")
+    # a snapshot of a Pending stream without a residual is bf16(s), with four partials and with one
+    d1 = workloads.fold_inputs(413, 12, H, 1)
+    for dd, what in ((d, "snapshot without a residual"), (d1, "one-partial snapshot without a residual")):
+        with forced_wave(vpt):
+            a = _complete(dd, "snapshot", with_residual=False)
+        e, mag = _oracle_complete(orc, dd, "snapshot", with_residual=False)
+        tolerance.check_bf16(bits(a.view), e, mag, what)
     # a snapshot of a Written stream copies the residual: no one-wavefront kernel, refused
     res = Guarded(12, H).from_host(d["residual"])
     out = Guarded(12, H)
