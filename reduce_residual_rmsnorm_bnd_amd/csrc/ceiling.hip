@@ -6,9 +6,11 @@
 // boundary kernels. The prefill fold's mix is nine reads (eight partials and the residual) and two
 // writes (the residual and the normalised output); complete_only's is eight and one, a snapshot's
 // or add_to_output's nine and one. The loaded vectors are combined with XOR so that every load is
-// consumed and every store depends on all of them. Its rate on a device is what that memory
-// system delivers for the stream in this layout; each call is compared with its own mix as
-// context. A gathering variant reads eight of
+// consumed and every store depends on all of them. With eight vectors per thread the stream
+// follows the one-wavefront boundary kernels' order (ring_stream below); with one, two or four a
+// thread issues a source's loads together. Its rate on a device is what that memory system
+// delivers for the stream in this layout; each call is compared with its own mix as context.
+// A gathering variant reads eight of
 // the nine rows through an int32 row index, as the MoE finalize reads its picks. An empty kernel
 // gives the cost of a launch with no work, the floor under the per-boundary time of small
 // batches. Built into its own library (libboundary_ceiling.so); the boundary library does not
@@ -31,6 +33,66 @@ struct MixArgs {
   int n_src;       // 1..16
 };
 
+// Eight vectors per thread stream as the one-wavefront boundary kernels do: source after source,
+// each thread's vectors of a source in order, two loads in flight through a ring that runs on
+// across source boundaries (the next source's first vectors load while this one's last vectors
+// are consumed), and during the last source's pass each finished vector stored at once to the
+// first output, as those kernels store the residual (or a complete's output); a second output
+// is stored after the stream, as they store y. `source_of(p)` is the resource of source p.
+template <int VPT, bool kStore>
+__device__ __forceinline__ void ring_pass(const bnd::Rsrc& cur, const bnd::Rsrc& next, const bnd::Rsrc& out,
+                                          const int (&off)[VPT], uint4 (&ring)[2], uint4 (&acc)[VPT]) {
+  static_assert(VPT % 2 == 0, "a ring slot is the vector index mod 2");
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const uint4 t = ring[v & 1];
+    ring[v & 1] = v + 2 < VPT ? bnd::load16(cur, off[v + 2]) : bnd::load16(next, off[v + 2 - VPT]);
+    acc[v].x ^= t.x; acc[v].y ^= t.y; acc[v].z ^= t.z; acc[v].w ^= t.w;
+    asm volatile("" : "+v"(acc[v].x), "+v"(acc[v].y), "+v"(acc[v].z), "+v"(acc[v].w));
+    if constexpr (kStore) bnd::store16(out, off[v], acc[v]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// kN > 0: a source count known at compile time, the loop unrolled (the gathering stream, whose
+// eight row indices then load together before the first pass, as the MoE finalize fetches its
+// picks once per row); kN = 0: n_src (>= 1) at run time.
+template <int VPT, int kN, typename SourceOf>
+__device__ __forceinline__ void ring_stream(int n_src, SourceOf source_of, const bnd::Rsrc& out,
+                                            const int (&off)[VPT], uint4 (&acc)[VPT]) {
+  // After the last source the refills read an empty resource (zeros, no memory access), so every
+  // step issues its load. The first source's pass runs before the loop, as in the boundary
+  // kernels: both edges into the loop then leave the same loads outstanding in the same order,
+  // and the compiler waits for one load at a time instead of draining the ring at each source.
+  const bnd::Rsrc empty = bnd::row_rsrc(nullptr, 0);
+  if constexpr (kN > 0) n_src = kN;
+  uint4 ring[2];
+  bnd::Rsrc cur = source_of(0);
+  ring[0] = bnd::load16(cur, off[0]);
+  ring[1] = bnd::load16(cur, off[1]);
+  if (n_src == 1) {
+    ring_pass<VPT, true>(cur, empty, out, off, ring, acc);
+    return;
+  }
+  bnd::Rsrc next = source_of(1);
+  ring_pass<VPT, false>(cur, next, out, off, ring, acc);
+  if constexpr (kN > 0) {
+#pragma unroll
+    for (int p = 1; p < kN - 1; ++p) {
+      cur = next;
+      next = source_of(p + 1);
+      ring_pass<VPT, false>(cur, next, out, off, ring, acc);
+    }
+  } else {
+    for (int p = 1; p < n_src - 1; ++p) {
+      cur = next;
+      next = source_of(p + 1);
+      ring_pass<VPT, false>(cur, next, out, off, ring, acc);
+    }
+  }
+  ring_pass<VPT, true>(next, empty, out, off, ring, acc);  // the last source
+}
+
 template <int VPT>
 __global__ __launch_bounds__(bnd::kMaxThreads) void mix_kernel(const MixArgs a) {
   const int64_t row = blockIdx.x;
@@ -39,22 +101,31 @@ __global__ __launch_bounds__(bnd::kMaxThreads) void mix_kernel(const MixArgs a) 
 #pragma unroll
   for (int v = 0; v < VPT; ++v) off[v] = (threadIdx.x + v * nthr) * 16;
   uint4 acc[VPT];
-  {
-    const bnd::Rsrc r = bnd::row_rsrc(a.src[0] + row * a.ld, a.row_bytes);
+  const bnd::Rsrc o0 = bnd::row_rsrc(a.out0 + row * a.ld, a.row_bytes);
+  if constexpr (VPT == 8) {
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) acc[v] = bnd::load16(r, off[v]);
-  }
-  for (int p = 1; p < a.n_src; ++p) {
-    const bnd::Rsrc r = bnd::row_rsrc(a.src[p] + row * a.ld, a.row_bytes);
+    for (int v = 0; v < VPT; ++v) acc[v] = make_uint4(0u, 0u, 0u, 0u);
+    ring_stream<VPT, 0>(a.n_src, [&](int p) { return bnd::row_rsrc(a.src[p] + row * a.ld, a.row_bytes); }, o0,
+                        off, acc);
+  } else {
+    {
+      const bnd::Rsrc r = bnd::row_rsrc(a.src[0] + row * a.ld, a.row_bytes);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const uint4 t = bnd::load16(r, off[v]);
-      acc[v].x ^= t.x; acc[v].y ^= t.y; acc[v].z ^= t.z; acc[v].w ^= t.w;
+      for (int v = 0; v < VPT; ++v) acc[v] = bnd::load16(r, off[v]);
+    }
+    for (int p = 1; p < a.n_src; ++p) {
+      const bnd::Rsrc r = bnd::row_rsrc(a.src[p] + row * a.ld, a.row_bytes);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        const uint4 t = bnd::load16(r, off[v]);
+        acc[v].x ^= t.x; acc[v].y ^= t.y; acc[v].z ^= t.z; acc[v].w ^= t.w;
+      }
     }
   }
-  const bnd::Rsrc o0 = bnd::row_rsrc(a.out0 + row * a.ld, a.row_bytes);
+  if constexpr (VPT != 8) {  // the ring stored the first output during its last pass
 #pragma unroll
-  for (int v = 0; v < VPT; ++v) bnd::store16(o0, off[v], acc[v]);
+    for (int v = 0; v < VPT; ++v) bnd::store16(o0, off[v], acc[v]);
+  }
   if (a.out1) {
     const bnd::Rsrc o1 = bnd::row_rsrc(a.out1 + row * a.ld, a.row_bytes);
 #pragma unroll
@@ -85,38 +156,34 @@ __global__ __launch_bounds__(bnd::kMaxThreads) void gather_kernel(const GatherAr
   uint4 acc[VPT];
 #pragma unroll
   for (int v = 0; v < VPT; ++v) acc[v] = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-  for (int p = 0; p < kSources; ++p) {
-    const uint16_t* base;
-    int bytes = a.row_bytes;
+  // source p < 8: row idx[row * 8 + p] of rows_src (an index outside the rows reads zeros);
+  // source 8: row `row` of src8
+  const auto source_of = [&](int p) {
     if (p < kSources - 1) {
       const int64_t e = a.idx[row * (kSources - 1) + p];
       const bool valid = e >= 0 && e < a.n_src_rows;
-      base = a.rows_src + (valid ? e : 0) * a.ld;
-      bytes = valid ? a.row_bytes : 0;
-    } else {
-      base = a.src8 + row * a.ld;
+      return bnd::row_rsrc(a.rows_src + (valid ? e : 0) * a.ld, valid ? a.row_bytes : 0);
     }
-    const bnd::Rsrc r = bnd::row_rsrc(base, bytes);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const uint4 t = bnd::load16(r, off[v]);
-      acc[v].x ^= t.x; acc[v].y ^= t.y; acc[v].z ^= t.z; acc[v].w ^= t.w;
-    }
-    // With eight vectors per thread a row's 72 loads (288 VGPRs) cannot all be in flight within
-    // the 128 VGPRs of a 1024-thread workgroup: one source's loads at a time, as in mix_kernel,
-    // instead of a spill to scratch.
-    if constexpr (VPT >= 8) {
-#pragma unroll
-      for (int v = 0; v < VPT; ++v) asm volatile("" : "+v"(acc[v].x), "+v"(acc[v].y), "+v"(acc[v].z), "+v"(acc[v].w));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+    return bnd::row_rsrc(a.src8 + row * a.ld, a.row_bytes);
+  };
   const bnd::Rsrc o0 = bnd::row_rsrc(a.out0 + row * a.ld, a.row_bytes);
   const bnd::Rsrc o1 = bnd::row_rsrc(a.out1 + row * a.ld, a.row_bytes);
+  if constexpr (VPT == 8) {
+    ring_stream<VPT, kSources>(kSources, source_of, o0, off, acc);
+  } else {
+#pragma unroll
+    for (int p = 0; p < kSources; ++p) {
+      const bnd::Rsrc r = source_of(p);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        const uint4 t = bnd::load16(r, off[v]);
+        acc[v].x ^= t.x; acc[v].y ^= t.y; acc[v].z ^= t.z; acc[v].w ^= t.w;
+      }
+    }
+  }
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    bnd::store16(o0, off[v], acc[v]);
+    if constexpr (VPT != 8) bnd::store16(o0, off[v], acc[v]);  // VPT 8: stored during the last pass
     bnd::store16(o1, off[v], acc[v]);
   }
 }
