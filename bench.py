@@ -572,7 +572,7 @@ def stream_ceiling(torch, T: int, H: int, n_src: int, n_out: int, kernel_us: dic
     return out
 
 
-def gather_ceiling(torch, dm, moe_us, rows=None):
+def gather_ceiling(torch, dm, moe_us, rows=None, others=None):
     """The gathering 9:2 stream (libboundary_ceiling.so: eight rows read through the MoE
     workload's own index, the ninth by row, two rows written, no arithmetic) over rotating copies
     of the expert rows, beside the MoE finalize timed the same way. `rows` = (row_begin, count)
@@ -618,7 +618,10 @@ def gather_ceiling(torch, dm, moe_us, rows=None):
             "best_shape": best, "GBps": nbytes / shapes[best] / 1e3,
             "frac": nbytes / shapes[best] / 1e3 / PEAK_HBM_GBPS,
             "moe_back_to_back_us": moe_us,
-            "moe_time_over_ceiling_time": moe_us / shapes[best] if moe_us else None}
+            "moe_time_over_ceiling_time": moe_us / shapes[best] if moe_us else None,
+            **{f"{name}_back_to_back_us": us for name, us in (others or {}).items()},
+            **{f"{name}_time_over_ceiling_time": us / shapes[best] if us else None
+               for name, us in (others or {}).items()}}
 
 
 def device_memory_info():
@@ -878,7 +881,7 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
     dm = workloads.moe()
     moe_us = {}
 
-    def moe(rb, rows, tg, back_to_back):
+    def moe(rb, rows, tg):
         # rotate over at least 1 GiB of the bytes a launch moves: a share reads only its rows' picks
         n_m = max(2, -(-ROTATE_BYTES // (rows * (dm["k"] + 3) * dm["H"] * 2)))
         step, nb, keep = moe_case(torch, bnd, dm, n_m, rb, rows, terminal_gemma=tg)
@@ -886,20 +889,20 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
         out = {"tokens_per_s_kernel": rows / tm["kernel_s"], **kernel_fields(tm, bnd),
                "GBps": nb / tm["kernel_s"] / 1e9, "frac": nb / tm["kernel_s"] / 1e9 / PEAK_HBM_GBPS,
                "algorithmic_bytes": nb}
-        if back_to_back:
-            moe_us[rows] = back_to_back_us(torch, lambda i: step(i, None, None), n_m)
-            out["back_to_back_us"] = moe_us[rows]
+        moe_us[(rows, tg)] = back_to_back_us(torch, lambda i: step(i, None, None), n_m)
+        out["back_to_back_us"] = moe_us[(rows, tg)]
         return out
 
     # the full-row calls first, then the share with its 47 rotation sets
-    leg(sec, "moe_full_T2048_H4096_k8", lambda: moe(0, 2048, False, True), torch)
-    leg(sec, "moe_terminal_gemma_T2048_H4096_k8", lambda: moe(0, 2048, True, False), torch)
-    leg(sec, "moe_slice_rows768_1023", lambda: moe(*workloads.MOE_SLICE, False, True), torch)
+    leg(sec, "moe_full_T2048_H4096_k8", lambda: moe(0, 2048, False), torch)
+    leg(sec, "moe_terminal_gemma_T2048_H4096_k8", lambda: moe(0, 2048, True), torch)
+    leg(sec, "moe_slice_rows768_1023", lambda: moe(*workloads.MOE_SLICE, False), torch)
     log("gathering 9:2 streaming ceilings (the MoE finalize's loads and stores without arithmetic)")
     leg(sec, "gather_ceiling_9r2w_T2048_H4096_k8",
-        lambda: gather_ceiling(torch, dm, moe_us.get(2048)), torch)
+        lambda: gather_ceiling(torch, dm, moe_us.get((2048, False)),
+                               others={"moe_terminal_gemma": moe_us.get((2048, True))}), torch)
     leg(sec, "gather_ceiling_9r2w_rows768_1023_H4096_k8",
-        lambda: gather_ceiling(torch, dm, moe_us.get(workloads.MOE_SLICE[1]), rows=workloads.MOE_SLICE), torch)
+        lambda: gather_ceiling(torch, dm, moe_us.get((workloads.MOE_SLICE[1], False)), rows=workloads.MOE_SLICE), torch)
     del dm
 
     log("complete_only, snapshot and add_to_output (prefill sizes), the unfused fallback, "
