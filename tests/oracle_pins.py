@@ -101,6 +101,23 @@ def pin_e8_fp8_decided_in_fp32(o):
     assert c["expect_codes"] != c["exact_quotient_codes"]
 
 
+def pin_e9_moe_finalize(o):
+    """A MoE finalize fold derived by hand: gate-weighted picks, an out-of-range pick with a large
+    gate that contributes nothing, rows whose mean square is exactly 4."""
+    c = CASES["E9_moe_finalize"]
+    w = f32(c["weight"])
+    out = o.moe_fold_norm(bits(c["expert_rows"]), np.asarray(c["idx"], np.int32), f32(c["gate"]), c["k"],
+                          bits(c["residual"]), w, c["eps"])
+    assert out["x_exact"].tolist() == c["expect_x"], out["x_exact"]
+    assert bval(out["residual"]).tolist() == c["expect_x"], bval(out["residual"])
+    assert bval(out["y"]).tolist() == c["expect_y_bf16"], bval(out["y"])
+    # inv from every nonzero element: y_exact = x w inv
+    x, y = out["x_exact"], out["y_exact"]
+    nz = x * w[None, :] != 0
+    inv2 = 2.0 * y[nz] / (x * w[None, :])[nz]
+    assert np.all(np.abs(inv2 - c["expect_inv_times_2"]) <= 1e-15), inv2
+
+
 def pin_e6_zero_row(o):
     c = CASES["E6_zero_row"]
     H = c["H"]
@@ -416,5 +433,5 @@ def pin_invariants(o):
 
 PINS = [pin_e1_closed_form, pin_e2_fold, pin_e3_eps_inside_root, pin_e4_one_hot, pin_e5_fp8,
         pin_e8_fp8_decided_in_fp32,
-        pin_e6_zero_row, pin_e7_gemma, pin_bruteforce_fold, pin_bruteforce_fp8, pin_bruteforce_moe,
+        pin_e6_zero_row, pin_e7_gemma, pin_e9_moe_finalize, pin_bruteforce_fold, pin_bruteforce_fp8, pin_bruteforce_moe,
         pin_bruteforce_complete, pin_add_to_output, pin_snapshot, pin_bf16_codec, pin_e4m3_codec, pin_invariants]
