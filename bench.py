@@ -529,22 +529,30 @@ def back_to_back_us(torch, launch, n_sets: int, reps: int = 300, warmup: int = 2
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def stream_ceiling(torch, T: int, H: int, n_src: int, n_out: int, kernel_us: dict):
+def stream_ceiling(torch, T: int, H: int, n_src: int, n_out: int, kernel_us: dict, byte_second: bool = False):
     """The arithmetic-free streaming kernel (libboundary_ceiling.so: n_src row reads and n_out row
     writes per row, the boundary kernels' rows, resources and cache policy) over rotating sets of
     [T, H] rows, for four launch shapes; beside it the boundary calls with the same mix, timed the
-    same way (back-to-back launches) in the same process (`kernel_us`: name -> us)."""
+    same way (back-to-back launches) in the same process (`kernel_us`: name -> us). With
+    `byte_second` the second output has one byte per element, as the fp8 read's codes."""
     from reduce_residual_rmsnorm_bnd_amd import _build
 
     L = ctypes.CDLL(_build.CEILING_LIB_PATH)
     vp = ctypes.c_void_p
-    L.bnd_ceiling_mix.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int64,
-                                  ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp]
-    nbytes = (n_src + n_out) * T * H * 2
+    args = [ctypes.POINTER(vp), ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+            ctypes.c_int, vp]
+    L.bnd_ceiling_mix.argtypes = args
+    L.bnd_ceiling_mix_byte_out1.argtypes = args
+    mix = L.bnd_ceiling_mix_byte_out1 if byte_second else L.bnd_ceiling_mix
+    if byte_second and n_out != 2:
+        raise ValueError("a byte-wide second output needs two outputs")
+    nbytes = (n_src + n_out) * T * H * 2 - (T * H if byte_second else 0)
     n_sets = max(2, -(-ROTATE_BYTES // nbytes))
     sets = []
     for _ in range(n_sets):
-        bufs = [torch.zeros(T, H, dtype=torch.bfloat16, device="cuda:0") for _ in range(n_src + n_out)]
+        bufs = [torch.zeros(T, H, dtype=torch.bfloat16, device="cuda:0") for _ in range(n_src + 1)]
+        if n_out == 2:
+            bufs.append(torch.zeros(T, H, dtype=torch.uint8 if byte_second else torch.bfloat16, device="cuda:0"))
         sets.append((bufs, (vp * n_src)(*[b.data_ptr() for b in bufs[:n_src]]), vp(bufs[n_src].data_ptr()),
                      vp(bufs[n_src + 1].data_ptr()) if n_out == 2 else vp()))
     stream = vp(torch.cuda.current_stream().cuda_stream)
@@ -556,14 +564,15 @@ def stream_ceiling(torch, T: int, H: int, n_src: int, n_out: int, kernel_us: dic
     for threads, vpt in cover:
         def launch(i, threads=threads, vpt=vpt):
             _, src, o0, o1 = sets[i]
-            rc = L.bnd_ceiling_mix(src, n_src, o0, o1, T, H, H, threads, vpt, stream)
+            rc = mix(src, n_src, o0, o1, T, H, H, threads, vpt, stream)
             if rc:
                 raise RuntimeError(f"ceiling launch failed: {rc}")
         shapes[f"{threads}x{vpt}"] = back_to_back_us(torch, launch, n_sets)
     best = min(shapes, key=shapes.get)
     del sets
     torch.cuda.empty_cache()
-    out = {"reads_writes": f"{n_src}:{n_out}", "bytes": nbytes, "us_per_launch_by_shape": shapes,
+    out = {"reads_writes": f"{n_src}:{n_out - 0.5 if byte_second else n_out}", "bytes": nbytes,
+           "us_per_launch_by_shape": shapes,
            "best_shape": best, "GBps": nbytes / shapes[best] / 1e3,
            "frac": nbytes / shapes[best] / 1e3 / PEAK_HBM_GBPS}
     for name, us in kernel_us.items():
@@ -871,11 +880,14 @@ def secondary(torch, bnd, workloads, d, timer, fold_step, n_sets) -> dict:
     leg(sec, "fp8_T2048_H7168_P8", fp8, torch)
     # the fp8 read writes a bf16 residual row and a row of one-byte codes: between the 9:1 and 9:2
     # streams at its width
-    log("9:1 and 9:2 streaming ceilings at H = 7168 (the quantised read's width)")
+    log("9:1, 9:2 and 9:1.5 streaming ceilings at H = 7168 (the quantised read's width)")
     leg(sec, "stream_ceiling_9r1w_T2048_H7168",
         lambda: stream_ceiling(torch, 2048, 7168, 9, 1, {"fp8": fp8_us.get("fp8")}), torch)
     leg(sec, "stream_ceiling_9r2w_T2048_H7168",
         lambda: stream_ceiling(torch, 2048, 7168, 9, 2, {"fp8": fp8_us.get("fp8")}), torch)
+    # the fp8 read's own mix: nine reads, a bf16 row and a row of one-byte codes written
+    leg(sec, "stream_ceiling_9r1h_T2048_H7168",
+        lambda: stream_ceiling(torch, 2048, 7168, 9, 2, {"fp8": fp8_us.get("fp8")}, byte_second=True), torch)
 
     log("MoE finalize (T=2048 H=4096 k=8), full rows and rows 768..1023")
     dm = workloads.moe()

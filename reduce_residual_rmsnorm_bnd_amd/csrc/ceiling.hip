@@ -1,7 +1,8 @@
 // ceiling.hip -- measurement support, not part of the boundary path.
 //
 // A kernel with a boundary call's memory access mix and none of its arithmetic: for every
-// 16-byte vector of a row it reads n rows and writes one or two, one row per workgroup, through
+// 16-byte vector of a row it reads n rows and writes one or two (the second may be one byte per
+// element, as the fp8 read's codes beside its bf16 residual), one row per workgroup, through
 // the same per-row buffer resources and cache policy (non-temporal loads, sc1 stores) as the
 // boundary kernels. The prefill fold's mix is nine reads (eight partials and the residual) and two
 // writes (the residual and the normalised output); complete_only's is eight and one, a snapshot's
@@ -31,6 +32,7 @@ struct MixArgs {
   int64_t ld;      // elements between rows, same for every operand
   int row_bytes;   // bytes of a row that are read and written
   int n_src;       // 1..16
+  int out1_bytes;  // out1's bytes per element: 2, or 1 (as the fp8 read's codes: 8 bytes per vector)
 };
 
 // Eight vectors per thread stream as the one-wavefront boundary kernels do: source after source,
@@ -126,7 +128,12 @@ __global__ __launch_bounds__(bnd::kMaxThreads) void mix_kernel(const MixArgs a) 
 #pragma unroll
     for (int v = 0; v < VPT; ++v) bnd::store16(o0, off[v], acc[v]);
   }
-  if (a.out1) {
+  if (a.out1 && a.out1_bytes == 1) {
+    // one byte per element: the first 8 bytes of each 16-byte vector, at half its offset
+    const bnd::Rsrc o1 = bnd::row_rsrc(reinterpret_cast<uint8_t*>(a.out1) + row * a.ld, a.row_bytes / 2);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) bnd::store8(o1, off[v] / 2, make_uint2(acc[v].x, acc[v].y));
+  } else if (a.out1) {
     const bnd::Rsrc o1 = bnd::row_rsrc(a.out1 + row * a.ld, a.row_bytes);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) bnd::store16(o1, off[v], acc[v]);
@@ -212,9 +219,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 //              threads * vpt * 8 must cover row_elems
 // Returns 0 on success, -1 on an invalid argument (nothing launched), or the hipError_t of the
 // launch.
-extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix(
-    const void* const* src, int n_src, void* out0, void* out1, int64_t rows, int64_t ld, int64_t row_elems,
-    int threads, int vpt, hipStream_t stream) {
+static int launch_mix(const void* const* src, int n_src, void* out0, void* out1, int out1_bytes, int64_t rows,
+                      int64_t ld, int64_t row_elems, int threads, int vpt, hipStream_t stream) {
   if (!src || n_src < 1 || n_src > kMaxMixSources || !out0 || rows < 1 || rows > 0x7fffffff || row_elems < 8 ||
       row_elems % 8 || ld < row_elems || ld % 8 || row_elems * 2 > 0x7fffffff)
     return -1;
@@ -226,18 +232,35 @@ extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix(
     if (!src[p] || !aligned16(src[p])) return -1;
     a.src[p] = static_cast<const uint16_t*>(src[p]);
   }
-  if (!aligned16(out0) || (out1 && !aligned16(out1))) return -1;
+  if (!aligned16(out0) || (out1 && (reinterpret_cast<uintptr_t>(out1) & (out1_bytes == 1 ? 7 : 15)))) return -1;
   a.out0 = static_cast<uint16_t*>(out0);
   a.out1 = static_cast<uint16_t*>(out1);
   a.ld = ld;
   a.row_bytes = (int)(row_elems * 2);
   a.n_src = n_src;
+  a.out1_bytes = out1_bytes;
   void* args[] = {&a};
   const void* fn = vpt == 1   ? reinterpret_cast<const void*>(&mix_kernel<1>)
                    : vpt == 2 ? reinterpret_cast<const void*>(&mix_kernel<2>)
                    : vpt == 4 ? reinterpret_cast<const void*>(&mix_kernel<4>)
                               : reinterpret_cast<const void*>(&mix_kernel<8>);
   return (int)hipLaunchKernel(fn, dim3((unsigned)rows), dim3((unsigned)threads), args, 0, stream);
+}
+
+extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix(
+    const void* const* src, int n_src, void* out0, void* out1, int64_t rows, int64_t ld, int64_t row_elems,
+    int threads, int vpt, hipStream_t stream) {
+  return launch_mix(src, n_src, out0, out1, 2, rows, ld, row_elems, threads, vpt, stream);
+}
+
+// As bnd_ceiling_mix with a second output of one byte per element, as the fp8 read writes its
+// codes beside the bf16 residual: out1 (8-byte aligned, required) is [rows, ld] bytes, and each
+// 16-byte vector of a row stores its first 8 bytes there at half its offset.
+extern "C" __attribute__((visibility("default"))) int bnd_ceiling_mix_byte_out1(
+    const void* const* src, int n_src, void* out0, void* out1, int64_t rows, int64_t ld, int64_t row_elems,
+    int threads, int vpt, hipStream_t stream) {
+  if (!out1) return -1;
+  return launch_mix(src, n_src, out0, out1, 1, rows, ld, row_elems, threads, vpt, stream);
 }
 
 // The prefill fold's mix: nine sources, two outputs (out1 must not be NULL).

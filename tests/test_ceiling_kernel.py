@@ -22,6 +22,8 @@ def _lib():
     L.bnd_ceiling_mix.argtypes = [ctypes.POINTER(VP), ctypes.c_int, VP, VP, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, VP]
     L.bnd_ceiling_mix.restype = ctypes.c_int
+    L.bnd_ceiling_mix_byte_out1.argtypes = L.bnd_ceiling_mix.argtypes
+    L.bnd_ceiling_mix_byte_out1.restype = ctypes.c_int
     for fn in (L.bnd_ceiling_empty, L.bnd_ceiling_empty_args):
         fn.argtypes = [ctypes.c_int64, ctypes.c_int, VP]
         fn.restype = ctypes.c_int
@@ -60,6 +62,9 @@ def test_ceiling_refuses_bad_shapes():
     for n in (0, 17):  # source counts outside 1..16
         assert L.bnd_ceiling_mix(src16, n, o0, None, 4, 4096, 4096, 512, 1, None) == -1, n
     assert L.bnd_ceiling_mix_9r2w(src, o0, None, 4, 4096, 4096, 512, 1, None) == -1  # 9:2 needs two outputs
+    # a byte-wide second output is required and 8-byte aligned
+    assert L.bnd_ceiling_mix_byte_out1(src16, 9, o0, None, 4, 4096, 4096, 512, 1, None) == -1
+    assert L.bnd_ceiling_mix_byte_out1(src16, 9, o0, VP(a + (21 << 24) + 4), 4, 4096, 4096, 512, 1, None) == -1
     for wg, threads in ((0, 64), (1, 32), (1, 100), (1, 2048), (1 << 31, 64), (1 << 26, 128)):
         assert L.bnd_ceiling_empty(wg, threads, None) == -1, (wg, threads)
         assert L.bnd_ceiling_empty_args(wg, threads, None) == -1, (wg, threads)
@@ -163,3 +168,32 @@ def test_mix_streams_the_xor(n_src, two_outputs):
         assert torch.equal(out[1].cpu(), expect)
     else:
         assert bool((out[1] == 7).all()), "one output: the second buffer is untouched"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("threads,vpt,H", [(64, 8, 4096), (128, 8, 7168), (1024, 1, 7168), (256, 4, 3600)])
+def test_mix_byte_second_output(threads, vpt, H):
+    """The second output one byte per element: each 16-byte vector's first 8 bytes at half its
+    offset; the bf16 output and everything past the row untouched otherwise."""
+    L = _lib()
+    rows, n_src = 11, 9
+    g = torch.Generator().manual_seed(threads + H)
+    host = [torch.randint(-32768, 32768, (rows, H), dtype=torch.int16, generator=g) for _ in range(n_src)]
+    srcs = [h.to("cuda:0") for h in host]
+    out0 = torch.full((rows, H), 7, dtype=torch.int16, device="cuda:0")
+    out1 = torch.full((rows, H + 64), 9, dtype=torch.uint8, device="cuda:0")  # ld = H elements; tail canary
+    print(f"\n  mix {n_src}:1.5 rows={rows} H={H} {threads}x{vpt}", flush=True)
+    rc = L.bnd_ceiling_mix_byte_out1((VP * n_src)(*[s.data_ptr() for s in srcs]), n_src, out0.data_ptr(),
+                                     out1.data_ptr(), rows, H, H, threads, vpt, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    expect = host[0].clone()
+    for h in host[1:]:
+        expect ^= h
+    assert torch.equal(out0.cpu(), expect)
+    b = out1.cpu()
+    first8 = expect.view(torch.uint8).reshape(rows, H // 8, 16)[:, :, :8].reshape(rows, H)
+    flat = b.reshape(-1)
+    got = torch.stack([flat[r * H:(r + 1) * H] for r in range(rows)])  # rows at ld = H bytes
+    assert torch.equal(got, first8)
+    assert bool((flat[rows * H:] == 9).all()), "nothing past the last row"
